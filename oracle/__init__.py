@@ -1,0 +1,112 @@
+"""The attention-forward oracle: a plain fp64 two-pass CPU implementation (``fa_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module.  It shares no code with the HIP library and imports nothing from
+the ``transformer_attention_fwd_amd`` package.
+
+The C file states what is computed and which passage of the pages each step follows.  This module only
+builds the C file with gcc, loads it with ctypes and marshals numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+DTYPES = {"fp32": 0, "fp16": 1, "bf16": 2, "fp64": 3}
+ITEMSIZE = {"fp32": 4, "fp16": 2, "bf16": 2, "fp64": 8}
+LAYOUTS = {"BHSD": 0, "BSND": 1}
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile ``fa_oracle.c`` into ``liboracle.so`` next to it (gcc -O2, pthreads)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC", "-pthread",
+                               _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.fa_oracle_rows.restype = ctypes.c_int
+        lib.fa_oracle_rows.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_double,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ]
+        _lib = lib
+    return _lib
+
+
+def _dims(shape, layout):
+    if len(shape) != 4:
+        raise ValueError("q, k, v must be 4-D")
+    if layout == "BHSD":
+        B, H, N, D = shape
+    elif layout == "BSND":
+        B, N, H, D = shape
+    else:
+        raise ValueError("layout must be 'BHSD' or 'BSND'")
+    return B, H, N, D
+
+
+def attention_rows(q, k, v, *, dtype: str, layout: str, causal: bool, scale: float, rows, nthreads: int = 1):
+    """O and lse of the requested query rows, in fp64.
+
+    q, k, v: numpy arrays holding the stored elements, shaped [B,H,N,D] (BHSD) or [B,N,H,D] (BSND),
+    with itemsize matching ``dtype`` (bf16 and fp16 as 16-bit patterns, e.g. uint16 or float16).
+    rows: int64 array of shape [R, 3] holding (b, h, i) triples.
+    scale: used as given (pass the fp32-rounded value to model an fp32 scale argument).
+    Returns (o [R, D] float64, lse [R] float64).
+    """
+    if dtype not in DTYPES:
+        raise ValueError("dtype must be one of %s" % sorted(DTYPES))
+    B, H, N, D = _dims(q.shape, layout)
+    for t in (q, k, v):
+        if t.shape != q.shape or t.dtype.itemsize != ITEMSIZE[dtype]:
+            raise ValueError("q, k, v must share the shape and have the itemsize of %s" % dtype)
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
+    R = rows.shape[0]
+    o = np.empty((R, D), dtype=np.float64)
+    lse = np.empty((R,), dtype=np.float64)
+    if R == 0:
+        return o, lse
+    rc = _load().fa_oracle_rows(q.ctypes.data, k.ctypes.data, v.ctypes.data, DTYPES[dtype], LAYOUTS[layout],
+                                B, H, N, D, 1 if causal else 0, float(scale), rows.ctypes.data, R,
+                                o.ctypes.data, lse.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError("fa_oracle_rows failed with status %d" % rc)
+    return o, lse
+
+
+def all_rows(B: int, H: int, N: int) -> np.ndarray:
+    """Every (b, h, i) triple in [B, H, N] order."""
+    b, h, i = np.meshgrid(np.arange(B), np.arange(H), np.arange(N), indexing="ij")
+    return np.stack([b.ravel(), h.ravel(), i.ravel()], axis=1).astype(np.int64)
+
+
+def attention(q, k, v, *, dtype: str, layout: str, causal: bool, scale: float, nthreads: int = 1):
+    """Full O and lse, in fp64.  O is returned in the input's layout; lse as [B, H, N]."""
+    B, H, N, D = _dims(q.shape, layout)
+    o_rows, lse = attention_rows(q, k, v, dtype=dtype, layout=layout, causal=causal, scale=scale,
+                                 rows=all_rows(B, H, N), nthreads=nthreads)
+    o = o_rows.reshape(B, H, N, D)
+    if layout == "BSND":
+        o = np.ascontiguousarray(o.transpose(0, 2, 1, 3))
+    return o, lse.reshape(B, H, N)

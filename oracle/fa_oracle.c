@@ -1,0 +1,195 @@
+/*
+ * fa_oracle.c -- the attention-forward oracle: a plain, slow, fp64, two-pass CPU implementation.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg
+ * may load this library.  It shares no code, header or constant with the HIP library and includes
+ * nothing from it.
+ *
+ * What it computes (for every requested query row i of head (b, h)):
+ *
+ *   Attention(Q, K, V) = Softmax(Q K^T / sqrt(d)) V, with the 1/sqrt(d) factor generalised to a
+ *   caller-given scale.  Source: page "FlashAttention：让长文本推理不再"卡显存"" (ai6s.net,
+ *   6a0d42d8...), section "Attention 的显存黑洞" (the formula and its three steps: scores,
+ *   softmax, product with V); the same three steps as code on page ai6s.net/6a0d3bfb... section
+ *   "为什么传统attention会卡住？" and in the precision check of page hwcomputing.csdn.net/6a0d4444...
+ *
+ *   Causal: key j is visible to query i iff j <= i.  Source: page ai6s.net/6a0d3bfb..., the
+ *   causal-mask section, where the mask tensor marks entries strictly above the diagonal
+ *   (torch.triu(..., diagonal=1)) as hidden; page hwcomputing.csdn.net/6a0d4681..., section
+ *   "Causal Mask的实现差异" (each position sees only earlier tokens).
+ *
+ *   lse_i = ln sum_{j visible} exp(s_ij), the natural-log log-sum-exp of the scaled logits, one fp
+ *   value per (b, h, i).  Source: page ai6s.net/6a140d07..., section "第二层：数值稳定性增强" (the
+ *   lse accumulator of shape [B, H, block_i], built with torch.log / torch.exp).
+ *
+ * Steps, per row, in this order (nothing is tiled, fused or reordered):
+ *   1. widen the stored q, k, v elements exactly to double;
+ *   2. pass 1: s_j = scale * sum_d q_d k_jd (d ascending) for every visible j; m = max_j s_j;
+ *   3. pass 2: e_j = exp(s_j - m); l = sum_j e_j (j ascending); o_d = (sum_j e_j v_jd) / l;
+ *   4. lse = m + log(l).
+ *
+ * Element addressing (packed, contiguous tensors):
+ *   layout 0, BHSD = [B][H][N][D]:  ((b*H + h)*N + i)*D + d
+ *   layout 1, BSND = [B][N][H][D]:  ((b*N + i)*H + h)*D + d
+ * Input element types: 0 = IEEE binary32, 1 = IEEE binary16, 2 = bfloat16, 3 = IEEE binary64.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_F32 0
+#define ORC_F16 1
+#define ORC_BF16 2
+#define ORC_F64 3
+
+/* binary16 -> double, exactly: sign, 5-bit exponent (bias 15), 10-bit fraction. */
+static double orc_half_to_double(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double mag;
+    if (e == 0)
+        mag = ldexp((double)f, -24); /* zero or subnormal: f * 2^-14 * 2^-10 */
+    else if (e == 31)
+        mag = f ? NAN : INFINITY;
+    else
+        mag = ldexp((double)(1024 + f), e - 25); /* (1 + f/1024) * 2^(e-15) */
+    return sign ? -mag : mag;
+}
+
+/* bfloat16 -> double, exactly: bfloat16 is the upper half of a binary32. */
+static double orc_bf16_to_double(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float x;
+    memcpy(&x, &u, sizeof x);
+    return (double)x;
+}
+
+static double orc_load(const void* base, int dtype, int64_t idx) {
+    switch (dtype) {
+    case ORC_F32: return (double)((const float*)base)[idx];
+    case ORC_F16: return orc_half_to_double(((const uint16_t*)base)[idx]);
+    case ORC_BF16: return orc_bf16_to_double(((const uint16_t*)base)[idx]);
+    default: return ((const double*)base)[idx];
+    }
+}
+
+typedef struct {
+    const void *q, *k, *v;
+    int dtype, layout, causal;
+    int64_t B, H, N, D;
+    double scale;
+    const int64_t* rows; /* nrows triples (b, h, i) */
+    int64_t nrows;
+    double* o;   /* nrows * D */
+    double* lse; /* nrows */
+    int64_t first, last;
+    int status;
+} orc_job;
+
+static int64_t orc_index(const orc_job* J, int64_t b, int64_t h, int64_t i, int64_t d) {
+    if (J->layout == 0) return ((b * J->H + h) * J->N + i) * J->D + d;
+    return ((b * J->N + i) * J->H + h) * J->D + d;
+}
+
+static void* orc_worker(void* arg) {
+    orc_job* J = (orc_job*)arg;
+    const int64_t N = J->N, D = J->D;
+    double* srow = (double*)malloc(sizeof(double) * (size_t)N);
+    double* qrow = (double*)malloc(sizeof(double) * (size_t)D);
+    if (!srow || !qrow) {
+        free(srow);
+        free(qrow);
+        J->status = -1;
+        return NULL;
+    }
+    for (int64_t r = J->first; r < J->last; ++r) {
+        const int64_t b = J->rows[3 * r], h = J->rows[3 * r + 1], i = J->rows[3 * r + 2];
+        const int64_t jend = J->causal ? i + 1 : N; /* visible keys: 0 .. jend-1 */
+        double* o = J->o + r * D;
+        for (int64_t d = 0; d < D; ++d) qrow[d] = orc_load(J->q, J->dtype, orc_index(J, b, h, i, d));
+
+        /* pass 1: scaled scores and their maximum */
+        double m = -INFINITY;
+        for (int64_t j = 0; j < jend; ++j) {
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; ++d) dot += qrow[d] * orc_load(J->k, J->dtype, orc_index(J, b, h, j, d));
+            srow[j] = J->scale * dot;
+            if (srow[j] > m) m = srow[j];
+        }
+
+        /* pass 2: exponentials relative to the maximum, their sum, and the weighted sum of V rows */
+        double l = 0.0;
+        for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+        for (int64_t j = 0; j < jend; ++j) {
+            const double e = exp(srow[j] - m);
+            l += e;
+            for (int64_t d = 0; d < D; ++d) o[d] += e * orc_load(J->v, J->dtype, orc_index(J, b, h, j, d));
+        }
+        for (int64_t d = 0; d < D; ++d) o[d] /= l;
+        J->lse[r] = m + log(l);
+    }
+    free(srow);
+    free(qrow);
+    return NULL;
+}
+
+/*
+ * Computes O (nrows x D, fp64, row r for triple r) and lse (nrows, fp64) for the requested
+ * (b, h, i) triples.  nthreads >= 1 workers take contiguous slices of the triple list.
+ * Returns 0 on success, -2 on a bad argument, -1 if memory for the row buffers ran out.
+ */
+int fa_oracle_rows(const void* q, const void* k, const void* v, int dtype, int layout, int64_t B,
+                   int64_t H, int64_t N, int64_t D, int causal, double scale, const int64_t* rows,
+                   int64_t nrows, double* o_out, double* lse_out, int nthreads) {
+    if (!q || !k || !v || !rows || !o_out || !lse_out) return -2;
+    if (dtype < 0 || dtype > 3 || layout < 0 || layout > 1) return -2;
+    if (B < 1 || H < 1 || N < 1 || D < 1 || nrows < 0) return -2;
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+        if (b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= N) return -2;
+    }
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 512) nthreads = 512;
+    if (nrows < nthreads) nthreads = nrows > 0 ? (int)nrows : 1;
+
+    orc_job* jobs = (orc_job*)calloc((size_t)nthreads, sizeof(orc_job));
+    pthread_t* tids = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    char* running = (char*)calloc((size_t)nthreads, 1);
+    if (!jobs || !tids || !running) {
+        free(jobs);
+        free(tids);
+        free(running);
+        return -1;
+    }
+    int status = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        orc_job* J = &jobs[t];
+        J->q = q; J->k = k; J->v = v;
+        J->dtype = dtype; J->layout = layout; J->causal = causal ? 1 : 0;
+        J->B = B; J->H = H; J->N = N; J->D = D;
+        J->scale = scale;
+        J->rows = rows; J->nrows = nrows;
+        J->o = o_out; J->lse = lse_out;
+        J->first = nrows * t / nthreads;
+        J->last = nrows * (t + 1) / nthreads;
+    }
+    for (int t = 1; t < nthreads; ++t) {
+        /* a worker that cannot be started has its slice done on this thread instead */
+        if (pthread_create(&tids[t], NULL, orc_worker, &jobs[t]) == 0)
+            running[t] = 1;
+        else
+            orc_worker(&jobs[t]);
+    }
+    orc_worker(&jobs[0]);
+    for (int t = 1; t < nthreads; ++t)
+        if (running[t]) pthread_join(tids[t], NULL);
+    for (int t = 0; t < nthreads; ++t)
+        if (jobs[t].status) status = jobs[t].status;
+    free(jobs);
+    free(tids);
+    free(running);
+    return status;
+}

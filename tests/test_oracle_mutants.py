@@ -1,0 +1,104 @@
+"""Plant plausible mistakes in a copy of the oracle's C source and check that the pins catch every one.
+
+Runs on the CPU only: each mutant is compiled with gcc into a temporary directory and called through
+ctypes; the committed oracle is never modified.
+"""
+import ctypes
+import math
+import os
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+from tests import bruteforce
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "fa_oracle.c")
+
+MUTANTS = {
+    "dropped_scale": ("srow[j] = J->scale * dot;", "srow[j] = dot;"),
+    "flipped_sign": ("srow[j] = J->scale * dot;", "srow[j] = -J->scale * dot;"),
+    "causal_excludes_diagonal": ("J->causal ? i + 1 : N", "J->causal ? (i > 0 ? i : 1) : N"),
+    "causal_one_extra_key": ("J->causal ? i + 1 : N", "J->causal ? (i + 2 < N ? i + 2 : N) : N"),
+    "no_max_subtraction": ("exp(srow[j] - m)", "exp(srow[j])"),
+    "bsnd_read_as_bhsd": ("return ((b * J->N + i) * J->H + h) * J->D + d;", "return ((b * J->H + h) * J->N + i) * J->D + d;"),
+    "key_row_index_is_query": ("qrow[d] * orc_load(J->k, J->dtype, orc_index(J, b, h, j, d))",
+                               "qrow[d] * orc_load(J->k, J->dtype, orc_index(J, b, h, i, d))"),
+    "value_row_index_is_query": ("e * orc_load(J->v, J->dtype, orc_index(J, b, h, j, d))",
+                                 "e * orc_load(J->v, J->dtype, orc_index(J, b, h, i, d))"),
+    "log2_lse": ("J->lse[r] = m + log(l);", "J->lse[r] = m + log2(l);"),
+    "no_normalisation": ("o[d] /= l;", "o[d] /= 1.0;"),
+    "fp16_exponent_bias": ("e - 25", "e - 24"),
+    "bf16_wrong_half": ("(uint32_t)b << 16", "(uint32_t)b << 15"),
+}
+
+
+def _build(tmp, name, old, new):
+    src = open(SRC).read()
+    assert old == "" or src.count(old) == 1, name
+    path = os.path.join(tmp, name + ".c")
+    open(path, "w").write(src.replace(old, new) if old else src)
+    lib = os.path.join(tmp, name + ".so")
+    subprocess.check_call(["gcc", "-O1", "-shared", "-fPIC", "-pthread", path, "-o", lib, "-lm"])
+    f = ctypes.CDLL(lib).fa_oracle_rows
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 2 + [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_double,
+                 ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    return f
+
+
+def _call(f, q, k, v, dtype, layout, causal, scale):
+    B, X, Y, D = q.shape
+    B, H, N = (B, X, Y) if layout == 0 else (B, Y, X)
+    b, h, i = np.meshgrid(np.arange(B), np.arange(H), np.arange(N), indexing="ij")
+    rows = np.ascontiguousarray(np.stack([b.ravel(), h.ravel(), i.ravel()], 1).astype(np.int64))
+    o = np.empty((rows.shape[0], D))
+    lse = np.empty(rows.shape[0])
+    rc = f(q.ctypes.data, k.ctypes.data, v.ctypes.data, dtype, layout, B, H, N, D, causal, scale,
+           rows.ctypes.data, rows.shape[0], o.ctypes.data, lse.ctypes.data, 1)
+    assert rc == 0
+    return o.reshape(B, H, N, D), lse.reshape(B, H, N)
+
+
+def _pins_pass(f):
+    """A compact subset of the pins; True iff the library passes all of them."""
+    rng = np.random.default_rng(5)
+    for causal in (0, 1):
+        q, k, v = (rng.standard_normal((2, 3, 11, 8)) for _ in range(3))
+        o, lse = _call(f, q, k, v, 3, 0, causal, 0.4)
+        o_bf, lse_bf, _ = bruteforce.attention_bhsd(q, k, v, causal=bool(causal), scale=0.4)
+        if not (np.allclose(o, o_bf, atol=1e-12) and np.allclose(lse, lse_bf, atol=1e-12)):
+            return False
+        t = lambda x: np.ascontiguousarray(x.transpose(0, 2, 1, 3))
+        o2, lse2 = _call(f, t(q), t(k), t(v), 3, 1, causal, 0.4)
+        if not (np.allclose(o2, o_bf, atol=1e-12) and np.allclose(lse2, lse_bf, atol=1e-12)):
+            return False
+    # large logits: a missing max subtraction overflows
+    q = np.zeros((1, 1, 5, 2)); k = np.zeros((1, 1, 5, 2)); v = rng.standard_normal((1, 1, 5, 2))
+    q[..., 0] = 100.0; k[0, 0, :, 0] = np.arange(5) * 10.0
+    o, lse = _call(f, q, k, v, 3, 0, 0, 1.0)
+    if not (np.allclose(o[0, 0], v[0, 0, 4], atol=1e-12) and np.allclose(lse, 4000.0)):
+        return False
+    # stored 16-bit types: N = 1 returns the widened v
+    vals = np.array([1.0, -2.5, 6.1e-5, 1234.5], dtype=np.float32)
+    for dt, bits, expect in ((1, vals.astype(np.float16).view(np.uint16), vals.astype(np.float16).astype(np.float64)),
+                             (2, (vals.view(np.uint32) >> 16).astype(np.uint16),
+                              ((vals.view(np.uint32) >> 16) << 16).view(np.float32).astype(np.float64))):
+        vv = np.ascontiguousarray(bits.reshape(1, 1, 1, 4))
+        o, _ = _call(f, np.zeros_like(vv), np.zeros_like(vv), vv, dt, 0, 0, 1.0)
+        if not np.array_equal(o.ravel(), expect):
+            return False
+    return True
+
+
+def test_unmutated_copy_passes():
+    with tempfile.TemporaryDirectory() as tmp:
+        assert _pins_pass(_build(tmp, "original", "", ""))
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    old, new = MUTANTS[name]
+    with tempfile.TemporaryDirectory() as tmp:
+        assert not _pins_pass(_build(tmp, name, old, new)), "pins missed mutant " + name
