@@ -50,7 +50,7 @@ extern "C" {
 #define FA_ERR_BAD_LAYOUT 3        /* layout is not FA_LAYOUT_* */
 #define FA_ERR_BAD_DTYPE 4         /* dtype is not FA_DTYPE_* */
 #define FA_ERR_UNSUPPORTED 5       /* D not in {64, 128}, or sizes beyond the limits below */
-#define FA_ERR_BAD_SCALE 6         /* scale is NaN or infinite */
+#define FA_ERR_BAD_SCALE 6         /* scale is NaN or infinite, or |scale|*log2(e) overflows fp32 */
 #define FA_ERR_MISALIGNED 7        /* a base pointer is not 16-byte aligned */
 #define FA_ERR_ALIAS 8             /* o or lse overlaps an input, or o overlaps lse */
 #define FA_ERR_NOT_DEVICE_MEMORY 9 /* a pointer is not device memory of the current device */

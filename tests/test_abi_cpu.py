@@ -1,0 +1,108 @@
+"""The C-ABI library loads, exports what include/fa.h declares, and rejects bad arguments before any
+HIP call (so these run on a host without a GPU)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import transformer_attention_fwd_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "fa.h")).read()
+    return sorted(set(re.findall(r"^\S[^\n(]*?\b(fa_\w+)\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    declared = _declared()
+    assert declared == ["fa_fwd", "fa_last_error", "fa_status_str", "fa_version"]
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], stdout=subprocess.PIPE,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.split() and l.split()[1] == "T"}
+    for name in declared:
+        assert name in exported, name
+    lib = fa.load()
+    for name in declared:
+        assert hasattr(lib, name)
+
+
+def test_header_constants_match_binding():
+    src = open(os.path.join(ROOT, "include", "fa.h")).read()
+    consts = dict((m[0], int(m[1])) for m in re.findall(r"#define (FA_\w+) (\d+)", src))
+    assert consts["FA_LAYOUT_BHSD"] == fa.LAYOUT_BHSD and consts["FA_LAYOUT_BSND"] == fa.LAYOUT_BSND
+    assert consts["FA_DTYPE_FP32"] == fa.DTYPE_FP32 and consts["FA_DTYPE_FP16"] == fa.DTYPE_FP16
+    assert consts["FA_DTYPE_BF16"] == fa.DTYPE_BF16
+    for name in ("FA_OK", "FA_ERR_NULL", "FA_ERR_BAD_DIM", "FA_ERR_BAD_LAYOUT", "FA_ERR_BAD_DTYPE",
+                 "FA_ERR_UNSUPPORTED", "FA_ERR_BAD_SCALE", "FA_ERR_MISALIGNED", "FA_ERR_ALIAS",
+                 "FA_ERR_NOT_DEVICE_MEMORY", "FA_ERR_HIP"):
+        assert consts[name] == getattr(fa, name), name
+
+
+def test_status_strings_and_version():
+    assert fa.version() == 100
+    for st in range(11):
+        assert fa.status_str(st)
+    assert fa.status_str(0) == "ok"
+    assert fa.status_str(999) == "unknown status"
+
+
+# Fake, distinct, 16-byte aligned "device" addresses; pure argument checks must fail before any HIP call.
+SZ = 1 << 40
+Q, K, V, O, L = (0x10000000000 + i * (SZ * 4) for i in range(5))
+GOOD = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, N=64, D=64, layout=0, causal=0, scale=0.125, dtype=2, stream=0)
+
+
+def _call(**kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["D"], a["layout"],
+                     a["causal"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), fa.FA_ERR_NULL), (dict(k=0), fa.FA_ERR_NULL), (dict(v=0), fa.FA_ERR_NULL),
+    (dict(o=0), fa.FA_ERR_NULL), (dict(lse=0), fa.FA_ERR_NULL),
+    (dict(layout=2), fa.FA_ERR_BAD_LAYOUT), (dict(layout=-1), fa.FA_ERR_BAD_LAYOUT),
+    (dict(dtype=3), fa.FA_ERR_BAD_DTYPE), (dict(dtype=-1), fa.FA_ERR_BAD_DTYPE),
+    (dict(B=0), fa.FA_ERR_BAD_DIM), (dict(H=0), fa.FA_ERR_BAD_DIM), (dict(N=0), fa.FA_ERR_BAD_DIM),
+    (dict(D=0), fa.FA_ERR_BAD_DIM), (dict(N=-5), fa.FA_ERR_BAD_DIM),
+    (dict(D=96), fa.FA_ERR_UNSUPPORTED), (dict(D=256), fa.FA_ERR_UNSUPPORTED), (dict(D=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=(1 << 30) + 1), fa.FA_ERR_UNSUPPORTED), (dict(B=1 << 20, H=1 << 12), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=1 << 40, H=1 << 40), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), fa.FA_ERR_BAD_SCALE), (dict(scale=float("inf")), fa.FA_ERR_BAD_SCALE),
+    (dict(scale=3.0e38), fa.FA_ERR_BAD_SCALE),
+    (dict(q=Q + 8), fa.FA_ERR_MISALIGNED), (dict(lse=L + 4), fa.FA_ERR_MISALIGNED),
+    (dict(o=Q), fa.FA_ERR_ALIAS), (dict(o=K + 64), fa.FA_ERR_ALIAS), (dict(lse=V + 1024), fa.FA_ERR_ALIAS),
+    (dict(lse=O + 16), fa.FA_ERR_ALIAS),
+])
+def test_pure_argument_checks(kw, status):
+    assert _call(**kw) == status
+
+
+def test_check_order_null_before_layout_before_dims():
+    assert _call(q=0, layout=7, B=0) == fa.FA_ERR_NULL
+    assert _call(layout=7, dtype=9) == fa.FA_ERR_BAD_LAYOUT
+    assert _call(dtype=9, B=0) == fa.FA_ERR_BAD_DTYPE
+    assert _call(B=0, D=96) == fa.FA_ERR_BAD_DIM
+    assert _call(D=96, scale=float("nan")) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_inputs_may_alias_each_other():
+    # q, k, v are read-only and may share memory (self-attention on one buffer): not an alias error.
+    # Without a GPU the call then stops at the device checks, never with FA_ERR_ALIAS.
+    st = _call(k=Q, v=Q)
+    assert st != fa.FA_ERR_ALIAS and st != fa.FA_OK
+
+
+def test_wrapper_rejects_shape_mismatch_before_calling():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 2, 8, 64)
+    with pytest.raises(ValueError):
+        fa.attention(q, torch.zeros(1, 2, 9, 64), q)
+    with pytest.raises(ValueError):
+        fa.attention(q, q, q, layout="BNSD")
+    with pytest.raises(TypeError):
+        fa.attention(q.double(), q.double(), q.double())

@@ -1,0 +1,135 @@
+// fa_api.cpp -- the C-ABI entry point of libfa.so: argument checks, device-residency checks, dispatch.
+//
+// Pure argument checks come first and touch no HIP API, so they behave the same on a host without a
+// GPU.  The error conventions answer the deployment page's error table (hwcomputing.csdn.net/
+// 6a0d4444..., section on common errors: host tensors crashing the operator, wrong input layout,
+// head-count mismatch): every bad call returns a status code and launches nothing.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+
+#define FA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+void set_error(const char* what, hipError_t e) {
+  snprintf(g_last_error, sizeof g_last_error, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+// Device memory of the current device (plain device allocation or managed memory).
+int check_device(const void* ptr, int device) {
+  hipPointerAttribute_t attr;
+  memset(&attr, 0, sizeof attr);
+  hipError_t e = hipPointerGetAttributes(&attr, ptr);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky "invalid value" a host pointer can leave
+    return FA_ERR_NOT_DEVICE_MEMORY;
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged) return FA_ERR_NOT_DEVICE_MEMORY;
+  if (attr.device != device) return FA_ERR_NOT_DEVICE_MEMORY;
+  return FA_OK;
+}
+
+}  // namespace
+
+FA_API const char* fa_status_str(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "null pointer";
+    case FA_ERR_BAD_DIM: return "B, H, N and D must be >= 1";
+    case FA_ERR_BAD_LAYOUT: return "layout must be FA_LAYOUT_BHSD or FA_LAYOUT_BSND";
+    case FA_ERR_BAD_DTYPE: return "dtype must be FA_DTYPE_FP32, FA_DTYPE_FP16 or FA_DTYPE_BF16";
+    case FA_ERR_UNSUPPORTED: return "unsupported size: D must be 64 or 128, N <= 2^30, B*H < 2^31";
+    case FA_ERR_BAD_SCALE: return "scale must be finite";
+    case FA_ERR_MISALIGNED: return "tensor base pointers must be 16-byte aligned";
+    case FA_ERR_ALIAS: return "o and lse must not overlap the inputs or each other";
+    case FA_ERR_NOT_DEVICE_MEMORY: return "a pointer is not device memory of the current device";
+    case FA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+FA_API const char* fa_last_error(void) { return g_last_error; }
+
+FA_API int fa_version(void) { return 100; }  // 0.1.0
+
+FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                  int64_t N, int64_t D, int layout, int causal, float scale, int dtype, void* stream) {
+  // ---- pure argument checks (no HIP calls) ----
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (layout != FA_LAYOUT_BHSD && layout != FA_LAYOUT_BSND) return FA_ERR_BAD_LAYOUT;
+  if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_BAD_DTYPE;
+  if (B < 1 || H < 1 || N < 1 || D < 1) return FA_ERR_BAD_DIM;
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  int64_t bh, rows, elems, bytes, lse_bytes;
+  const int64_t esize = dtype == FA_DTYPE_FP32 ? 4 : 2;
+  if (N > (int64_t(1) << 30) || !mul_ok(B, H, &bh) || bh > INT32_MAX || !mul_ok(bh, N, &rows) ||
+      !mul_ok(rows, D, &elems) || !mul_ok(elems, esize, &bytes) || !mul_ok(rows, 4, &lse_bytes))
+    return FA_ERR_UNSUPPORTED;
+  // grid: one workgroup per (b, h, query tile); must fit a 32-bit grid dimension
+  const int64_t qpw = fa::queries_per_workgroup(dtype == FA_DTYPE_FP32 ? fa::kDtypeFp32 : fa::kDtypeBf16);
+  if (bh * ((N + qpw - 1) / qpw) > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  if (!isfinite(scale) || !isfinite(fabsf(scale) * 1.4426950408889634f)) return FA_ERR_BAD_SCALE;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15) return FA_ERR_MISALIGNED;
+  if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes) ||
+      overlaps(lse, lse_bytes, q, bytes) || overlaps(lse, lse_bytes, k, bytes) ||
+      overlaps(lse, lse_bytes, v, bytes) || overlaps(lse, lse_bytes, o, bytes))
+    return FA_ERR_ALIAS;
+
+  // ---- device residency ----
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) {
+    set_error("hipGetDevice", e);
+    return FA_ERR_HIP;
+  }
+  const void* ptrs[5] = {q, k, v, o, lse};
+  for (const void* ptr : ptrs) {
+    const int st = check_device(ptr, device);
+    if (st != FA_OK) return st;
+  }
+
+  // ---- launch ----
+  fa::Params p;
+  memset(&p, 0, sizeof p);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = (int)B;
+  p.H = (int)H;
+  p.N = (int)N;
+  p.stride_b = H * N * D;
+  if (layout == FA_LAYOUT_BHSD) {
+    p.stride_h = N * D;
+    p.stride_s = D;
+  } else {
+    p.stride_h = D;
+    p.stride_s = H * D;
+  }
+  p.c = fabsf(scale) * 1.4426950408889634f;  // |scale| * log2(e)
+  p.qsign = scale < 0.0f ? (dtype == FA_DTYPE_FP32 ? 0x80000000u : 0x80008000u) : 0u;
+  const int kd = dtype == FA_DTYPE_FP32 ? fa::kDtypeFp32 : dtype == FA_DTYPE_FP16 ? fa::kDtypeFp16 : fa::kDtypeBf16;
+  e = fa::launch(p, kd, (int)D, causal != 0, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    set_error("kernel launch", e);
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}

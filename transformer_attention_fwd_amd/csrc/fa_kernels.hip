@@ -1,0 +1,590 @@
+// fa_kernels.hip -- attention forward kernels for gfx950 (MI355X, CDNA4).
+//
+// What is computed: O = softmax(scale * Q K^T [+ causal mask]) V and lse = ln sum_j exp(scale * q.k_j),
+// one (batch, head, 128-query tile) per workgroup, walking the K/V tiles with a running row maximum and
+// running exponential sum so that the score matrix only ever exists as a register tile.
+//   * Formula and tiling: page "FlashAttention：让长文本推理不再"卡显存"" (ai6s.net/6a0d42d8...),
+//     sections "Attention 的显存黑洞" and "1. 分块计算（Tiling）".
+//   * Running (m, l) update: same page, section "2. 在线归一化（Online Softmax）".  The page leaves
+//     the output update implicit; the accumulator is multiplied by the same exp(m_old - m_new) as l and
+//     divided by l at the end, the reading under which tiles reproduce the global softmax.
+//   * lse output [B, H, N]: page ai6s.net/6a140d07..., section "第二层：数值稳定性增强".
+//   * Causal diagonal skipping: page hwcomputing.csdn.net/6a0d4681..., section "Causal Mask的实现差异",
+//     mode 2, with the exact rule "K tile visited iff its first key <= the tile's last query" and an
+//     element mask (key > query) on the tiles that straddle the diagonal.
+//   * Q tiles outer, K/V tiles inner, K/V re-read per Q tile: page hwcomputing.csdn.net/6a0d4681...,
+//     section "分块策略：不是越大越好", constraint 2.
+//
+// gfx950 design (16-bit inputs):
+//   * 4 waves x 32 queries = 128 queries per workgroup; K/V tiles of 64 keys.
+//   * MFMA v_mfma_f32_16x16x32_{bf16,f16}.  The kernel computes S^T = K Q^T and O^T = V^T P^T, so a
+//     lane's accumulator registers all belong to one query (lane % 16): the softmax rescale is a
+//     per-lane scalar, row reductions are in-lane plus two cross-lane steps, and the exponentiated
+//     S^T registers are already laid out as the B operand of the P.V product (no LDS round trip).
+//   * Q stays in VGPRs for the whole workgroup (B operand of S^T = K Q^T).
+//   * K/V: global_load_lds_dwordx4 straight into a 2-stage LDS ring; the 16-byte chunk XOR swizzle is
+//     applied on the global side (each lane fetches the chunk that belongs at its LDS slot).
+//   * V^T operand: ds_read_b64_tr_b16 (transposing LDS read) from the row-major V tile.
+//   * exp2 with scale*log2(e) folded into one FMA; the reference maximum only moves when the new block
+//     maximum exceeds it by more than 2^8 (a deferred rescale, exact up to rounding).
+//   * Causal: per-wave skip of K tiles wholly above the wave's queries; element mask only on tiles
+//     crossing the diagonal or the sequence end.
+//   * Workgroup -> (head, Q tile) order: every XCD takes a contiguous run of heads (its L2 then holds
+//     those heads' K/V), heaviest causal Q tiles first.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "fa_launch.h"
+
+namespace fa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kNegInf = -__builtin_inff();
+// deferred rescale threshold, in log2 units: probabilities stay below 2^8 before renormalising
+constexpr float kRescaleThreshold = 8.0f;
+
+// s_waitcnt immediate for "vmcnt <= n" on gfx9-family encodings (expcnt and lgkmcnt left free).
+__device__ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// s_waitcnt immediate for "lgkmcnt == 0" (vmcnt and expcnt left free).
+__device__ constexpr int waitcnt_lgkm0() { return 15 | (3 << 14) | (7 << 4); }
+
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// Workgroup barrier for LDS hand-offs: the caller has already waited for the loads it needs.
+__device__ __forceinline__ void lds_barrier() {
+  compiler_fence();
+  __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+}
+
+// Block index -> (b*H + h, q_tile).  Workgroups reach the 8 XCDs round robin; XCD x gets a
+// contiguous run of the head-major unit list, heaviest causal tiles first inside each head.
+__device__ __forceinline__ void unit_of(int bid, int n_units, int n_qtiles, bool causal, int& bh, int& qt) {
+  constexpr int X = 8;
+  const int x = bid % X, u = bid / X;
+  const int base = n_units / X, rem = n_units % X;
+  const int L = x * base + (x < rem ? x : rem) + u;
+  bh = L / n_qtiles;
+  const int r = L - bh * n_qtiles;
+  qt = causal ? n_qtiles - 1 - r : r;
+}
+
+__device__ __forceinline__ float wave_max_xor16_32(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+__device__ __forceinline__ float wave_sum_xor16_32(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+template <bool IS_BF16>
+struct Elem;
+template <>
+struct Elem<true> {
+  typedef bf16x8_t vec8;
+  __device__ static __forceinline__ uint32_t pack2(float a, float b) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    bf16x2_t v;
+    v[0] = (__bf16)a;
+    v[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static __forceinline__ f32x4_t mfma(const vec8& a, const vec8& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  // acc + (sum of the two packed values), the values exactly as the P.V product sees them
+  __device__ static __forceinline__ float sum2(uint32_t pk, float acc) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), one, acc, false);
+  }
+};
+template <>
+struct Elem<false> {
+  typedef f16x8_t vec8;
+  __device__ static __forceinline__ uint32_t pack2(float a, float b) {
+    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+    f16x2_t v;
+    v[0] = (_Float16)a;
+    v[1] = (_Float16)b;
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static __forceinline__ f32x4_t mfma(const vec8& a, const vec8& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ float sum2(uint32_t pk, float acc) {
+    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+    const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk), one, acc, false);
+  }
+};
+
+// ------------------------------------------------------------------------------------------------
+// 16-bit inputs (bf16 / fp16)
+// ------------------------------------------------------------------------------------------------
+template <int D>
+struct Tile16 {
+  static constexpr int NW = 4;              // waves per workgroup
+  static constexpr int QW = 32;             // queries per wave
+  static constexpr int BM = NW * QW;        // queries per workgroup
+  static constexpr int BN = 64;             // keys per K/V tile
+  static constexpr int QG = QW / 16;        // 16-query groups per wave
+  static constexpr int DC = D / 32;         // 32-wide d chunks (k dimension of S^T = K Q^T)
+  static constexpr int DT = D / 16;         // 16-wide d tiles (rows of O^T)
+  static constexpr int KT = BN / 16;        // 16-key tiles (rows of S^T)
+  static constexpr int KC = BN / 32;        // 32-key chunks (k dimension of O^T = V^T P^T)
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int CHUNKS = D / 8;      // 16-byte chunks per row
+  static constexpr int TILE_BYTES = BN * ROW_BYTES;
+  static constexpr int LOADS = TILE_BYTES / (16 * 64 * NW);  // 16-byte DMA loads per lane per tensor
+  // XOR swizzle of the 16-byte chunk index within a row, chosen so that 16 consecutive rows read at
+  // one logical chunk land in 16 distinct 16-byte bank groups of a 256-byte bank line.
+  __device__ static __forceinline__ int swz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+};
+
+template <int D, bool IS_BF16, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
+  typedef Tile16<D> T;
+  typedef Elem<IS_BF16> E;
+  typedef typename E::vec8 vec8;
+  // Two stages for K and two for V, as four separate LDS objects: with the stage fixed at compile
+  // time the compiler can tell that reads of one stage do not depend on the DMA filling the other.
+  __shared__ __attribute__((aligned(1024))) uint8_t ks0[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks1[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs0[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs1[T::TILE_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;    // lane group 0..3
+  const int li = lane & 15;   // index within the group
+
+  int bh, qt;
+  unit_of(blockIdx.x, p.n_units, p.n_qtiles, CAUSAL, bh, qt);
+  const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
+  const int N = p.N;
+  const int q_wg = qt * T::BM;
+  const int q0 = q_wg + wave * T::QW;
+
+  const uint16_t* __restrict__ qg_ptr = (const uint16_t*)p.q + b * p.stride_b + h * p.stride_h;
+  const uint8_t* __restrict__ kg_ptr = (const uint8_t*)p.k + 2 * (b * p.stride_b + h * p.stride_h);
+  const uint8_t* __restrict__ vg_ptr = (const uint8_t*)p.v + 2 * (b * p.stride_b + h * p.stride_h);
+  const int64_t row_bytes_g = 2 * p.stride_s;
+
+  // ---- number of K/V tiles this workgroup visits ----
+  const int last_key = CAUSAL ? min(N - 1, q_wg + T::BM - 1) : N - 1;
+  const int n_kt = last_key / T::BN + 1;
+
+  // ---- K/V tile DMA: lane slot -> (row, logical chunk) with the swizzle applied on the global side ----
+  auto issue_tile = [&](int j, uint8_t* kdst, uint8_t* vdst) {
+    const int key0 = j * T::BN;
+#pragma unroll
+    for (int i = 0; i < T::LOADS; ++i) {
+      const int slot = (i * T::NW + wave) * 64 + lane;  // 16-byte slot within the tile
+      const int row = slot / T::CHUNKS;
+      const int pc = slot % T::CHUNKS;
+      const int lc = pc ^ T::swz(row);
+      const int key = min(key0 + row, N - 1);          // rows past the end are fetched clamped, then masked
+      const int64_t goff = key * row_bytes_g + lc * 16;
+      const int lds_off = (i * T::NW + wave) * 1024;    // wave-uniform base; lane lands at +16*lane
+      __builtin_amdgcn_global_load_lds((const void*)(kg_ptr + goff), (lds_void_t*)(kdst + lds_off), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vg_ptr + goff), (lds_void_t*)(vdst + lds_off), 16, 0, 0);
+    }
+  };
+
+  issue_tile(0, ks0, vs0);
+
+  // ---- Q fragments (B operand of S^T = K Q^T): lane holds q[q0 + 16*qg + li][32*c + 8*g .. +7] ----
+  vec8 qf[T::QG][T::DC];
+#pragma unroll
+  for (int qg = 0; qg < T::QG; ++qg) {
+    const int qrow = min(q0 + 16 * qg + li, N - 1);
+#pragma unroll
+    for (int c = 0; c < T::DC; ++c) {
+      u32x4_t raw = *(const u32x4_t*)(qg_ptr + qrow * p.stride_s + 32 * c + 8 * g);
+      raw ^= p.qsign;  // exact negation when scale < 0 (the exponent then uses |scale|)
+      qf[qg][c] = __builtin_bit_cast(vec8, raw);
+    }
+  }
+
+  const float cexp = p.c;  // |scale| * log2(e)
+  float m_ref[T::QG], l_part[T::QG], u_part[T::QG];
+  f32x4_t oacc[T::QG][T::DT];
+#pragma unroll
+  for (int qg = 0; qg < T::QG; ++qg) {
+    m_ref[qg] = kNegInf;
+    l_part[qg] = 0.f;
+    u_part[qg] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt) oacc[qg][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // One K/V tile: wait for its DMA, prefetch the next one into the other stage, compute.
+  // The last tile is a separate compile-time variant (no prefetch, full wait) so that every wait on
+  // the DMA counter is unconditional and the compiler adds none of its own before LDS reads.
+  auto step = [&](int j, const uint8_t* ks, const uint8_t* vs, uint8_t* kn, uint8_t* vn, auto last_c) {
+    if constexpr (!decltype(last_c)::value) {
+      issue_tile(j + 1, kn, vn);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * T::LOADS));
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+    lds_barrier();  // tile j is in LDS for every wave
+
+    const int key0 = j * T::BN;
+    const bool active = !CAUSAL || key0 <= q0 + T::QW - 1;
+    if (active) {
+      // ---- S^T = K Q^T : s[qg][kt] holds keys key0 + 16*kt + 4*g + r for query q0 + 16*qg + li ----
+      f32x4_t s[T::QG][T::KT];
+#pragma unroll
+      for (int kt = 0; kt < T::KT; ++kt) {
+#pragma unroll
+        for (int qg = 0; qg < T::QG; ++qg) s[qg][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int row = 16 * kt + li;
+#pragma unroll
+        for (int c = 0; c < T::DC; ++c) {
+          const int lc = 4 * c + g;
+          const vec8 kf = *(const vec8*)(ks + row * T::ROW_BYTES + ((lc ^ T::swz(row)) << 4));
+#pragma unroll
+          for (int qg = 0; qg < T::QG; ++qg) s[qg][kt] = E::mfma(kf, qf[qg][c], s[qg][kt]);
+        }
+      }
+
+      // ---- mask, online softmax, P ----
+      const bool need_mask = (CAUSAL && key0 + T::BN - 1 > q0) || (key0 + T::BN > N);
+      uint32_t pf[T::QG][T::KC][4];
+#pragma unroll
+      for (int qg = 0; qg < T::QG; ++qg) {
+        const int qi = q0 + 16 * qg + li;
+        if (need_mask) {
+#pragma unroll
+          for (int kt = 0; kt < T::KT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int key = key0 + 16 * kt + 4 * g + r;
+              if ((CAUSAL && key > qi) || key >= N) s[qg][kt][r] = kNegInf;
+            }
+        }
+        float mx = kNegInf;
+#pragma unroll
+        for (int kt = 0; kt < T::KT; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[qg][kt][r]);
+        mx = wave_max_xor16_32(mx);
+        const float mx_c = (mx == kNegInf) ? kNegInf : mx * cexp;
+        const float m_cand = fmaxf(m_ref[qg], mx_c);
+        const bool move = m_cand > m_ref[qg] + kRescaleThreshold;
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {  // wave-uniform branch
+          const float m_new = move ? m_cand : m_ref[qg];
+          const float alpha = __builtin_amdgcn_exp2f(m_ref[qg] - m_new);
+          l_part[qg] *= alpha;
+          u_part[qg] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < T::DT; ++dt) oacc[qg][dt] *= alpha;
+          m_ref[qg] = m_new;
+        }
+        const float neg_m = -m_ref[qg];
+        // Two row sums: l of the fp32 probabilities (for lse), and u of the probabilities after
+        // rounding to the input type, i.e. exactly the weights the P.V product applies (the divisor of
+        // O, which then stays a convex combination of V rows however peaked the row is).
+        float rowsum = 0.f, used0 = 0.f, used1 = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < T::KT; ++kt) {
+          float pv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float x = __builtin_fmaf(s[qg][kt][r], cexp, neg_m);
+            if (need_mask && s[qg][kt][r] == kNegInf) x = kNegInf;
+            pv[r] = __builtin_amdgcn_exp2f(x);
+            rowsum += pv[r];
+          }
+          const int kc = kt >> 1, half = kt & 1;
+          const uint32_t pk0 = E::pack2(pv[0], pv[1]);
+          const uint32_t pk1 = E::pack2(pv[2], pv[3]);
+          pf[qg][kc][2 * half + 0] = pk0;
+          pf[qg][kc][2 * half + 1] = pk1;
+          used0 = E::sum2(pk0, used0);
+          used1 = E::sum2(pk1, used1);
+        }
+        l_part[qg] += rowsum;
+        u_part[qg] += used0 + used1;
+      }
+
+      // ---- O^T += V^T P^T ----
+#pragma unroll
+      for (int kc = 0; kc < T::KC; ++kc) {
+        vec8 pb[T::QG];
+#pragma unroll
+        for (int qg = 0; qg < T::QG; ++qg) {
+          u32x4_t w = {pf[qg][kc][0], pf[qg][kc][1], pf[qg][kc][2], pf[qg][kc][3]};
+          pb[qg] = __builtin_bit_cast(vec8, w);
+        }
+        // transposing read: lanes 4e..4e+3 of each 16-lane group address row e; lane li receives
+        // column li of those four rows.
+        const int vrow = 32 * kc + 4 * g + (li >> 2);
+#pragma unroll
+        for (int dt = 0; dt < T::DT; ++dt) {
+          const int col = 16 * dt + 4 * (li & 3);        // element column of this lane's 4-element read
+          const int lc = col >> 3, off = (col & 7) * 2;
+          const uint8_t* a0 = vs + vrow * T::ROW_BYTES + ((lc ^ T::swz(vrow)) << 4) + off;
+          const uint8_t* a1 = vs + (vrow + 16) * T::ROW_BYTES + ((lc ^ T::swz(vrow + 16)) << 4) + off;
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a0);
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a1);
+          u32x4_t w = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
+                       __builtin_bit_cast(u32x2_t, hi)[0], __builtin_bit_cast(u32x2_t, hi)[1]};
+          const vec8 vf = __builtin_bit_cast(vec8, w);
+#pragma unroll
+          for (int qg = 0; qg < T::QG; ++qg) oacc[qg][dt] = E::mfma(vf, pb[qg], oacc[qg][dt]);
+        }
+      }
+    }
+    lds_barrier();  // every wave is done with this stage before it is refilled
+  };
+
+  const std::integral_constant<bool, false> more;
+  const std::integral_constant<bool, true> last;
+  int j = 0;
+  for (; j + 2 < n_kt; j += 2) {
+    step(j, ks0, vs0, ks1, vs1, more);
+    step(j + 1, ks1, vs1, ks0, vs0, more);
+  }
+  if (j + 2 == n_kt) {
+    step(j, ks0, vs0, ks1, vs1, more);
+    step(j + 1, ks1, vs1, ks0, vs0, last);
+  } else {
+    step(j, ks0, vs0, ks1, vs1, last);
+  }
+
+  // ---- epilogue: O = acc / l, lse = (m + log2 l) ln 2 ----
+  uint16_t* og_ptr = (uint16_t*)p.o + b * p.stride_b + h * p.stride_h;
+#pragma unroll
+  for (int qg = 0; qg < T::QG; ++qg) {
+    const float l = wave_sum_xor16_32(l_part[qg]);
+    const float inv = 1.0f / wave_sum_xor16_32(u_part[qg]);
+    const int qi = q0 + 16 * qg + li;
+    if (qi < N) {
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt) {
+        const f32x4_t o = oacc[qg][dt] * inv;
+        u32x2_t w = {E::pack2(o[0], o[1]), E::pack2(o[2], o[3])};
+        *(u32x2_t*)(og_ptr + qi * p.stride_s + 16 * dt + 4 * g) = w;
+      }
+      if (g == 0) p.lse[(int64_t)bh * N + qi] = (m_ref[qg] + __builtin_log2f(l)) * kLn2;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// fp32 inputs: the same S^T / O^T formulation on v_mfma_f32_16x16x4_f32 (fp32 end to end).
+// ------------------------------------------------------------------------------------------------
+template <int D>
+struct Tile32 {
+  static constexpr int NW = 4;
+  static constexpr int QW = 32;
+  static constexpr int BM = NW * QW;
+  static constexpr int BN = 32;
+  static constexpr int QG = QW / 16;
+  static constexpr int DK = D / 4;       // k steps of S^T = K Q^T
+  static constexpr int DT = D / 16;      // 16-wide d tiles of O^T
+  static constexpr int KT = BN / 16;
+  static constexpr int LD = D + 4;       // padded LDS row (floats)
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void fa_fwd_32(Params p) {
+  typedef Tile32<D> T;
+  __shared__ float ks[T::BN * T::LD];
+  __shared__ float vs[T::BN * T::LD];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4, li = lane & 15;
+
+  int bh, qt;
+  unit_of(blockIdx.x, p.n_units, p.n_qtiles, CAUSAL, bh, qt);
+  const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
+  const int N = p.N;
+  const int q_wg = qt * T::BM;
+  const int q0 = q_wg + wave * T::QW;
+  const float* qg_ptr = (const float*)p.q + b * p.stride_b + h * p.stride_h;
+  const float* kg_ptr = (const float*)p.k + b * p.stride_b + h * p.stride_h;
+  const float* vg_ptr = (const float*)p.v + b * p.stride_b + h * p.stride_h;
+  const float qsign = p.qsign ? -1.0f : 1.0f;
+
+  // Q^T fragments: lane holds q[q0 + 16*qg + li][4*kk + g]
+  float qf[T::QG][T::DK];
+#pragma unroll
+  for (int qg = 0; qg < T::QG; ++qg) {
+    const int qrow = min(q0 + 16 * qg + li, N - 1);
+#pragma unroll
+    for (int kk = 0; kk < T::DK; ++kk) qf[qg][kk] = qsign * qg_ptr[qrow * p.stride_s + 4 * kk + g];
+  }
+  const int last_key = CAUSAL ? min(N - 1, q_wg + T::BM - 1) : N - 1;
+  const int n_kt = last_key / T::BN + 1;
+  const float cexp = p.c;
+  float m_ref[T::QG], l_part[T::QG];
+  f32x4_t oacc[T::QG][T::DT];
+#pragma unroll
+  for (int qg = 0; qg < T::QG; ++qg) {
+    m_ref[qg] = kNegInf;
+    l_part[qg] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt) oacc[qg][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  for (int j = 0; j < n_kt; ++j) {
+    const int key0 = j * T::BN;
+    // stage K, V tile through registers (16-byte loads, padded rows)
+    for (int idx = threadIdx.x; idx < T::BN * (D / 4); idx += 256) {
+      const int row = idx / (D / 4), c4 = idx % (D / 4);
+      const int key = min(key0 + row, N - 1);
+      const float4 kv = *(const float4*)(kg_ptr + key * p.stride_s + 4 * c4);
+      const float4 vv = *(const float4*)(vg_ptr + key * p.stride_s + 4 * c4);
+      *(float4*)(ks + row * T::LD + 4 * c4) = kv;
+      *(float4*)(vs + row * T::LD + 4 * c4) = vv;
+    }
+    __syncthreads();
+    const bool active = !CAUSAL || key0 <= q0 + T::QW - 1;
+    if (active) {
+      f32x4_t s[T::QG][T::KT];
+#pragma unroll
+      for (int kt = 0; kt < T::KT; ++kt) {
+#pragma unroll
+        for (int qg = 0; qg < T::QG; ++qg) s[qg][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < T::DK; ++kk) {
+          const float kf = ks[(16 * kt + li) * T::LD + 4 * kk + g];
+#pragma unroll
+          for (int qg = 0; qg < T::QG; ++qg) s[qg][kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf, qf[qg][kk], s[qg][kt], 0, 0, 0);
+        }
+      }
+      const bool need_mask = (CAUSAL && key0 + T::BN - 1 > q0) || (key0 + T::BN > N);
+#pragma unroll
+      for (int qg = 0; qg < T::QG; ++qg) {
+        const int qi = q0 + 16 * qg + li;
+        if (need_mask) {
+#pragma unroll
+          for (int kt = 0; kt < T::KT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int key = key0 + 16 * kt + 4 * g + r;
+              if ((CAUSAL && key > qi) || key >= N) s[qg][kt][r] = kNegInf;
+            }
+        }
+        float mx = kNegInf;
+#pragma unroll
+        for (int kt = 0; kt < T::KT; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[qg][kt][r]);
+        mx = wave_max_xor16_32(mx);
+        const float mx_c = (mx == kNegInf) ? kNegInf : mx * cexp;
+        const float m_cand = fmaxf(m_ref[qg], mx_c);
+        const bool move = m_cand > m_ref[qg] + kRescaleThreshold;
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+          const float m_new = move ? m_cand : m_ref[qg];
+          const float alpha = __builtin_amdgcn_exp2f(m_ref[qg] - m_new);
+          l_part[qg] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < T::DT; ++dt) oacc[qg][dt] *= alpha;
+          m_ref[qg] = m_new;
+        }
+        const float neg_m = -m_ref[qg];
+#pragma unroll
+        for (int kt = 0; kt < T::KT; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float x = __builtin_fmaf(s[qg][kt][r], cexp, neg_m);
+            if (need_mask && s[qg][kt][r] == kNegInf) x = kNegInf;
+            const float pv = __builtin_amdgcn_exp2f(x);
+            s[qg][kt][r] = pv;
+            l_part[qg] += pv;
+          }
+      }
+      // O^T += V^T P^T, one k step per (kt, r): key slot g <-> key 16*kt + 4*g + r
+#pragma unroll
+      for (int kt = 0; kt < T::KT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int vrow = 16 * kt + 4 * g + r;
+#pragma unroll
+          for (int dt = 0; dt < T::DT; ++dt) {
+            const float vf = vs[vrow * T::LD + 16 * dt + li];
+#pragma unroll
+            for (int qg = 0; qg < T::QG; ++qg)
+              oacc[qg][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(vf, s[qg][kt][r], oacc[qg][dt], 0, 0, 0);
+          }
+        }
+    }
+    __syncthreads();
+  }
+
+  float* og_ptr = (float*)p.o + b * p.stride_b + h * p.stride_h;
+#pragma unroll
+  for (int qg = 0; qg < T::QG; ++qg) {
+    const float l = wave_sum_xor16_32(l_part[qg]);
+    const float inv = 1.0f / l;
+    const int qi = q0 + 16 * qg + li;
+    if (qi < N) {
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt) {
+        const f32x4_t o = oacc[qg][dt] * inv;
+        *(float4*)(og_ptr + qi * p.stride_s + 16 * dt + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
+      }
+      if (g == 0) p.lse[(int64_t)bh * N + qi] = (m_ref[qg] + __builtin_log2f(l)) * kLn2;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// launchers
+// ------------------------------------------------------------------------------------------------
+template <int D, bool IS_BF16, bool CAUSAL>
+static hipError_t launch16(Params p, hipStream_t stream) {
+  typedef Tile16<D> T;
+  p.n_qtiles = (p.N + T::BM - 1) / T::BM;
+  p.n_units = p.n_qtiles * p.B * p.H;
+  hipLaunchKernelGGL((fa_fwd_16<D, IS_BF16, CAUSAL>), dim3(p.n_units), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch32(Params p, hipStream_t stream) {
+  typedef Tile32<D> T;
+  p.n_qtiles = (p.N + T::BM - 1) / T::BM;
+  p.n_units = p.n_qtiles * p.B * p.H;
+  hipLaunchKernelGGL((fa_fwd_32<D, CAUSAL>), dim3(p.n_units), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch(const Params& p, int dtype, int d, bool causal, hipStream_t stream) {
+  if (dtype == kDtypeBf16) {
+    if (d == 128) return causal ? launch16<128, true, true>(p, stream) : launch16<128, true, false>(p, stream);
+    return causal ? launch16<64, true, true>(p, stream) : launch16<64, true, false>(p, stream);
+  }
+  if (dtype == kDtypeFp16) {
+    if (d == 128) return causal ? launch16<128, false, true>(p, stream) : launch16<128, false, false>(p, stream);
+    return causal ? launch16<64, false, true>(p, stream) : launch16<64, false, false>(p, stream);
+  }
+  if (d == 128) return causal ? launch32<128, true>(p, stream) : launch32<128, false>(p, stream);
+  return causal ? launch32<64, true>(p, stream) : launch32<64, false>(p, stream);
+}
+
+int queries_per_workgroup(int dtype) { return dtype == kDtypeFp32 ? Tile32<64>::BM : Tile16<64>::BM; }
+
+}  // namespace fa

@@ -67,12 +67,12 @@ WORKLOADS = {
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """fp32 -> bfloat16 bit patterns (uint16), round to nearest, ties to even; NaN stays NaN."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    out = rounded.astype(np.uint16)
+    u = x.view(np.uint32)
+    # u + 0x7FFF + lsb cannot wrap for finite values or infinities (largest pattern 0xFF800000)
+    out = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
-        out[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
+        out[nan] = ((u[nan] >> np.uint32(16)) | np.uint32(0x40)).astype(np.uint16)
     return out
 
 
