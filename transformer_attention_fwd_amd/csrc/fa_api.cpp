@@ -123,7 +123,10 @@ FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* l
     p.stride_h = D;
     p.stride_s = H * D;
   }
-  p.c = fabsf(scale) * 1.4426950408889634f;  // |scale| * log2(e)
+  // |scale| * log2(e).  The kernels need it positive (masked -inf scores then give exp2(-inf) = 0); a
+  // zero scale becomes FLT_MIN, which keeps every visible weight exactly 1 in fp32 for any logit below
+  // about 2^100 in magnitude, and lse = ln(count) to within FLT_MIN * |logit|.
+  p.c = scale == 0.0f ? 1.17549435e-38f : fabsf(scale) * 1.4426950408889634f;
   p.qsign = scale < 0.0f ? (dtype == FA_DTYPE_FP32 ? 0x80000000u : 0x80008000u) : 0u;
   const int kd = dtype == FA_DTYPE_FP32 ? fa::kDtypeFp32 : dtype == FA_DTYPE_FP16 ? fa::kDtypeFp16 : fa::kDtypeBf16;
   e = fa::launch(p, kd, (int)D, causal != 0, (hipStream_t)stream);

@@ -61,9 +61,19 @@ __device__ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) 
 __device__ constexpr int waitcnt_lgkm0() { return 15 | (3 << 14) | (7 << 4); }
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
-// An empty volatile asm statement inside a wave-uniform branch keeps the compiler from turning the
-// branch into selects that would run on every tile.
 __device__ __forceinline__ void keep_branch() { asm volatile(""); }
+__device__ __forceinline__ float quad_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 // Workgroup barrier for LDS hand-offs: the caller has already waited for the loads it needs.
 __device__ __forceinline__ void lds_barrier() {
@@ -143,8 +153,8 @@ struct Elem<false> {
 // ------------------------------------------------------------------------------------------------
 template <int D>
 struct Tile16 {
-  static constexpr int NW = 4;              // waves per workgroup (one per SIMD)
-  static constexpr int QW = 64;             // queries per wave
+  static constexpr int NW = 4;              // waves per workgroup
+  static constexpr int QW = 32;             // queries per wave
   static constexpr int BM = NW * QW;        // queries per workgroup
   static constexpr int BN = 64;             // keys per K/V tile
   static constexpr int QG = QW / 16;        // 16-query groups per wave
@@ -155,275 +165,235 @@ struct Tile16 {
   static constexpr int ROW_BYTES = D * 2;
   static constexpr int CHUNKS = D / 8;      // 16-byte chunks per row
   static constexpr int TILE_BYTES = BN * ROW_BYTES;
-  static constexpr int LOADS = TILE_BYTES / (16 * 64 * NW);  // 16-byte DMA loads per lane per tile
-  // XOR swizzles of the 16-byte chunk index within a row (K and V tiles have their own).
-  // K is read 16 rows x one 16-byte chunk per 16-lane group: the rows must land in 16 distinct
-  // 16-byte bank groups of a 256-byte bank line.
+  static constexpr int LOADS = TILE_BYTES / (16 * 64 * NW);  // 16-byte DMA loads per lane per tensor
   __device__ static __forceinline__ int swz_k(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
-  // V is read by ds_read_b64_tr_b16: 32 lanes cover 8 rows x two adjacent chunks (2*dt, 2*dt + 1);
-  // XOR-ing bits 1..3 only keeps the two chunks apart and spreads the 8 rows over the bank line.
   __device__ static __forceinline__ int swz_v(int row) { return D == 128 ? ((row & 7) << 1) : (((row >> 1) & 3) << 1); }
 };
 
-// max / sum over the four lanes {l, l^16, l^32, l^48} that hold one query's scores
-__device__ __forceinline__ float quad_max(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float quad_sum(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
 template <int D, bool IS_BF16, bool CAUSAL>
-struct Fwd16 {
+__global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
   typedef Tile16<D> T;
   typedef Elem<IS_BF16> E;
   typedef typename E::vec8 vec8;
+  // Two stages for K and two for V, as four separate LDS objects: with the stage fixed at compile
+  // time the compiler can tell that reads of one stage do not depend on the DMA filling the other.
+  __shared__ __attribute__((aligned(1024))) uint8_t ks0[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks1[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs0[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs1[T::TILE_BYTES];
 
-  // per-wave state, all in registers
-  vec8 qf[T::QG][T::DC];              // Q fragments (B operand of S^T = K Q^T)
-  f32x4_t oacc[T::QG][T::DT];         // O^T accumulators: query 16*qg + li, d = 16*dt + 4*g + r
-  float m_ref[T::QG], l_part[T::QG], u_part[T::QG];
-  int lane, wave, g, li, q0, N, n_kt, n_act;
-  float cexp;
-  const uint8_t* kg;
-  const uint8_t* vg;
-  int64_t row_bytes_g;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4;    // lane group 0..3
+  const int li = lane & 15;   // index within the group
 
-  __device__ __forceinline__ void issue(const uint8_t* src, int j, uint8_t* dst, bool is_v) const {
+  int bh, qt;
+  unit_of(blockIdx.x, p.n_units, p.n_qtiles, CAUSAL, bh, qt);
+  const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
+  const int N = p.N;
+  const int q_wg = qt * T::BM;
+  const int q0 = q_wg + wave * T::QW;
+
+  const uint16_t* __restrict__ qg_ptr = (const uint16_t*)p.q + b * p.stride_b + h * p.stride_h;
+  const uint8_t* __restrict__ kg_ptr = (const uint8_t*)p.k + 2 * (b * p.stride_b + h * p.stride_h);
+  const uint8_t* __restrict__ vg_ptr = (const uint8_t*)p.v + 2 * (b * p.stride_b + h * p.stride_h);
+  const int64_t row_bytes_g = 2 * p.stride_s;
+
+  // ---- number of K/V tiles this workgroup visits ----
+  const int last_key = CAUSAL ? min(N - 1, q_wg + T::BM - 1) : N - 1;
+  const int n_kt = last_key / T::BN + 1;
+
+  // ---- K/V tile DMA: lane slot -> (row, logical chunk) with the swizzle applied on the global side ----
+  auto issue_tile = [&](int j, uint8_t* kdst, uint8_t* vdst) {
     const int key0 = j * T::BN;
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
       const int slot = (i * T::NW + wave) * 64 + lane;  // 16-byte slot within the tile
       const int row = slot / T::CHUNKS;
       const int pc = slot % T::CHUNKS;
-      const int key = min(key0 + row, N - 1);          // rows past the end are fetched clamped, then masked
-      const int lc = pc ^ (is_v ? T::swz_v(row) : T::swz_k(row));
-      const int64_t goff = key * row_bytes_g + lc * 16;
-      __builtin_amdgcn_global_load_lds((const void*)(src + goff), (lds_void_t*)(dst + (i * T::NW + wave) * 1024), 16, 0, 0);
+      const int key = min(key0 + row, N - 1);
+      const int64_t gk = key * row_bytes_g + (pc ^ T::swz_k(row)) * 16;
+      const int64_t gv = key * row_bytes_g + (pc ^ T::swz_v(row)) * 16;
+      const int lds_off = (i * T::NW + wave) * 1024;
+      __builtin_amdgcn_global_load_lds((const void*)(kg_ptr + gk), (lds_void_t*)(kdst + lds_off), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(vg_ptr + gv), (lds_void_t*)(vdst + lds_off), 16, 0, 0);
     }
-  }
+  };
 
-  // S^T = K Q^T for one 64-key tile: s[qg][kt] = keys 16*kt + 4*g + r, query q0 + 16*qg + li
-  __device__ __forceinline__ void qk(const uint8_t* ks, f32x4_t (&s)[T::QG][T::KT]) const {
-#pragma unroll
-    for (int kt = 0; kt < T::KT; ++kt) {
-#pragma unroll
-      for (int qg = 0; qg < T::QG; ++qg) s[qg][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const int row = 16 * kt + li;
-#pragma unroll
-      for (int c = 0; c < T::DC; ++c) {
-        const vec8 kf = *(const vec8*)(ks + row * T::ROW_BYTES + (((4 * c + g) ^ T::swz_k(row)) << 4));
-#pragma unroll
-        for (int qg = 0; qg < T::QG; ++qg) s[qg][kt] = E::mfma(kf, qf[qg][c], s[qg][kt]);
-      }
-    }
-  }
+  issue_tile(0, ks0, vs0);
 
-  // online softmax of one tile for query group qg: P (packed input-type pairs), running m, l, u
-  __device__ __forceinline__ void softmax(f32x4_t (&s)[T::QG][T::KT], int qg, int key0, bool need_mask,
-                                          uint32_t (&pf)[T::QG][T::KC][4]) {
-    const int qi = q0 + 16 * qg + li;
-    if (need_mask) {  // wave-uniform; only the diagonal tile and the tile holding the sequence end
-      keep_branch();
-#pragma unroll
-      for (int kt = 0; kt < T::KT; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = key0 + 16 * kt + 4 * g + r;
-          if ((CAUSAL && key > qi) || key >= N) s[qg][kt][r] = kNegInf;
-        }
-    }
-    float mx = fmaxf(fmaxf(s[qg][0][0], s[qg][0][1]), fmaxf(s[qg][0][2], s[qg][0][3]));
-#pragma unroll
-    for (int kt = 1; kt < T::KT; ++kt)
-      mx = fmaxf(mx, fmaxf(fmaxf(s[qg][kt][0], s[qg][kt][1]), fmaxf(s[qg][kt][2], s[qg][kt][3])));
-    mx = quad_max(mx);
-    const float mx_c = (mx == kNegInf) ? kNegInf : mx * cexp;
-    const float m_cand = fmaxf(m_ref[qg], mx_c);
-    const bool move = m_cand > m_ref[qg] + kRescaleThreshold;
-    if (__builtin_amdgcn_ballot_w64(move) != 0) {  // wave-uniform branch, rarely taken after tile 0
-      keep_branch();
-      const float m_new = move ? m_cand : m_ref[qg];
-      const float alpha = __builtin_amdgcn_exp2f(m_ref[qg] - m_new);
-      l_part[qg] *= alpha;
-      u_part[qg] *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < T::DT; ++dt) oacc[qg][dt] *= alpha;
-      m_ref[qg] = m_new;
-    }
-    const float neg_m = -m_ref[qg];
-    // Two row sums: l of the fp32 probabilities (for lse), and u of the probabilities after rounding
-    // to the input type, i.e. exactly the weights the P.V product applies (the divisor of O, which
-    // then stays a convex combination of V rows however peaked the row is).
-    float rowsum = 0.f, used0 = 0.f, used1 = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < T::KT; ++kt) {
-      float pv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qg][kt][r], cexp, neg_m));
-      if (need_mask) {  // masked scores are -inf; zero their weight explicitly (scale 0 gives 0*inf)
-        keep_branch();
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (s[qg][kt][r] == kNegInf) pv[r] = 0.f;
-      }
-      rowsum += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-      const uint32_t pk0 = E::pack2(pv[0], pv[1]);
-      const uint32_t pk1 = E::pack2(pv[2], pv[3]);
-      pf[qg][kt >> 1][2 * (kt & 1) + 0] = pk0;
-      pf[qg][kt >> 1][2 * (kt & 1) + 1] = pk1;
-      used0 = E::sum2(pk0, used0);
-      used1 = E::sum2(pk1, used1);
-    }
-    l_part[qg] += rowsum;
-    u_part[qg] += used0 + used1;
-  }
-
-  // O^T += V^T P^T for one tile
-  __device__ __forceinline__ void pv(const uint8_t* vs, const uint32_t (&pf)[T::QG][T::KC][4]) {
-#pragma unroll
-    for (int kc = 0; kc < T::KC; ++kc) {
-      vec8 pb[T::QG];
-#pragma unroll
-      for (int qg = 0; qg < T::QG; ++qg) {
-        u32x4_t w = {pf[qg][kc][0], pf[qg][kc][1], pf[qg][kc][2], pf[qg][kc][3]};
-        pb[qg] = __builtin_bit_cast(vec8, w);
-      }
-      // transposing read: lanes 4e..4e+3 of each 16-lane group address row e; lane li receives
-      // column li of those four rows.
-      const int vrow = 32 * kc + 4 * g + (li >> 2);
-#pragma unroll
-      for (int dt = 0; dt < T::DT; ++dt) {
-        const int col = 16 * dt + 4 * (li & 3);  // element column of this lane's 4-element read
-        const int lc = col >> 3, off = (col & 7) * 2;
-        const uint8_t* a0 = vs + vrow * T::ROW_BYTES + ((lc ^ T::swz_v(vrow)) << 4) + off;
-        const uint8_t* a1 = vs + (vrow + 16) * T::ROW_BYTES + ((lc ^ T::swz_v(vrow + 16)) << 4) + off;
-        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a0);
-        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a1);
-        u32x4_t w = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
-                     __builtin_bit_cast(u32x2_t, hi)[0], __builtin_bit_cast(u32x2_t, hi)[1]};
-        const vec8 vf = __builtin_bit_cast(vec8, w);
-#pragma unroll
-        for (int qg = 0; qg < T::QG; ++qg) oacc[qg][dt] = E::mfma(vf, pb[qg], oacc[qg][dt]);
-      }
-    }
-  }
-
-  __device__ __forceinline__ bool needs_mask(int j) const {
-    const int key0 = j * T::BN;
-    return (CAUSAL && key0 + T::BN - 1 > q0) || (key0 + T::BN > N);
-  }
-
-  // One pipelined iteration: tile j's softmax and P.V, tile j+1's S^T.  K(j+1) is read from kr,
-  // V(j) from vr; K(j+2) is fetched into kw and V(j+1) into vw meanwhile.
-  __device__ __forceinline__ void iteration(int j, f32x4_t (&s_cur)[T::QG][T::KT], f32x4_t (&s_next)[T::QG][T::KT],
-                                            const uint8_t* kr, const uint8_t* vr, uint8_t* kw, uint8_t* vw) {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // K(j+1) and V(j) have landed (this wave's part)
-    lds_barrier();                              // ... for every wave; tile j-1's stages are free
-    if (j + 2 < n_kt) issue(kg, j + 2, kw, false);
-    if (j + 1 < n_kt) issue(vg, j + 1, vw, true);
-    uint32_t pf[T::QG][T::KC][4];
-    const bool act = j < n_act;
-    if (j + 1 < n_act) qk(kr, s_next);
-    if (act) {
-      const bool nm = needs_mask(j);
-#pragma unroll
-      for (int qg = 0; qg < T::QG; ++qg) softmax(s_cur, qg, j * T::BN, nm, pf);
-      pv(vr, pf);
-    }
-  }
-};
-
-template <int D, bool IS_BF16, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void fa_fwd_16(Params p) {
-  typedef Tile16<D> T;
-  typedef Fwd16<D, IS_BF16, CAUSAL> F;
-  typedef typename F::vec8 vec8;
-  // Two stages each for K and V, as four separate LDS objects: with the stage fixed at compile time
-  // the compiler can tell that reads of one stage do not depend on the DMA filling another.
-  __shared__ __attribute__((aligned(1024))) uint8_t ks0[T::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t ks1[T::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs0[T::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs1[T::TILE_BYTES];
-
-  F f;
-  f.lane = threadIdx.x & 63;
-  f.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  f.g = f.lane >> 4;
-  f.li = f.lane & 15;
-
-  int bh, qt;
-  unit_of(blockIdx.x, p.n_units, p.n_qtiles, CAUSAL, bh, qt);
-  const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
-  f.N = p.N;
-  const int q_wg = qt * T::BM;
-  f.q0 = q_wg + f.wave * T::QW;
-  f.cexp = p.c;
-  f.row_bytes_g = 2 * p.stride_s;
-  f.kg = (const uint8_t*)p.k + 2 * (b * p.stride_b + h * p.stride_h);
-  f.vg = (const uint8_t*)p.v + 2 * (b * p.stride_b + h * p.stride_h);
-
-  // K/V tiles visited by the workgroup, and by this wave (causal: tiles past the wave's last query
-  // are skipped by the wave, which still takes part in the loads and barriers)
-  const int last_key = CAUSAL ? min(f.N - 1, q_wg + T::BM - 1) : f.N - 1;
-  f.n_kt = last_key / T::BN + 1;
-  f.n_act = CAUSAL ? min(f.n_kt, (f.q0 + T::QW - 1) / T::BN + 1) : f.n_kt;
-
-  f.issue(f.kg, 0, ks0, false);
-
-  const uint16_t* qg_ptr = (const uint16_t*)p.q + b * p.stride_b + h * p.stride_h;
+  // ---- Q fragments (B operand of S^T = K Q^T): lane holds q[q0 + 16*qg + li][32*c + 8*g .. +7] ----
+  vec8 qf[T::QG][T::DC];
 #pragma unroll
   for (int qg = 0; qg < T::QG; ++qg) {
-    const int qrow = min(f.q0 + 16 * qg + f.li, f.N - 1);
+    const int qrow = min(q0 + 16 * qg + li, N - 1);
 #pragma unroll
     for (int c = 0; c < T::DC; ++c) {
-      u32x4_t raw = *(const u32x4_t*)(qg_ptr + qrow * p.stride_s + 32 * c + 8 * f.g);
+      u32x4_t raw = *(const u32x4_t*)(qg_ptr + qrow * p.stride_s + 32 * c + 8 * g);
       raw ^= p.qsign;  // exact negation when scale < 0 (the exponent then uses |scale|)
-      f.qf[qg][c] = __builtin_bit_cast(vec8, raw);
+      qf[qg][c] = __builtin_bit_cast(vec8, raw);
     }
-    f.m_ref[qg] = kNegInf;
-    f.l_part[qg] = 0.f;
-    f.u_part[qg] = 0.f;
+  }
+
+  const float cexp = p.c;  // |scale| * log2(e)
+  float m_ref[T::QG], l_part[T::QG], u_part[T::QG];
+  f32x4_t oacc[T::QG][T::DT];
 #pragma unroll
-    for (int dt = 0; dt < T::DT; ++dt) f.oacc[qg][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int qg = 0; qg < T::QG; ++qg) {
+    m_ref[qg] = kNegInf;
+    l_part[qg] = 0.f;
+    u_part[qg] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt) oacc[qg][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  f32x4_t sa[T::QG][T::KT], sb[T::QG][T::KT];
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  lds_barrier();
-  if (1 < f.n_kt) f.issue(f.kg, 1, ks1, false);
-  f.issue(f.vg, 0, vs0, true);
-  f.qk(ks0, sa);  // every wave visits tile 0
+  // One K/V tile: wait for its DMA, prefetch the next one into the other stage, compute.
+  // The last tile is a separate compile-time variant (no prefetch, full wait) so that every wait on
+  // the DMA counter is unconditional and the compiler adds none of its own before LDS reads.
+  auto step = [&](int j, const uint8_t* ks, const uint8_t* vs, uint8_t* kn, uint8_t* vn, auto last_c) {
+    if constexpr (!decltype(last_c)::value) {
+      issue_tile(j + 1, kn, vn);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * T::LOADS));
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+    lds_barrier();  // tile j is in LDS for every wave
 
+    const int key0 = j * T::BN;
+    const bool active = !CAUSAL || key0 <= q0 + T::QW - 1;
+    if (active) {
+      // ---- S^T = K Q^T : s[qg][kt] holds keys key0 + 16*kt + 4*g + r for query q0 + 16*qg + li ----
+      f32x4_t s[T::QG][T::KT];
+#pragma unroll
+      for (int kt = 0; kt < T::KT; ++kt) {
+#pragma unroll
+        for (int qg = 0; qg < T::QG; ++qg) s[qg][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int row = 16 * kt + li;
+#pragma unroll
+        for (int c = 0; c < T::DC; ++c) {
+          const int lc = 4 * c + g;
+          const vec8 kf = *(const vec8*)(ks + row * T::ROW_BYTES + ((lc ^ T::swz_k(row)) << 4));
+#pragma unroll
+          for (int qg = 0; qg < T::QG; ++qg) s[qg][kt] = E::mfma(kf, qf[qg][c], s[qg][kt]);
+        }
+      }
+
+      // ---- mask, online softmax, P ----
+      const bool need_mask = (CAUSAL && key0 + T::BN - 1 > q0) || (key0 + T::BN > N);
+      uint32_t pf[T::QG][T::KC][4];
+#pragma unroll
+      for (int qg = 0; qg < T::QG; ++qg) {
+        const int qi = q0 + 16 * qg + li;
+        if (need_mask) {
+          keep_branch();
+#pragma unroll
+          for (int kt = 0; kt < T::KT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int key = key0 + 16 * kt + 4 * g + r;
+              if ((CAUSAL && key > qi) || key >= N) s[qg][kt][r] = kNegInf;
+            }
+        }
+        float mx = kNegInf;
+#pragma unroll
+        for (int kt = 0; kt < T::KT; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[qg][kt][r]);
+        mx = quad_max(mx);
+        const float mx_c = (mx == kNegInf) ? kNegInf : mx * cexp;
+        const float m_cand = fmaxf(m_ref[qg], mx_c);
+        const bool move = m_cand > m_ref[qg] + kRescaleThreshold;
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {
+          keep_branch();
+          const float m_new = move ? m_cand : m_ref[qg];
+          const float alpha = __builtin_amdgcn_exp2f(m_ref[qg] - m_new);
+          l_part[qg] *= alpha;
+          u_part[qg] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < T::DT; ++dt) oacc[qg][dt] *= alpha;
+          m_ref[qg] = m_new;
+        }
+        const float neg_m = -m_ref[qg];
+        float rowsum = 0.f, used0 = 0.f, used1 = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < T::KT; ++kt) {
+          float pv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qg][kt][r], cexp, neg_m));
+          rowsum += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+          const int kc = kt >> 1, half = kt & 1;
+          const uint32_t pk0 = E::pack2(pv[0], pv[1]);
+          const uint32_t pk1 = E::pack2(pv[2], pv[3]);
+          pf[qg][kc][2 * half + 0] = pk0;
+          pf[qg][kc][2 * half + 1] = pk1;
+          used0 = E::sum2(pk0, used0);
+          used1 = E::sum2(pk1, used1);
+        }
+        l_part[qg] += rowsum;
+        u_part[qg] += used0 + used1;
+        u_part[qg] += used0 + used1;
+      }
+
+      // ---- O^T += V^T P^T ----
+#pragma unroll
+      for (int kc = 0; kc < T::KC; ++kc) {
+        vec8 pb[T::QG];
+#pragma unroll
+        for (int qg = 0; qg < T::QG; ++qg) {
+          u32x4_t w = {pf[qg][kc][0], pf[qg][kc][1], pf[qg][kc][2], pf[qg][kc][3]};
+          pb[qg] = __builtin_bit_cast(vec8, w);
+        }
+        // transposing read: lanes 4e..4e+3 of each 16-lane group address row e; lane li receives
+        // column li of those four rows.
+        const int vrow = 32 * kc + 4 * g + (li >> 2);
+#pragma unroll
+        for (int dt = 0; dt < T::DT; ++dt) {
+          const int col = 16 * dt + 4 * (li & 3);        // element column of this lane's 4-element read
+          const int lc = col >> 3, off = (col & 7) * 2;
+          const uint8_t* a0 = vs + vrow * T::ROW_BYTES + ((lc ^ T::swz_v(vrow)) << 4) + off;
+          const uint8_t* a1 = vs + (vrow + 16) * T::ROW_BYTES + ((lc ^ T::swz_v(vrow + 16)) << 4) + off;
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a0);
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a1);
+          u32x4_t w = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
+                       __builtin_bit_cast(u32x2_t, hi)[0], __builtin_bit_cast(u32x2_t, hi)[1]};
+          const vec8 vf = __builtin_bit_cast(vec8, w);
+#pragma unroll
+          for (int qg = 0; qg < T::QG; ++qg) oacc[qg][dt] = E::mfma(vf, pb[qg], oacc[qg][dt]);
+        }
+      }
+    }
+    lds_barrier();  // every wave is done with this stage before it is refilled
+  };
+
+  const std::integral_constant<bool, false> more;
+  const std::integral_constant<bool, true> last;
   int j = 0;
-  for (; j + 1 < f.n_kt; j += 2) {
-    f.iteration(j, sa, sb, ks1, vs0, ks0, vs1);
-    f.iteration(j + 1, sb, sa, ks0, vs1, ks1, vs0);
+  for (; j + 2 < n_kt; j += 2) {
+    step(j, ks0, vs0, ks1, vs1, more);
+    step(j + 1, ks1, vs1, ks0, vs0, more);
   }
-  if (j < f.n_kt) f.iteration(j, sa, sb, ks1, vs0, ks0, vs1);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  if (j + 2 == n_kt) {
+    step(j, ks0, vs0, ks1, vs1, more);
+    step(j + 1, ks1, vs1, ks0, vs0, last);
+  } else {
+    step(j, ks0, vs0, ks1, vs1, last);
+  }
 
-  // ---- epilogue: O = acc / u, lse = (m + log2 l) ln 2 ----
+  // ---- epilogue: O = acc / l, lse = (m + log2 l) ln 2 ----
   uint16_t* og_ptr = (uint16_t*)p.o + b * p.stride_b + h * p.stride_h;
 #pragma unroll
   for (int qg = 0; qg < T::QG; ++qg) {
-    const float l = quad_sum(f.l_part[qg]);
-    const float inv = 1.0f / quad_sum(f.u_part[qg]);
-    const int qi = f.q0 + 16 * qg + f.li;
-    if (qi < f.N) {
+    const float l = wave_sum_xor16_32(l_part[qg]);
+    const float inv = 1.0f / wave_sum_xor16_32(u_part[qg]);
+    const int qi = q0 + 16 * qg + li;
+    if (qi < N) {
 #pragma unroll
       for (int dt = 0; dt < T::DT; ++dt) {
-        const f32x4_t o = f.oacc[qg][dt] * inv;
-        u32x2_t w = {F::E::pack2(o[0], o[1]), F::E::pack2(o[2], o[3])};
-        *(u32x2_t*)(og_ptr + qi * p.stride_s + 16 * dt + 4 * f.g) = w;
+        const f32x4_t o = oacc[qg][dt] * inv;
+        u32x2_t w = {E::pack2(o[0], o[1]), E::pack2(o[2], o[3])};
+        *(u32x2_t*)(og_ptr + qi * p.stride_s + 16 * dt + 4 * g) = w;
       }
-      if (f.g == 0) p.lse[(int64_t)bh * f.N + qi] = (f.m_ref[qg] + __builtin_log2f(l)) * kLn2;
+      if (g == 0) p.lse[(int64_t)bh * N + qi] = (m_ref[qg] + __builtin_log2f(l)) * kLn2;
     }
   }
 }

@@ -23,7 +23,7 @@ struct Params {
   int B, H, N;
   int n_qtiles;   // filled by the launcher
   int n_units;    // filled by the launcher
-  float c;        // |scale| * log2(e)
+  float c;        // |scale| * log2(e), > 0 (a zero scale is passed as FLT_MIN by the entry point)
   uint32_t qsign; // XOR mask applied to Q's stored bits: flips the sign when scale < 0
 };
 
