@@ -56,7 +56,9 @@ extern "C" {
 #define FA_ERR_NOT_DEVICE_MEMORY 9 /* a pointer is not device memory of the current device */
 #define FA_ERR_HIP 10              /* the HIP runtime reported an error; see fa_last_error() */
 
-/* Limits: 1 <= N <= 2^30, B*H <= 2^31 - 1, and every tensor's byte size must fit in int64. */
+/* Limits: 1 <= N <= 2^30, B*H <= 2^31 - 1, every tensor's byte size must fit in int64, and one head's
+ * span -- (N - 1) * (bytes between consecutive positions) + D * element size -- must be below 2^31
+ * (BHSD bf16 D=128: N up to 8M; BSND: N * H * D * element size below 2 GiB). */
 
 /*
  * fa_fwd -- enqueue the attention forward on `stream` and return.

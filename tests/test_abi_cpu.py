@@ -106,3 +106,11 @@ def test_wrapper_rejects_shape_mismatch_before_calling():
         fa.attention(q, q, q, layout="BNSD")
     with pytest.raises(TypeError):
         fa.attention(q.double(), q.double(), q.double())
+
+
+def test_every_kernel_stub_is_defined():
+    # A kernel whose host-side stub failed to instantiate leaves an undefined __device_stub__ symbol:
+    # the library would then fail to load at run time.
+    out = subprocess.run(["nm", "-C", "--undefined-only", fa.library_path()], stdout=subprocess.PIPE, text=True,
+                         check=True).stdout
+    assert "__device_stub__" not in out, out

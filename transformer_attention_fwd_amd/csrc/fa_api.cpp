@@ -84,6 +84,10 @@ FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* l
   // grid: one workgroup per (b, h, query tile); must fit a 32-bit grid dimension
   const int64_t qpw = fa::queries_per_workgroup(dtype == FA_DTYPE_FP32 ? fa::kDtypeFp32 : fa::kDtypeBf16);
   if (bh * ((N + qpw - 1) / qpw) > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  // one head's rows, from its first element to the end of its last row, are addressed with 32-bit
+  // offsets from a per-head buffer descriptor
+  const int64_t row_stride_bytes = (layout == FA_LAYOUT_BHSD ? D : H * D) * esize;
+  if ((N - 1) * row_stride_bytes + D * esize > INT32_MAX) return FA_ERR_UNSUPPORTED;
   if (!isfinite(scale) || !isfinite(fabsf(scale) * 1.4426950408889634f)) return FA_ERR_BAD_SCALE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15) return FA_ERR_MISALIGNED;
   if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes) ||

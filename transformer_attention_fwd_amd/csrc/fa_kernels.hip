@@ -54,6 +54,8 @@ constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kNegInf = -__builtin_inff();
 // deferred rescale threshold, in log2 units: probabilities stay below 2^8 before renormalising
 constexpr float kRescaleThreshold = 8.0f;
+// word 3 of a buffer resource on gfx9-family parts: 32-bit data format, raw (unswizzled) addressing
+constexpr int kBufferFlags = 0x00020000;
 
 // s_waitcnt immediate for "vmcnt <= n" on gfx9-family encodings (expcnt and lgkmcnt left free).
 __device__ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -170,6 +172,20 @@ struct Tile16 {
   __device__ static __forceinline__ int swz_v(int row) { return D == 128 ? ((row & 7) << 1) : (((row >> 1) & 3) << 1); }
 };
 
+// Buffer loads of one K and one V tile straight into LDS: lane slot (i*NW + wave)*64 + lane of a tile
+// holds the global 16-byte chunk at byte offset voff[i] + soff from the head base.
+template <int LOADS, int NW>
+__device__ __forceinline__ void issue_kv_tile(__amdgpu_buffer_rsrc_t kbuf, __amdgpu_buffer_rsrc_t vbuf,
+                                              const int* voff_k, const int* voff_v, int soff, int wave,
+                                              uint8_t* kdst, uint8_t* vdst) {
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int lds_off = (i * NW + wave) * 1024;  // wave-uniform base; lane lands at +16*lane
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kbuf, (lds_void_t*)(kdst + lds_off), 16, voff_k[i], soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vbuf, (lds_void_t*)(vdst + lds_off), 16, voff_v[i], soff, 0, 0);
+  }
+}
+
 template <int D, bool IS_BF16, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
   typedef Tile16<D> T;
@@ -197,27 +213,29 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
   const uint16_t* __restrict__ qg_ptr = (const uint16_t*)p.q + b * p.stride_b + h * p.stride_h;
   const uint8_t* __restrict__ kg_ptr = (const uint8_t*)p.k + 2 * (b * p.stride_b + h * p.stride_h);
   const uint8_t* __restrict__ vg_ptr = (const uint8_t*)p.v + 2 * (b * p.stride_b + h * p.stride_h);
-  const int64_t row_bytes_g = 2 * p.stride_s;
 
   // ---- number of K/V tiles this workgroup visits ----
   const int last_key = CAUSAL ? min(N - 1, q_wg + T::BM - 1) : N - 1;
   const int n_kt = last_key / T::BN + 1;
 
-  // ---- K/V tile DMA: lane slot -> (row, logical chunk) with the swizzle applied on the global side ----
-  auto issue_tile = [&](int j, uint8_t* kdst, uint8_t* vdst) {
-    const int key0 = j * T::BN;
+  // ---- K/V tile DMA: buffer loads straight into LDS.  The (b, h) base and the valid byte range sit in
+  // a buffer descriptor (rows past the sequence end read as zeros and are masked); each lane adds a
+  // fixed offset -- the global chunk that belongs at its LDS slot, i.e. the XOR swizzle applied on the
+  // global side -- and each tile a uniform one. ----
+  const int row_bytes = (int)(2 * p.stride_s);
+  const int span = (N - 1) * row_bytes + T::ROW_BYTES;  // the host keeps this below 2^31
+  const __amdgpu_buffer_rsrc_t kbuf = __builtin_amdgcn_make_buffer_rsrc((void*)kg_ptr, 0, span, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vbuf = __builtin_amdgcn_make_buffer_rsrc((void*)vg_ptr, 0, span, kBufferFlags);
+  int voff_k[T::LOADS], voff_v[T::LOADS];
 #pragma unroll
-    for (int i = 0; i < T::LOADS; ++i) {
-      const int slot = (i * T::NW + wave) * 64 + lane;  // 16-byte slot within the tile
-      const int row = slot / T::CHUNKS;
-      const int pc = slot % T::CHUNKS;
-      const int key = min(key0 + row, N - 1);
-      const int64_t gk = key * row_bytes_g + (pc ^ T::swz_k(row)) * 16;
-      const int64_t gv = key * row_bytes_g + (pc ^ T::swz_v(row)) * 16;
-      const int lds_off = (i * T::NW + wave) * 1024;
-      __builtin_amdgcn_global_load_lds((const void*)(kg_ptr + gk), (lds_void_t*)(kdst + lds_off), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vg_ptr + gv), (lds_void_t*)(vdst + lds_off), 16, 0, 0);
-    }
+  for (int i = 0; i < T::LOADS; ++i) {
+    const int slot = (i * T::NW + wave) * 64 + lane;  // 16-byte slot within the LDS tile
+    const int row = slot / T::CHUNKS, pc = slot % T::CHUNKS;
+    voff_k[i] = row * row_bytes + ((pc ^ T::swz_k(row)) << 4);
+    voff_v[i] = row * row_bytes + ((pc ^ T::swz_v(row)) << 4);
+  }
+  auto issue_tile = [&](int j, uint8_t* kdst, uint8_t* vdst) {
+    issue_kv_tile<T::LOADS, T::NW>(kbuf, vbuf, voff_k, voff_v, j * T::BN * row_bytes, wave, kdst, vdst);
   };
 
   issue_tile(0, ks0, vs0);
@@ -251,13 +269,9 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
   // The last tile is a separate compile-time variant (no prefetch, full wait) so that every wait on
   // the DMA counter is unconditional and the compiler adds none of its own before LDS reads.
   auto step = [&](int j, const uint8_t* ks, const uint8_t* vs, uint8_t* kn, uint8_t* vn, auto last_c) {
-    if constexpr (!decltype(last_c)::value) {
-      issue_tile(j + 1, kn, vn);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * T::LOADS));
-    } else {
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    }
-    lds_barrier();  // tile j is in LDS for every wave
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's share of tile j has landed
+    lds_barrier();  // tile j is in LDS for every wave, and every wave is done with tile j-1
+    if constexpr (!decltype(last_c)::value) issue_tile(j + 1, kn, vn);  // into tile j-1's stage
 
     const int key0 = j * T::BN;
     const bool active = !CAUSAL || key0 <= q0 + T::QW - 1;
@@ -331,7 +345,6 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
         }
         l_part[qg] += rowsum;
         u_part[qg] += used0 + used1;
-        u_part[qg] += used0 + used1;
       }
 
       // ---- O^T += V^T P^T ----
@@ -362,7 +375,6 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
         }
       }
     }
-    lds_barrier();  // every wave is done with this stage before it is refilled
   };
 
   const std::integral_constant<bool, false> more;
