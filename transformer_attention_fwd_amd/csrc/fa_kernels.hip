@@ -277,19 +277,29 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
     const bool active = !CAUSAL || key0 <= q0 + T::QW - 1;
     if (active) {
       // ---- S^T = K Q^T : s[qg][kt] holds keys key0 + 16*kt + 4*g + r for query q0 + 16*qg + li ----
+      // the K fragments of 16-key tile kt+1 are read while tile kt's MFMAs run
       f32x4_t s[T::QG][T::KT];
+      auto k_frag = [&](int kt, int c) {
+        const int row = 16 * kt + li;
+        return *(const vec8*)(ks + row * T::ROW_BYTES + (((4 * c + g) ^ T::swz_k(row)) << 4));
+      };
+      vec8 kf[T::DC], kf_next[T::DC];
+#pragma unroll
+      for (int c = 0; c < T::DC; ++c) kf_next[c] = k_frag(0, c);
 #pragma unroll
       for (int kt = 0; kt < T::KT; ++kt) {
 #pragma unroll
-        for (int qg = 0; qg < T::QG; ++qg) s[qg][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const int row = 16 * kt + li;
+        for (int c = 0; c < T::DC; ++c) kf[c] = kf_next[c];
+        if (kt + 1 < T::KT) {
 #pragma unroll
-        for (int c = 0; c < T::DC; ++c) {
-          const int lc = 4 * c + g;
-          const vec8 kf = *(const vec8*)(ks + row * T::ROW_BYTES + ((lc ^ T::swz_k(row)) << 4));
-#pragma unroll
-          for (int qg = 0; qg < T::QG; ++qg) s[qg][kt] = E::mfma(kf, qf[qg][c], s[qg][kt]);
+          for (int c = 0; c < T::DC; ++c) kf_next[c] = k_frag(kt + 1, c);
         }
+#pragma unroll
+        for (int qg = 0; qg < T::QG; ++qg) s[qg][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < T::DC; ++c)
+#pragma unroll
+          for (int qg = 0; qg < T::QG; ++qg) s[qg][kt] = E::mfma(kf[c], qf[qg][c], s[qg][kt]);
       }
 
       // ---- mask, online softmax, P ----
@@ -348,30 +358,34 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
       }
 
       // ---- O^T += V^T P^T ----
+      // V^T fragments of (kc, dt) via transposing reads: lanes 4e..4e+3 of each 16-lane group address
+      // row e and lane li receives column li of those rows; read VA fragments ahead of their MFMAs
+      auto v_frag = [&](int f) {
+        const int kc = f / T::DT, dt = f % T::DT;
+        const int vrow = 32 * kc + 4 * g + (li >> 2);
+        const int col = 16 * dt + 4 * (li & 3);  // element column of this lane's 4-element read
+        const int lc = col >> 3, off = (col & 7) * 2;
+        const uint8_t* a0 = vs + vrow * T::ROW_BYTES + ((lc ^ T::swz_v(vrow)) << 4) + off;
+        const uint8_t* a1 = vs + (vrow + 16) * T::ROW_BYTES + ((lc ^ T::swz_v(vrow + 16)) << 4) + off;
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a0);
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a1);
+        u32x4_t w = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
+                     __builtin_bit_cast(u32x2_t, hi)[0], __builtin_bit_cast(u32x2_t, hi)[1]};
+        return __builtin_bit_cast(vec8, w);
+      };
+      constexpr int NF = T::KC * T::DT, VA = 4;
+      vec8 vring[VA];
 #pragma unroll
-      for (int kc = 0; kc < T::KC; ++kc) {
-        vec8 pb[T::QG];
+      for (int f = 0; f < VA; ++f) vring[f] = v_frag(f);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const vec8 vf = vring[f % VA];
+        if (f + VA < NF) vring[f % VA] = v_frag(f + VA);
+        const int kc = f / T::DT, dt = f % T::DT;
 #pragma unroll
         for (int qg = 0; qg < T::QG; ++qg) {
           u32x4_t w = {pf[qg][kc][0], pf[qg][kc][1], pf[qg][kc][2], pf[qg][kc][3]};
-          pb[qg] = __builtin_bit_cast(vec8, w);
-        }
-        // transposing read: lanes 4e..4e+3 of each 16-lane group address row e; lane li receives
-        // column li of those four rows.
-        const int vrow = 32 * kc + 4 * g + (li >> 2);
-#pragma unroll
-        for (int dt = 0; dt < T::DT; ++dt) {
-          const int col = 16 * dt + 4 * (li & 3);        // element column of this lane's 4-element read
-          const int lc = col >> 3, off = (col & 7) * 2;
-          const uint8_t* a0 = vs + vrow * T::ROW_BYTES + ((lc ^ T::swz_v(vrow)) << 4) + off;
-          const uint8_t* a1 = vs + (vrow + 16) * T::ROW_BYTES + ((lc ^ T::swz_v(vrow + 16)) << 4) + off;
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a0);
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a1);
-          u32x4_t w = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
-                       __builtin_bit_cast(u32x2_t, hi)[0], __builtin_bit_cast(u32x2_t, hi)[1]};
-          const vec8 vf = __builtin_bit_cast(vec8, w);
-#pragma unroll
-          for (int qg = 0; qg < T::QG; ++qg) oacc[qg][dt] = E::mfma(vf, pb[qg], oacc[qg][dt]);
+          oacc[qg][dt] = E::mfma(vf, __builtin_bit_cast(vec8, w), oacc[qg][dt]);
         }
       }
     }
