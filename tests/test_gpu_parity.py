@@ -143,6 +143,31 @@ def test_ragged_sizes(N, D, dtype, causal):
                  % (N, D, dtype, causal, layout))
 
 
+@pytest.mark.parametrize("layout", ["BHSD", "BSND"])
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_memory_past_the_end_never_reaches_o(layout, dtype, causal):
+    """K and V are views at the start of NaN-filled buffers: the key rows of the last K/V tile that lie past
+    the sequence end (of the last head, past the end of the tensor) must not reach O or lse."""
+    B, H, N, D = 1, 2, 100, 128
+    q, k, v = inputs.make(B, H, N, D, layout=layout, dtype=dtype, seed=77)
+    qd = to_dev(q, dtype)
+
+    def nan_padded(x):
+        t = to_dev(x, dtype)
+        buf = torch.full((t.numel() + 64 * H * D + D,), float("nan"), dtype=t.dtype, device="cuda")
+        buf[: t.numel()].copy_(t.reshape(-1))
+        return buf[: t.numel()].view(t.shape)
+
+    kd, vd = nan_padded(k), nan_padded(v)
+    o, lse = fa.attention(qd, kd, vd, layout=layout, causal=causal, scale=0.125)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(q, k, v, dtype=dtype, layout=layout, causal=causal, scale=0.125,
+                                      nthreads=NTHREADS)
+    check(o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref,
+          dtype, "NaN past the end %s %s c=%d" % (layout, dtype, causal))
+
+
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 def test_fp16_large_logits_no_overflow(dtype):
     # Logits of order 300 (Q, K drawn x8, D=128): the fp16 overflow case of the catlass tuning page must
