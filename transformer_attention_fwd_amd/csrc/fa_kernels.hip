@@ -25,8 +25,12 @@
 //   * K/V: global_load_lds_dwordx4 straight into a 2-stage LDS ring; the 16-byte chunk XOR swizzle is
 //     applied on the global side (each lane fetches the chunk that belongs at its LDS slot).
 //   * V^T operand: ds_read_b64_tr_b16 (transposing LDS read) from the row-major V tile.
-//   * exp2 with scale*log2(e) folded into one FMA; the reference maximum only moves when the new block
-//     maximum exceeds it by more than 2^8 (a deferred rescale, exact up to rounding).
+//   * exp2 with scale*log2(e) folded into one FMA, against a reference maximum that is only moved when
+//     needed: P is computed against the current reference, and only when some lane's partial sum shows a
+//     probability above 2^8 (a new maximum well above the reference), or on a wave's first tile, is the
+//     row maximum taken, the state rescaled and P recomputed.  Exact up to rounding either way.
+//   * Row sums: l (for lse) in fp32 from the unrounded P; the normaliser of O from the P.V MFMA itself
+//     against an all-ones operand, i.e. the sum of P exactly as rounded for the P.V product.
 //   * Causal: per-wave skip of K tiles wholly above the wave's queries; element mask only on tiles
 //     crossing the diagonal or the sequence end.
 //   * Workgroup -> (head, Q tile) order: every XCD takes a contiguous run of heads (its L2 then holds
@@ -54,6 +58,8 @@ constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kNegInf = -__builtin_inff();
 // deferred rescale threshold, in log2 units: probabilities stay below 2^8 before renormalising
 constexpr float kRescaleThreshold = 8.0f;
+// a lane's partial sum of 16 probabilities above this means some probability may exceed 2^8
+constexpr float kPartLimit = 256.0f;
 // word 3 of a buffer resource on gfx9-family parts: 32-bit data format, raw (unswizzled) addressing
 constexpr int kBufferFlags = 0x00020000;
 
@@ -69,12 +75,6 @@ __device__ __forceinline__ float quad_max(float x) {
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float quad_sum(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Workgroup barrier for LDS hand-offs: the caller has already waited for the loads it needs.
@@ -123,11 +123,10 @@ struct Elem<true> {
   __device__ static __forceinline__ f32x4_t mfma(const vec8& a, const vec8& b, const f32x4_t& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
-  // acc + (sum of the two packed values), the values exactly as the P.V product sees them
-  __device__ static __forceinline__ float sum2(uint32_t pk, float acc) {
-    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-    const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), one, acc, false);
+  // all-ones operand: an MFMA against it sums the other operand's values as rounded
+  __device__ static __forceinline__ vec8 ones() {
+    const __bf16 o = (__bf16)1.0f;
+    return vec8{o, o, o, o, o, o, o, o};
   }
 };
 template <>
@@ -143,10 +142,9 @@ struct Elem<false> {
   __device__ static __forceinline__ f32x4_t mfma(const vec8& a, const vec8& b, const f32x4_t& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
-  __device__ static __forceinline__ float sum2(uint32_t pk, float acc) {
-    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-    const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, pk), one, acc, false);
+  __device__ static __forceinline__ vec8 ones() {
+    const _Float16 o = (_Float16)1.0f;
+    return vec8{o, o, o, o, o, o, o, o};
   }
 };
 
@@ -254,15 +252,28 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
   }
 
   const float cexp = p.c;  // |scale| * log2(e)
-  float m_ref[T::QG], l_part[T::QG], u_part[T::QG];
-  f32x4_t oacc[T::QG][T::DT];
+  float m_ref[T::QG], l_part[T::QG];
+  f32x4_t oacc[T::QG][T::DT], uacc[T::QG];
 #pragma unroll
   for (int qg = 0; qg < T::QG; ++qg) {
     m_ref[qg] = kNegInf;
     l_part[qg] = 0.f;
-    u_part[qg] = 0.f;
+    uacc[qg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < T::DT; ++dt) oacc[qg][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Per-lane LDS byte offsets of the fragment reads.  Both swizzles depend on the row only through
+  // bits that a 16-row (K) or 32-row (V) step leaves alone, so each read is one of these per-lane
+  // bases plus a constant (the row step), which goes into the instruction's offset field.
+  int kb[T::DC], vb[T::DT];
+#pragma unroll
+  for (int c = 0; c < T::DC; ++c) kb[c] = li * T::ROW_BYTES + (((4 * c + g) ^ T::swz_k(li)) << 4);
+#pragma unroll
+  for (int dt = 0; dt < T::DT; ++dt) {
+    const int vrow = 4 * g + (li >> 2);
+    const int col = 16 * dt + 4 * (li & 3);  // element column of this lane's 4-element read
+    vb[dt] = vrow * T::ROW_BYTES + (((col >> 3) ^ T::swz_v(vrow)) << 4) + (col & 7) * 2;
   }
 
   // One K/V tile: wait for its DMA, prefetch the next one into the other stage, compute.
@@ -279,10 +290,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
       // ---- S^T = K Q^T : s[qg][kt] holds keys key0 + 16*kt + 4*g + r for query q0 + 16*qg + li ----
       // the K fragments of 16-key tile kt+1 are read while tile kt's MFMAs run
       f32x4_t s[T::QG][T::KT];
-      auto k_frag = [&](int kt, int c) {
-        const int row = 16 * kt + li;
-        return *(const vec8*)(ks + row * T::ROW_BYTES + (((4 * c + g) ^ T::swz_k(row)) << 4));
-      };
+      auto k_frag = [&](int kt, int c) { return *(const vec8*)(ks + kb[c] + 16 * kt * T::ROW_BYTES); };
       vec8 kf[T::DC], kf_next[T::DC];
 #pragma unroll
       for (int c = 0; c < T::DC; ++c) kf_next[c] = k_frag(0, c);
@@ -304,71 +312,79 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
 
       // ---- mask, online softmax, P ----
       const bool need_mask = (CAUSAL && key0 + T::BN - 1 > q0) || (key0 + T::BN > N);
-      uint32_t pf[T::QG][T::KC][4];
+      if (need_mask) {
+        keep_branch();
 #pragma unroll
-      for (int qg = 0; qg < T::QG; ++qg) {
-        const int qi = q0 + 16 * qg + li;
-        if (need_mask) {
-          keep_branch();
+        for (int qg = 0; qg < T::QG; ++qg) {
+          const int lim = min(CAUSAL ? q0 + 16 * qg + li : N - 1, N - 1) - key0 - 4 * g;  // last valid slot
 #pragma unroll
           for (int kt = 0; kt < T::KT; ++kt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int key = key0 + 16 * kt + 4 * g + r;
-              if ((CAUSAL && key > qi) || key >= N) s[qg][kt][r] = kNegInf;
-            }
+            for (int r = 0; r < 4; ++r)
+              if (16 * kt + r > lim) s[qg][kt][r] = kNegInf;
         }
-        float mx = kNegInf;
-#pragma unroll
-        for (int kt = 0; kt < T::KT; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[qg][kt][r]);
-        mx = quad_max(mx);
-        const float mx_c = (mx == kNegInf) ? kNegInf : mx * cexp;
-        const float m_cand = fmaxf(m_ref[qg], mx_c);
-        const bool move = m_cand > m_ref[qg] + kRescaleThreshold;
-        if (__builtin_amdgcn_ballot_w64(move) != 0) {
-          keep_branch();
-          const float m_new = move ? m_cand : m_ref[qg];
-          const float alpha = __builtin_amdgcn_exp2f(m_ref[qg] - m_new);
-          l_part[qg] *= alpha;
-          u_part[qg] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < T::DT; ++dt) oacc[qg][dt] *= alpha;
-          m_ref[qg] = m_new;
-        }
+      }
+      // P = exp2(c s - m_ref) against the current reference maximum; valid while no probability exceeds
+      // 2^8, which each lane checks through its partial sums.  Otherwise (and on a wave's first tile)
+      // the reference moves to the running maximum first and P is recomputed.
+      uint32_t pf[T::QG][T::KC][4];
+      float part[T::QG];
+      auto expo = [&](int qg) __attribute__((always_inline)) {
         const float neg_m = -m_ref[qg];
-        float rowsum = 0.f, used0 = 0.f, used1 = 0.f;
+        float acc = 0.f;
 #pragma unroll
         for (int kt = 0; kt < T::KT; ++kt) {
           float pv[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qg][kt][r], cexp, neg_m));
-          rowsum += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+          acc += (pv[0] + pv[1]) + (pv[2] + pv[3]);
           const int kc = kt >> 1, half = kt & 1;
-          const uint32_t pk0 = E::pack2(pv[0], pv[1]);
-          const uint32_t pk1 = E::pack2(pv[2], pv[3]);
-          pf[qg][kc][2 * half + 0] = pk0;
-          pf[qg][kc][2 * half + 1] = pk1;
-          used0 = E::sum2(pk0, used0);
-          used1 = E::sum2(pk1, used1);
+          pf[qg][kc][2 * half + 0] = E::pack2(pv[0], pv[1]);
+          pf[qg][kc][2 * half + 1] = E::pack2(pv[2], pv[3]);
         }
-        l_part[qg] += rowsum;
-        u_part[qg] += used0 + used1;
+        part[qg] = acc;
+      };
+      bool slow = (j == 0);
+      if (!slow) {
+        bool over = false;
+#pragma unroll
+        for (int qg = 0; qg < T::QG; ++qg) {
+          expo(qg);
+          over |= part[qg] > kPartLimit;
+        }
+        slow = __builtin_amdgcn_ballot_w64(over) != 0;
       }
+      if (slow) {
+        keep_branch();
+#pragma unroll
+        for (int qg = 0; qg < T::QG; ++qg) {
+          float mx = kNegInf;
+#pragma unroll
+          for (int kt = 0; kt < T::KT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[qg][kt][r]);
+          mx = quad_max(mx);
+          const float m_new = fmaxf(m_ref[qg], mx * cexp);  // finite: every row has a valid key in its first tile
+          const float alpha = __builtin_amdgcn_exp2f(m_ref[qg] - m_new);
+          l_part[qg] *= alpha;
+          uacc[qg] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < T::DT; ++dt) oacc[qg][dt] *= alpha;
+          m_ref[qg] = m_new;
+          expo(qg);
+        }
+      }
+#pragma unroll
+      for (int qg = 0; qg < T::QG; ++qg) l_part[qg] += part[qg];
 
       // ---- O^T += V^T P^T ----
       // V^T fragments of (kc, dt) via transposing reads: lanes 4e..4e+3 of each 16-lane group address
       // row e and lane li receives column li of those rows; read VA fragments ahead of their MFMAs
       auto v_frag = [&](int f) {
         const int kc = f / T::DT, dt = f % T::DT;
-        const int vrow = 32 * kc + 4 * g + (li >> 2);
-        const int col = 16 * dt + 4 * (li & 3);  // element column of this lane's 4-element read
-        const int lc = col >> 3, off = (col & 7) * 2;
-        const uint8_t* a0 = vs + vrow * T::ROW_BYTES + ((lc ^ T::swz_v(vrow)) << 4) + off;
-        const uint8_t* a1 = vs + (vrow + 16) * T::ROW_BYTES + ((lc ^ T::swz_v(vrow + 16)) << 4) + off;
+        const uint8_t* a0 = vs + vb[dt] + 32 * kc * T::ROW_BYTES;
         const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a0);
-        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a1);
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a0 + 16 * T::ROW_BYTES));
         u32x4_t w = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
                      __builtin_bit_cast(u32x2_t, hi)[0], __builtin_bit_cast(u32x2_t, hi)[1]};
         return __builtin_bit_cast(vec8, w);
@@ -377,6 +393,14 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
       vec8 vring[VA];
 #pragma unroll
       for (int f = 0; f < VA; ++f) vring[f] = v_frag(f);
+      // u: the same MFMA against an all-ones operand sums P as rounded for the P.V product
+#pragma unroll
+      for (int kc = 0; kc < T::KC; ++kc)
+#pragma unroll
+        for (int qg = 0; qg < T::QG; ++qg) {
+          u32x4_t w = {pf[qg][kc][0], pf[qg][kc][1], pf[qg][kc][2], pf[qg][kc][3]};
+          uacc[qg] = E::mfma(E::ones(), __builtin_bit_cast(vec8, w), uacc[qg]);
+        }
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         const vec8 vf = vring[f % VA];
@@ -410,7 +434,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
 #pragma unroll
   for (int qg = 0; qg < T::QG; ++qg) {
     const float l = wave_sum_xor16_32(l_part[qg]);
-    const float inv = 1.0f / wave_sum_xor16_32(u_part[qg]);
+    const float inv = 1.0f / uacc[qg][0];
     const int qi = q0 + 16 * qg + li;
     if (qi < N) {
 #pragma unroll
