@@ -14,6 +14,8 @@ Prints ONE JSON line.  Besides the contract fields it carries:
   cpu_baseline  - the fp64 oracle timed on a bounded sample of the same workload's rows on the host
                   cores, in the same unit; the sample also checks the timed GPU output (parity_sample).
 
+Defaults: 50 untimed warm-up steps (the GPU clock settles over the first few tens of milliseconds),
+then 100 timed steps.
 Options: --gpus N (only 1 is supported), --steps K, --warmup W, --no-cpu-baseline,
          --calibrate-copy (after timing, run one plain device copy of 1 GiB for counter calibration).
 """
@@ -50,8 +52,8 @@ def log(msg):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--workload", default="c3", help=argparse.SUPPRESS)
