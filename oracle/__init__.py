@@ -47,6 +47,13 @@ def _load():
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_double,
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ]
+        lib.fa_oracle_rows_ex.restype = ctypes.c_int
+        lib.fa_oracle_rows_ex.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ]
         _lib = lib
     return _lib
 
@@ -110,3 +117,75 @@ def attention(q, k, v, *, dtype: str, layout: str, causal: bool, scale: float, n
     if layout == "BSND":
         o = np.ascontiguousarray(o.transpose(0, 2, 1, 3))
     return o, lse.reshape(B, H, N)
+
+
+def attention_rows_ex(q, k, v, *, dtype: str, layout: str, causal: bool, scale: float, rows, window: int = -1,
+                      q_offset: int = 0, kv_start: int = 0, kv_len=None, nthreads: int = 1):
+    """O and lse (fp64) of the requested rows under the generalised visibility rule of ``fa_oracle.c``:
+    query row i sits at position q_offset + i, key j at position j, only keys in
+    [kv_start, kv_start + kv_len) take part, causal hides keys after the query, and window >= 0 (with
+    causal) hides keys more than ``window`` positions before it.  q is [B,H,Nq,D] / [B,Nq,H,D]; k and v
+    are [B,H,Nk,D] / [B,Nk,H,D].  A row with no visible key gets O = 0 and lse = -inf.
+    """
+    if dtype not in DTYPES:
+        raise ValueError("dtype must be one of %s" % sorted(DTYPES))
+    B, H, Nq, D = _dims(q.shape, layout)
+    Bk, Hk, Nk, Dk = _dims(k.shape, layout)
+    if (Bk, Hk, Dk) != (B, H, D) or v.shape != k.shape:
+        raise ValueError("k and v must share a shape matching q in B, H and D")
+    for t in (q, k, v):
+        if t.dtype.itemsize != ITEMSIZE[dtype]:
+            raise ValueError("q, k, v must have the itemsize of %s" % dtype)
+    if kv_len is None:
+        kv_len = Nk - kv_start
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
+    R = rows.shape[0]
+    o = np.empty((R, D), dtype=np.float64)
+    lse = np.empty((R,), dtype=np.float64)
+    if R == 0:
+        return o, lse
+    rc = _load().fa_oracle_rows_ex(q.ctypes.data, k.ctypes.data, v.ctypes.data, DTYPES[dtype], LAYOUTS[layout],
+                                   B, H, Nq, Nk, D, 1 if causal else 0, int(window), int(q_offset),
+                                   int(kv_start), int(kv_len), float(scale), rows.ctypes.data, R,
+                                   o.ctypes.data, lse.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError("fa_oracle_rows_ex failed with status %d" % rc)
+    return o, lse
+
+
+def attention_ex(q, k, v, *, dtype: str, layout: str, causal: bool, scale: float, window: int = -1,
+                 q_offset: int = 0, kv_start: int = 0, kv_len=None, nthreads: int = 1):
+    """Full O (in q's layout) and lse [B, H, Nq] under the generalised rule, in fp64."""
+    B, H, Nq, D = _dims(q.shape, layout)
+    o_rows, lse = attention_rows_ex(q, k, v, dtype=dtype, layout=layout, causal=causal, scale=scale,
+                                    rows=all_rows(B, H, Nq), window=window, q_offset=q_offset,
+                                    kv_start=kv_start, kv_len=kv_len, nthreads=nthreads)
+    o = o_rows.reshape(B, H, Nq, D)
+    if layout == "BSND":
+        o = np.ascontiguousarray(o.transpose(0, 2, 1, 3))
+    return o, lse.reshape(B, H, Nq)
+
+
+def merge(o_parts, lse_parts):
+    """Combine partial results over disjoint key sets, in fp64.
+
+    o_parts: sequence of arrays [..., D]; lse_parts: matching arrays [...] (natural-log lse of each part;
+    -inf for a part with no visible key, whose O must be 0).  With M = max_s lse_s:
+        lse = M + log(sum_s exp(lse_s - M)),   O = sum_s exp(lse_s - lse) * O_s,
+    the two-term combination of page ai6s.net/6a140d07..., section "第二层：数值稳定性增强", applied to
+    any number of parts.  Rows where every part has lse = -inf get O = 0 and lse = -inf.
+    """
+    lse_s = np.stack([np.asarray(x, dtype=np.float64) for x in lse_parts])
+    o_s = np.stack([np.asarray(x, dtype=np.float64) for x in o_parts])
+    m = lse_s.max(axis=0)
+    empty = np.isneginf(m)
+    m_safe = np.where(empty, 0.0, m)
+    total = np.exp(lse_s - m_safe).sum(axis=0)
+    lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, total)))
+    w = np.exp(lse_s - np.where(empty, 0.0, lse))  # 0 for empty parts
+    o = (w[..., None] * o_s).sum(axis=0)
+    o = np.where(empty[..., None], 0.0, o)
+    return o, lse

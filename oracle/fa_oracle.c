@@ -22,6 +22,22 @@
  *   value per (b, h, i).  Source: page ai6s.net/6a140d07..., section "第二层：数值稳定性增强" (the
  *   lse accumulator of shape [B, H, block_i], built with torch.log / torch.exp).
  *
+ * Generalised rows (fa_oracle_rows_ex).  Query row i of an Nq-row Q sits at sequence position
+ * q_offset + i; key row j of an Nk-row K/V at position j.  A call covers the key chunk
+ * [kv_start, kv_start + kv_len), so that one long key sequence can be processed in pieces whose
+ * partial (O, lse) are combined exactly afterwards through their lse: page ai6s.net/6a0d3bfb...,
+ * section "ops-transformer仓库里还有什么？" (Ring Attention and block-wise attention for long
+ * sequences) and page ai6s.net/6a140d07..., sections "第二层：数值稳定性增强" (combining two partial
+ * log-sum-exps, shifted by their maximum) and "多卡并行" (a 64K sequence split into 8K pieces).
+ * Visible keys of row i (qpos = q_offset + i):
+ *     j in [kv_start, kv_start + kv_len),
+ *     j <= qpos                if causal,
+ *     j >= qpos - window       if window >= 0 (a sliding window of `window` earlier keys plus the
+ *                              query's own position; page ai6s.net/6a140d07..., section
+ *                              "与其他优化方法对比", lists sliding-window attention; only with causal).
+ * A row with no visible key has O = 0 and lse = -inf (the identity of the lse combination).
+ * Q/O are [B][H][Nq][D] or [B][Nq][H][D]; K/V [B][H][Nk][D] or [B][Nk][H][D].
+ *
  * Steps, per row, in this order (nothing is tiled, fused or reordered):
  *   1. widen the stored q, k, v elements exactly to double;
  *   2. pass 1: s_j = scale * sum_d q_d k_jd (d ascending) for every visible j; m = max_j s_j;
@@ -79,7 +95,8 @@ static double orc_load(const void* base, int dtype, int64_t idx) {
 typedef struct {
     const void *q, *k, *v;
     int dtype, layout, causal;
-    int64_t B, H, N, D;
+    int64_t B, H, Nq, Nk, D;
+    int64_t window, q_offset, kv_start, kv_len;
     double scale;
     const int64_t* rows; /* nrows triples (b, h, i) */
     int64_t nrows;
@@ -89,15 +106,16 @@ typedef struct {
     int status;
 } orc_job;
 
-static int64_t orc_index(const orc_job* J, int64_t b, int64_t h, int64_t i, int64_t d) {
-    if (J->layout == 0) return ((b * J->H + h) * J->N + i) * J->D + d;
-    return ((b * J->N + i) * J->H + h) * J->D + d;
+/* element index of row i of a tensor with N rows per (b, h) */
+static int64_t orc_index(const orc_job* J, int64_t N, int64_t b, int64_t h, int64_t i, int64_t d) {
+    if (J->layout == 0) return ((b * J->H + h) * N + i) * J->D + d;
+    return ((b * N + i) * J->H + h) * J->D + d;
 }
 
 static void* orc_worker(void* arg) {
     orc_job* J = (orc_job*)arg;
-    const int64_t N = J->N, D = J->D;
-    double* srow = (double*)malloc(sizeof(double) * (size_t)N);
+    const int64_t Nq = J->Nq, Nk = J->Nk, D = J->D;
+    double* srow = (double*)malloc(sizeof(double) * (size_t)(J->kv_len > 0 ? J->kv_len : 1));
     double* qrow = (double*)malloc(sizeof(double) * (size_t)D);
     if (!srow || !qrow) {
         free(srow);
@@ -107,26 +125,34 @@ static void* orc_worker(void* arg) {
     }
     for (int64_t r = J->first; r < J->last; ++r) {
         const int64_t b = J->rows[3 * r], h = J->rows[3 * r + 1], i = J->rows[3 * r + 2];
-        const int64_t jend = J->causal ? i + 1 : N; /* visible keys: 0 .. jend-1 */
+        /* visible keys: jbeg .. jend-1 */
+        const int64_t qpos = J->q_offset + i;
+        int64_t jbeg = J->kv_start, jend = J->kv_start + J->kv_len;
+        if (J->causal && qpos + 1 < jend) jend = qpos + 1;
+        if (J->window >= 0 && qpos - J->window > jbeg) jbeg = qpos - J->window;
         double* o = J->o + r * D;
-        for (int64_t d = 0; d < D; ++d) qrow[d] = orc_load(J->q, J->dtype, orc_index(J, b, h, i, d));
+        for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
+        if (jend <= jbeg) { /* no visible key */
+            J->lse[r] = -INFINITY;
+            continue;
+        }
+        for (int64_t d = 0; d < D; ++d) qrow[d] = orc_load(J->q, J->dtype, orc_index(J, Nq, b, h, i, d));
 
         /* pass 1: scaled scores and their maximum */
         double m = -INFINITY;
-        for (int64_t j = 0; j < jend; ++j) {
+        for (int64_t j = jbeg; j < jend; ++j) {
             double dot = 0.0;
-            for (int64_t d = 0; d < D; ++d) dot += qrow[d] * orc_load(J->k, J->dtype, orc_index(J, b, h, j, d));
-            srow[j] = J->scale * dot;
-            if (srow[j] > m) m = srow[j];
+            for (int64_t d = 0; d < D; ++d) dot += qrow[d] * orc_load(J->k, J->dtype, orc_index(J, Nk, b, h, j, d));
+            srow[j - jbeg] = J->scale * dot;
+            if (srow[j - jbeg] > m) m = srow[j - jbeg];
         }
 
         /* pass 2: exponentials relative to the maximum, their sum, and the weighted sum of V rows */
         double l = 0.0;
-        for (int64_t d = 0; d < D; ++d) o[d] = 0.0;
-        for (int64_t j = 0; j < jend; ++j) {
-            const double e = exp(srow[j] - m);
+        for (int64_t j = jbeg; j < jend; ++j) {
+            const double e = exp(srow[j - jbeg] - m);
             l += e;
-            for (int64_t d = 0; d < D; ++d) o[d] += e * orc_load(J->v, J->dtype, orc_index(J, b, h, j, d));
+            for (int64_t d = 0; d < D; ++d) o[d] += e * orc_load(J->v, J->dtype, orc_index(J, Nk, b, h, j, d));
         }
         for (int64_t d = 0; d < D; ++d) o[d] /= l;
         J->lse[r] = m + log(l);
@@ -138,18 +164,22 @@ static void* orc_worker(void* arg) {
 
 /*
  * Computes O (nrows x D, fp64, row r for triple r) and lse (nrows, fp64) for the requested
- * (b, h, i) triples.  nthreads >= 1 workers take contiguous slices of the triple list.
- * Returns 0 on success, -2 on a bad argument, -1 if memory for the row buffers ran out.
+ * (b, h, i) triples, i < Nq, under the generalised visibility rule above.  nthreads >= 1 workers
+ * take contiguous slices of the triple list.  Returns 0 on success, -2 on a bad argument, -1 if
+ * memory for the row buffers ran out.
  */
-int fa_oracle_rows(const void* q, const void* k, const void* v, int dtype, int layout, int64_t B,
-                   int64_t H, int64_t N, int64_t D, int causal, double scale, const int64_t* rows,
-                   int64_t nrows, double* o_out, double* lse_out, int nthreads) {
+int fa_oracle_rows_ex(const void* q, const void* k, const void* v, int dtype, int layout, int64_t B,
+                      int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal, int64_t window,
+                      int64_t q_offset, int64_t kv_start, int64_t kv_len, double scale,
+                      const int64_t* rows, int64_t nrows, double* o_out, double* lse_out, int nthreads) {
     if (!q || !k || !v || !rows || !o_out || !lse_out) return -2;
     if (dtype < 0 || dtype > 3 || layout < 0 || layout > 1) return -2;
-    if (B < 1 || H < 1 || N < 1 || D < 1 || nrows < 0) return -2;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || D < 1 || nrows < 0) return -2;
+    if (kv_start < 0 || kv_len < 0 || kv_start + kv_len > Nk) return -2;
+    if (window >= 0 && !causal) return -2;
     for (int64_t r = 0; r < nrows; ++r) {
         const int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
-        if (b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= N) return -2;
+        if (b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= Nq) return -2;
     }
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 512) nthreads = 512;
@@ -169,7 +199,9 @@ int fa_oracle_rows(const void* q, const void* k, const void* v, int dtype, int l
         orc_job* J = &jobs[t];
         J->q = q; J->k = k; J->v = v;
         J->dtype = dtype; J->layout = layout; J->causal = causal ? 1 : 0;
-        J->B = B; J->H = H; J->N = N; J->D = D;
+        J->B = B; J->H = H; J->Nq = Nq; J->Nk = Nk; J->D = D;
+        J->window = window < 0 ? -1 : window;
+        J->q_offset = q_offset; J->kv_start = kv_start; J->kv_len = kv_len;
         J->scale = scale;
         J->rows = rows; J->nrows = nrows;
         J->o = o_out; J->lse = lse_out;
@@ -192,4 +224,12 @@ int fa_oracle_rows(const void* q, const void* k, const void* v, int dtype, int l
     free(tids);
     free(running);
     return status;
+}
+
+/* The plain case: Nq = Nk = N, every key, query i at position i. */
+int fa_oracle_rows(const void* q, const void* k, const void* v, int dtype, int layout, int64_t B,
+                   int64_t H, int64_t N, int64_t D, int causal, double scale, const int64_t* rows,
+                   int64_t nrows, double* o_out, double* lse_out, int nthreads) {
+    return fa_oracle_rows_ex(q, k, v, dtype, layout, B, H, N, N, D, causal, -1, 0, 0, N, scale, rows, nrows,
+                             o_out, lse_out, nthreads);
 }

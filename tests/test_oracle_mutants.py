@@ -17,20 +17,33 @@ from tests import bruteforce
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "fa_oracle.c")
 
 MUTANTS = {
-    "dropped_scale": ("srow[j] = J->scale * dot;", "srow[j] = dot;"),
-    "flipped_sign": ("srow[j] = J->scale * dot;", "srow[j] = -J->scale * dot;"),
-    "causal_excludes_diagonal": ("J->causal ? i + 1 : N", "J->causal ? (i > 0 ? i : 1) : N"),
-    "causal_one_extra_key": ("J->causal ? i + 1 : N", "J->causal ? (i + 2 < N ? i + 2 : N) : N"),
-    "no_max_subtraction": ("exp(srow[j] - m)", "exp(srow[j])"),
-    "bsnd_read_as_bhsd": ("return ((b * J->N + i) * J->H + h) * J->D + d;", "return ((b * J->H + h) * J->N + i) * J->D + d;"),
-    "key_row_index_is_query": ("qrow[d] * orc_load(J->k, J->dtype, orc_index(J, b, h, j, d))",
-                               "qrow[d] * orc_load(J->k, J->dtype, orc_index(J, b, h, i, d))"),
-    "value_row_index_is_query": ("e * orc_load(J->v, J->dtype, orc_index(J, b, h, j, d))",
-                                 "e * orc_load(J->v, J->dtype, orc_index(J, b, h, i, d))"),
+    "dropped_scale": ("srow[j - jbeg] = J->scale * dot;", "srow[j - jbeg] = dot;"),
+    "flipped_sign": ("srow[j - jbeg] = J->scale * dot;", "srow[j - jbeg] = -J->scale * dot;"),
+    "causal_excludes_diagonal": ("if (J->causal && qpos + 1 < jend) jend = qpos + 1;",
+                                 "if (J->causal && qpos < jend) jend = qpos > jbeg ? qpos : jbeg + 1;"),
+    "causal_one_extra_key": ("if (J->causal && qpos + 1 < jend) jend = qpos + 1;",
+                             "if (J->causal && qpos + 2 < jend) jend = qpos + 2;"),
+    "no_max_subtraction": ("exp(srow[j - jbeg] - m)", "exp(srow[j - jbeg])"),
+    "bsnd_read_as_bhsd": ("return ((b * N + i) * J->H + h) * J->D + d;", "return ((b * J->H + h) * N + i) * J->D + d;"),
+    "key_row_index_is_query": ("qrow[d] * orc_load(J->k, J->dtype, orc_index(J, Nk, b, h, j, d))",
+                               "qrow[d] * orc_load(J->k, J->dtype, orc_index(J, Nk, b, h, i, d))"),
+    "value_row_index_is_query": ("e * orc_load(J->v, J->dtype, orc_index(J, Nk, b, h, j, d))",
+                                 "e * orc_load(J->v, J->dtype, orc_index(J, Nk, b, h, i, d))"),
     "log2_lse": ("J->lse[r] = m + log(l);", "J->lse[r] = m + log2(l);"),
     "no_normalisation": ("o[d] /= l;", "o[d] /= 1.0;"),
     "fp16_exponent_bias": ("e - 25", "e - 24"),
     "bf16_wrong_half": ("(uint32_t)b << 16", "(uint32_t)b << 15"),
+    # the generalised visibility rule
+    "window_excludes_edge": ("if (J->window >= 0 && qpos - J->window > jbeg) jbeg = qpos - J->window;",
+                             "if (J->window >= 0 && qpos - J->window + 1 > jbeg) jbeg = qpos - J->window + 1;"),
+    "chunk_end_one_short": ("int64_t jbeg = J->kv_start, jend = J->kv_start + J->kv_len;",
+                            "int64_t jbeg = J->kv_start, jend = J->kv_start + J->kv_len - 1;"),
+    "chunk_start_ignored": ("int64_t jbeg = J->kv_start, jend = J->kv_start + J->kv_len;",
+                            "int64_t jbeg = 0, jend = J->kv_start + J->kv_len;"),
+    "q_offset_ignored": ("const int64_t qpos = J->q_offset + i;", "const int64_t qpos = i;"),
+    "empty_row_lse_zero": ("J->lse[r] = -INFINITY;", "J->lse[r] = 0.0;"),
+    "keys_indexed_with_query_length": ("qrow[d] * orc_load(J->k, J->dtype, orc_index(J, Nk, b, h, j, d))",
+                                       "qrow[d] * orc_load(J->k, J->dtype, orc_index(J, Nq, b, h, j, d))"),
 }
 
 
@@ -41,10 +54,17 @@ def _build(tmp, name, old, new):
     open(path, "w").write(src.replace(old, new) if old else src)
     lib = os.path.join(tmp, name + ".so")
     subprocess.check_call(["gcc", "-O1", "-shared", "-fPIC", "-pthread", path, "-o", lib, "-lm"])
-    f = ctypes.CDLL(lib).fa_oracle_rows
+    so = ctypes.CDLL(lib)
+    f = so.fa_oracle_rows
     f.restype = ctypes.c_int
     f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 2 + [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_double,
                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    fx = so.fa_oracle_rows_ex
+    fx.restype = ctypes.c_int
+    fx.argtypes = ([ctypes.c_void_p] * 3 + [ctypes.c_int] * 2 + [ctypes.c_int64] * 5 + [ctypes.c_int] +
+                   [ctypes.c_int64] * 4 + [ctypes.c_double, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                           ctypes.c_void_p, ctypes.c_int])
+    f.ex = fx
     return f
 
 
@@ -61,8 +81,35 @@ def _call(f, q, k, v, dtype, layout, causal, scale):
     return o.reshape(B, H, N, D), lse.reshape(B, H, N)
 
 
+def _call_ex(f, q, k, v, causal, scale, q_offset, kv_start, kv_len, window):
+    """fp64 BHSD call of the generalised entry point on every row."""
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    b, h, i = np.meshgrid(np.arange(B), np.arange(H), np.arange(Nq), indexing="ij")
+    rows = np.ascontiguousarray(np.stack([b.ravel(), h.ravel(), i.ravel()], 1).astype(np.int64))
+    o = np.empty((rows.shape[0], D))
+    lse = np.empty(rows.shape[0])
+    rc = f.ex(q.ctypes.data, k.ctypes.data, v.ctypes.data, 3, 0, B, H, Nq, Nk, D, causal, window, q_offset,
+              kv_start, kv_len, scale, rows.ctypes.data, rows.shape[0], o.ctypes.data, lse.ctypes.data, 1)
+    assert rc == 0
+    return o.reshape(B, H, Nq, D), lse.reshape(B, H, Nq)
+
+
 def _pins_pass(f):
     """A compact subset of the pins; True iff the library passes all of them."""
+    rng = np.random.default_rng(6)
+    # generalised rule against the explicit-mask brute force: bottom-right causal with Nq != Nk, a key
+    # chunk with rows that see nothing, and a sliding window
+    for (Nq, Nk, qoff, ks, kl, win) in ((5, 13, 8, 0, 13, -1), (6, 11, 2, 3, 6, 4), (7, 9, 2, 0, 9, 2)):
+        q = np.ascontiguousarray(rng.standard_normal((1, 2, Nq, 8)))
+        k = np.ascontiguousarray(rng.standard_normal((1, 2, Nk, 8)))
+        v = np.ascontiguousarray(rng.standard_normal((1, 2, Nk, 8)))
+        o, lse = _call_ex(f, q, k, v, 1, 0.4, qoff, ks, kl, win)
+        o_bf, lse_bf = bruteforce.attention_general(q, k, v, causal=True, scale=0.4, q_offset=qoff, kv_start=ks,
+                                                    kv_len=kl, window=win)
+        if not (np.allclose(o, o_bf, atol=1e-12) and np.array_equal(np.isneginf(lse), np.isneginf(lse_bf))
+                and np.allclose(lse[np.isfinite(lse_bf)], lse_bf[np.isfinite(lse_bf)], atol=1e-12)):
+            return False
     rng = np.random.default_rng(5)
     for causal in (0, 1):
         q, k, v = (rng.standard_normal((2, 3, 11, 8)) for _ in range(3))
