@@ -55,6 +55,8 @@ extern "C" {
 #define FA_ERR_ALIAS 8             /* o or lse overlaps an input, or o overlaps lse */
 #define FA_ERR_NOT_DEVICE_MEMORY 9 /* a pointer is not device memory of the current device */
 #define FA_ERR_HIP 10              /* the HIP runtime reported an error; see fa_last_error() */
+#define FA_ERR_BAD_RANGE 11        /* fa_fwd_ex: key chunk outside [0, Nk], a window without causal, or
+                                      |q_offset| > 2^30 */
 
 /* Limits: 1 <= N <= 2^30, B*H <= 2^31 - 1, every tensor's byte size must fit in int64, and one head's
  * span -- (N - 1) * (bytes between consecutive positions) + D * element size -- must be below 2^31
@@ -87,6 +89,50 @@ extern "C" {
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
            int64_t N, int64_t D, int layout, int causal, float scale, int dtype, void* stream);
+
+/*
+ * fa_fwd_ex -- the same forward over a chunk of keys, for queries placed anywhere in the sequence, with an
+ * optional sliding window.  fa_fwd(...) is fa_fwd_ex(..., Nq = Nk = N, window = -1, q_offset = 0,
+ * kv_start = 0, kv_len = N, ...).
+ *
+ * Processing one long key sequence in chunks and combining the partial results through their lse is the
+ * single-GPU building block of ring and block-wise attention (page ai6s.net/6a0d3bfb..., section
+ * "ops-transformer仓库里还有什么？"; a 64K sequence split into 8K pieces: page ai6s.net/6a140d07...,
+ * section "多卡并行"); fa_merge below does the combination.  Sliding-window attention is one of the
+ * variants the same page compares in section "与其他优化方法对比".
+ *
+ * q, o     : B*H*Nq*D elements of `dtype` in `layout` ([B][H][Nq][D] or [B][Nq][H][D]).
+ * k, v     : B*H*Nk*D elements, same dtype and layout ([B][H][Nk][D] or [B][Nk][H][D]).
+ * lse      : B*H*Nq fp32 values, [B][H][Nq].
+ * Positions: query row i is at sequence position q_offset + i; key row j at position j.  Only the keys
+ *            j in [kv_start, kv_start + kv_len) take part (the chunk; kv_len may be 0).  Key j is visible
+ *            to query i iff it is in the chunk, j <= q_offset + i when causal, and
+ *            j >= q_offset + i - window when window >= 0 (window >= 0 requires causal; window < 0: none).
+ *            Queries that are the last Nq positions of an Nk-long sequence (prefill with a key cache) use
+ *            q_offset = Nk - Nq.
+ * Rows with no visible key get O = 0 and lse = -inf (the identity of the lse combination).
+ * Limits: Nq, Nk <= 2^30, |q_offset| <= 2^30, and the other limits of fa_fwd with Nk for the key span.
+ * Ownership, errors and check order as fa_fwd; FA_ERR_BAD_RANGE comes after the size limits.
+ */
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+              int64_t Nq, int64_t Nk, int64_t D, int layout, int causal, int64_t window, int64_t q_offset,
+              int64_t kv_start, int64_t kv_len, float scale, int dtype, void* stream);
+
+/*
+ * fa_merge -- combine n_parts partial results over disjoint key sets into the result over their union:
+ * with M = max_s lse_s,  lse = M + ln sum_s exp(lse_s - M)  and  O = sum_s exp(lse_s - lse) O_s
+ * (the max-shifted log-sum-exp combination of page ai6s.net/6a140d07..., section
+ * "第二层：数值稳定性增强", for any number of parts).  Parts with lse = -inf contribute nothing; a row
+ * where every part has lse = -inf gets O = 0 and lse = -inf.  Computed in fp32, rounded to `dtype`.
+ *
+ * o_parts  : n_parts consecutive tensors of B*H*N*D elements of `dtype` in `layout` (part s starts at
+ *            element s*B*H*N*D).  Read only.
+ * lse_parts: n_parts consecutive [B][H][N] fp32 arrays.  Read only.
+ * o, lse   : the combined result, same shapes as one part.  Must not overlap the parts or each other.
+ * Ownership and error conventions as fa_fwd (FA_ERR_BAD_DIM for n_parts < 1).
+ */
+int fa_merge(const void* o_parts, const float* lse_parts, int64_t n_parts, void* o, float* lse, int64_t B,
+             int64_t H, int64_t N, int64_t D, int layout, int dtype, void* stream);
 
 /* Static description of a status code ("ok", "null pointer", ...).  Never NULL. */
 const char* fa_status_str(int status);

@@ -18,7 +18,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     declared = _declared()
-    assert declared == ["fa_fwd", "fa_last_error", "fa_status_str", "fa_version"]
+    assert declared == ["fa_fwd", "fa_fwd_ex", "fa_last_error", "fa_merge", "fa_status_str", "fa_version"]
     out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], stdout=subprocess.PIPE,
                          text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.split() and l.split()[1] == "T"}
@@ -37,13 +37,13 @@ def test_header_constants_match_binding():
     assert consts["FA_DTYPE_BF16"] == fa.DTYPE_BF16
     for name in ("FA_OK", "FA_ERR_NULL", "FA_ERR_BAD_DIM", "FA_ERR_BAD_LAYOUT", "FA_ERR_BAD_DTYPE",
                  "FA_ERR_UNSUPPORTED", "FA_ERR_BAD_SCALE", "FA_ERR_MISALIGNED", "FA_ERR_ALIAS",
-                 "FA_ERR_NOT_DEVICE_MEMORY", "FA_ERR_HIP"):
+                 "FA_ERR_NOT_DEVICE_MEMORY", "FA_ERR_HIP", "FA_ERR_BAD_RANGE"):
         assert consts[name] == getattr(fa, name), name
 
 
 def test_status_strings_and_version():
-    assert fa.version() == 100
-    for st in range(11):
+    assert fa.version() == 200
+    for st in range(12):
         assert fa.status_str(st)
     assert fa.status_str(0) == "ok"
     assert fa.status_str(999) == "unknown status"
@@ -114,3 +114,59 @@ def test_every_kernel_stub_is_defined():
     out = subprocess.run(["nm", "-C", "--undefined-only", fa.library_path()], stdout=subprocess.PIPE, text=True,
                          check=True).stdout
     assert "__device_stub__" not in out, out
+
+
+# ---- fa_fwd_ex and fa_merge: pure argument checks ----
+GOOD_EX = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Nq=64, Nk=100, D=64, layout=0, causal=1, window=-1, q_offset=36,
+               kv_start=0, kv_len=100, scale=0.125, dtype=2, stream=0)
+
+
+def _call_ex(**kw):
+    a = dict(GOOD_EX)
+    a.update(kw)
+    return fa.fa_fwd_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Nq"], a["Nk"], a["D"],
+                        a["layout"], a["causal"], a["window"], a["q_offset"], a["kv_start"], a["kv_len"], a["scale"],
+                        a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), fa.FA_ERR_NULL), (dict(v=0), fa.FA_ERR_NULL), (dict(layout=5), fa.FA_ERR_BAD_LAYOUT),
+    (dict(dtype=7), fa.FA_ERR_BAD_DTYPE), (dict(Nq=0), fa.FA_ERR_BAD_DIM), (dict(Nk=0), fa.FA_ERR_BAD_DIM),
+    (dict(D=80), fa.FA_ERR_UNSUPPORTED), (dict(Nk=(1 << 30) + 1, kv_len=1), fa.FA_ERR_UNSUPPORTED),
+    (dict(kv_start=-1), fa.FA_ERR_BAD_RANGE), (dict(kv_len=-1), fa.FA_ERR_BAD_RANGE),
+    (dict(kv_start=50, kv_len=51), fa.FA_ERR_BAD_RANGE), (dict(kv_start=101, kv_len=0), fa.FA_ERR_BAD_RANGE),
+    (dict(causal=0, window=3), fa.FA_ERR_BAD_RANGE), (dict(q_offset=(1 << 30) + 1), fa.FA_ERR_BAD_RANGE),
+    (dict(q_offset=-(1 << 30) - 1), fa.FA_ERR_BAD_RANGE),
+    (dict(scale=float("nan")), fa.FA_ERR_BAD_SCALE), (dict(k=K + 4), fa.FA_ERR_MISALIGNED),
+    (dict(o=K + 64 * 2), fa.FA_ERR_ALIAS), (dict(lse=O + 16), fa.FA_ERR_ALIAS),
+])
+def test_fa_fwd_ex_argument_checks(kw, status):
+    assert _call_ex(**kw) == status
+
+
+def test_fa_fwd_ex_range_check_comes_after_size_limits():
+    # a bad chunk and an unsupported D together: the size error wins (documented order)
+    assert _call_ex(D=96, kv_start=-1) == fa.FA_ERR_UNSUPPORTED
+    # an empty chunk at the end is a valid range (it fails later, on the fake device pointers)
+    assert _call_ex(kv_start=100, kv_len=0) not in (fa.FA_ERR_BAD_RANGE, fa.FA_OK)
+
+
+GOOD_M = dict(op=Q, lp=K, n=3, o=O, lse=L, B=1, H=2, N=64, D=64, layout=0, dtype=2, stream=0)
+
+
+def _call_m(**kw):
+    a = dict(GOOD_M)
+    a.update(kw)
+    return fa.fa_merge(a["op"], a["lp"], a["n"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["D"], a["layout"],
+                       a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(op=0), fa.FA_ERR_NULL), (dict(lse=0), fa.FA_ERR_NULL), (dict(layout=3), fa.FA_ERR_BAD_LAYOUT),
+    (dict(dtype=3), fa.FA_ERR_BAD_DTYPE), (dict(n=0), fa.FA_ERR_BAD_DIM), (dict(N=0), fa.FA_ERR_BAD_DIM),
+    (dict(D=100), fa.FA_ERR_UNSUPPORTED), (dict(n=1 << 40), fa.FA_ERR_UNSUPPORTED),
+    (dict(o=Q + 8), fa.FA_ERR_MISALIGNED), (dict(o=Q + 2 * 2 * 64 * 64 * 2), fa.FA_ERR_ALIAS),
+    (dict(lse=K + 16), fa.FA_ERR_ALIAS), (dict(lse=O), fa.FA_ERR_ALIAS),
+])
+def test_fa_merge_argument_checks(kw, status):
+    assert _call_m(**kw) == status

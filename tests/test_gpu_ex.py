@@ -1,0 +1,158 @@
+"""GPU parity of fa_fwd_ex (key chunks, query offsets, sliding windows, Nq != Nk) and fa_merge against the
+oracle, on seeded inputs, through the C ABI (the thin torch wrappers attention_ex and merge)."""
+import math
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_attention_fwd_amd as fa
+from transformer_attention_fwd_amd import inputs
+from tests.test_gpu_parity import check, to_dev
+
+pytestmark = pytest.mark.gpu
+NTHREADS = min(16, os.cpu_count() or 1)
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _make_qk(B, H, Nq, Nk, D, layout, dtype, seed):
+    """Q with Nq rows and K, V with Nk rows, drawn by the shared seeded generator."""
+    q, _, _ = inputs.make(B, H, Nq, D, layout=layout, dtype=dtype, seed=seed)
+    _, k, v = inputs.make(B, H, Nk, D, layout=layout, dtype=dtype, seed=seed + 1000)
+    return q, k, v
+
+
+def _check_ex(o, lse, o_ref, lse_ref, dtype, what):
+    """check() plus exact handling of rows without visible keys (O = 0 and lse = -inf on both sides)."""
+    o = o.float().cpu().numpy().astype(np.float64)
+    lse = lse.cpu().numpy().astype(np.float64)
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse), empty), what + ": rows without visible keys differ"
+    if empty.any():
+        if o.shape[:3] == lse.shape:  # BHSD
+            assert np.all(o[empty] == 0.0), what + ": O of rows without visible keys is not 0"
+        _say("%s: %d rows without visible keys" % (what, int(empty.sum())))
+    lse_c = np.where(empty, 0.0, lse)
+    ref_c = np.where(empty, 0.0, lse_ref)
+    check(o, lse_c, o_ref, ref_c, dtype, what)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("layout", ["BHSD", "BSND"])
+def test_split_kv_chunks_and_merge(dtype, causal, layout):
+    B, H, N, D = 2, 3, 300, 128 if dtype != "fp32" else 64
+    cuts = (0, 70, 71, 200, 300)
+    q, k, v = inputs.make(B, H, N, D, layout=layout, dtype=dtype, seed=200)
+    qd, kd, vd = (to_dev(x, dtype) for x in (q, k, v))
+    o_parts, l_parts = [], []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        o, l = fa.attention_ex(qd, kd, vd, layout=layout, causal=causal, scale=0.1, kv_start=a, kv_len=b - a)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.attention_ex(q, k, v, dtype=dtype, layout=layout, causal=causal, scale=0.1,
+                                           kv_start=a, kv_len=b - a, nthreads=NTHREADS)
+        _check_ex(o, l, o_ref, l_ref, dtype, "chunk [%d,%d) %s %s c=%d" % (a, b, dtype, layout, causal))
+        o_parts.append(o)
+        l_parts.append(l)
+    om, lm = fa.merge(torch.stack(o_parts), torch.stack(l_parts), layout=layout)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention(q, k, v, dtype=dtype, layout=layout, causal=causal, scale=0.1, nthreads=NTHREADS)
+    _check_ex(om, lm, o_ref, l_ref, dtype, "merged %d chunks %s %s c=%d" % (len(cuts) - 1, dtype, layout, causal))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("nq,nk", [(1, 4097), (100, 1000), (130, 130), (7, 300)])
+def test_bottom_right_causal(dtype, nq, nk):
+    D = 128
+    layout = "BHSD" if nq % 2 else "BSND"
+    q, k, v = _make_qk(1, 4, nq, nk, D, layout, dtype, seed=300 + nq)
+    qd, kd, vd = (to_dev(x, dtype) for x in (q, k, v))
+    o, l = fa.attention_ex(qd, kd, vd, layout=layout, causal=True, scale=1 / math.sqrt(D), q_offset=nk - nq)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_ex(q, k, v, dtype=dtype, layout=layout, causal=True,
+                                       scale=float(np.float32(1 / math.sqrt(D))), q_offset=nk - nq, nthreads=NTHREADS)
+    _check_ex(o, l, o_ref, l_ref, dtype, "bottom-right causal Nq=%d Nk=%d %s %s" % (nq, nk, dtype, layout))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("window", [0, 1, 63, 64, 200])
+@pytest.mark.parametrize("D", [64, 128])
+def test_sliding_window(dtype, window, D):
+    N = 500
+    layout = "BHSD" if window % 2 == 0 else "BSND"
+    q, k, v = inputs.make(1, 3, N, D, layout=layout, dtype=dtype, seed=400 + window)
+    qd, kd, vd = (to_dev(x, dtype) for x in (q, k, v))
+    o, l = fa.attention_ex(qd, kd, vd, layout=layout, causal=True, scale=0.125, window=window)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_ex(q, k, v, dtype=dtype, layout=layout, causal=True, scale=0.125, window=window,
+                                       nthreads=NTHREADS)
+    _check_ex(o, l, o_ref, l_ref, dtype, "window %d D=%d %s %s" % (window, D, dtype, layout))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("case", [
+    dict(nq=90, nk=700, q_offset=400, kv_start=128, kv_len=300, window=150),
+    dict(nq=257, nk=257, q_offset=0, kv_start=200, kv_len=57, window=-1),
+    dict(nq=64, nk=512, q_offset=-40, kv_start=0, kv_len=512, window=-1),
+    dict(nq=33, nk=200, q_offset=150, kv_start=0, kv_len=0, window=-1),
+])
+def test_offsets_chunks_windows_combined(dtype, case):
+    D = 64
+    q, k, v = _make_qk(2, 2, case["nq"], case["nk"], D, "BHSD", dtype, seed=500 + case["nq"])
+    qd, kd, vd = (to_dev(x, dtype) for x in (q, k, v))
+    kw = dict(q_offset=case["q_offset"], kv_start=case["kv_start"], kv_len=case["kv_len"], window=case["window"])
+    o, l = fa.attention_ex(qd, kd, vd, layout="BHSD", causal=True, scale=0.2, **kw)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_ex(q, k, v, dtype=dtype, layout="BHSD", causal=True, scale=0.2, nthreads=NTHREADS,
+                                       **kw)
+    _check_ex(o, l, o_ref, l_ref, dtype, "combined %s %s" % (case, dtype))
+
+
+def test_plain_call_equals_generalised_defaults():
+    q, k, v = inputs.make(2, 2, 333, 128, layout="BSND", dtype="bf16", seed=600)
+    qd, kd, vd = (to_dev(x, "bf16") for x in (q, k, v))
+    o1, l1 = fa.attention(qd, kd, vd, layout="BSND", causal=True, scale=0.1)
+    o2, l2 = fa.attention_ex(qd, kd, vd, layout="BSND", causal=True, scale=0.1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("layout", ["BHSD", "BSND"])
+def test_merge_kernel_against_fp64_merge(dtype, layout):
+    """fa_merge on given partials (some rows empty in some parts, some in all) against the oracle's fp64 merge
+    of the same stored values."""
+    S, B, H, N, D = 4, 2, 3, 77, 64
+    rng = np.random.default_rng(700)
+    parts = [inputs.make(B, H, N, D, layout=layout, dtype=dtype, seed=710 + s)[0] for s in range(S)]
+    lse = rng.standard_normal((S, B, H, N)).astype(np.float32) * 5.0
+    lse[1, :, :, :10] = -np.inf
+    lse[:, 0, 0, 20:23] = -np.inf  # rows empty in every part
+    o_parts = np.stack(parts)
+    for s in range(S):  # a part without visible keys has O = 0
+        if layout == "BHSD":
+            o_parts[s][np.isneginf(lse[s])] = 0
+        else:
+            o_parts[s].transpose(0, 2, 1, 3)[np.isneginf(lse[s])] = 0
+    od = to_dev(o_parts, dtype)
+    ld = torch.from_numpy(lse).cuda()
+    om, lm = fa.merge(od, ld, layout=layout)
+    torch.cuda.synchronize()
+    wid = {"fp32": np.float32, "fp16": np.float16}
+    if dtype == "bf16":
+        vals = (o_parts.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    else:
+        vals = o_parts.view(wid[dtype]).astype(np.float64)
+    if layout == "BSND":
+        vals = vals.transpose(0, 1, 3, 2, 4)
+    o_ref, l_ref = oracle.merge(list(vals), list(lse.astype(np.float64)))
+    if layout == "BSND":
+        o_ref = o_ref.transpose(0, 2, 1, 3)
+    _check_ex(om, lm, o_ref, l_ref, dtype, "merge kernel %s %s" % (dtype, layout))

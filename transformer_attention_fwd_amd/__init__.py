@@ -6,9 +6,18 @@ There is no CPU or framework fallback: if ``libfa.so`` is missing the first call
     fa_fwd(q, k, v, o, lse, B, H, N, D, layout, causal, scale, dtype, stream) -> status
         the C entry point with raw device pointers (ints) and sizes, same names and meaning as in
         include/fa.h.
+    fa_fwd_ex(q, k, v, o, lse, B, H, Nq, Nk, D, layout, causal, window, q_offset, kv_start, kv_len,
+              scale, dtype, stream) -> status
+    fa_merge(o_parts, lse_parts, n_parts, o, lse, B, H, N, D, layout, dtype, stream) -> status
+        the other two C entry points, same conventions.
     attention(q, k, v, *, layout="BHSD", causal=False, scale=None, out=None, lse=None) -> (o, lse)
         convenience wrapper for torch device tensors: checks shapes, allocates o and lse with torch,
         passes torch's current stream, raises FaError on a non-zero status.  scale=None means 1/sqrt(D).
+    attention_ex(q, k, v, *, layout, causal, scale=None, window=-1, q_offset=0, kv_start=0, kv_len=None,
+                 out=None, lse=None) -> (o, lse)
+        the same for fa_fwd_ex (q [B,H,Nq,D] / [B,Nq,H,D], k and v [B,H,Nk,D] / [B,Nk,H,D]).
+    merge(o_parts, lse_parts, *, layout, out=None, lse=None) -> (o, lse)
+        fa_merge on torch tensors stacked along a leading parts dimension.
 """
 from __future__ import annotations
 
@@ -16,7 +25,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "attention", "FaError", "library_path", "load", "status_str", "version",
+__all__ = ["fa_fwd", "fa_fwd_ex", "fa_merge", "attention", "attention_ex", "merge", "FaError", "library_path",
+           "load", "status_str", "version",
            "LAYOUT_BHSD", "LAYOUT_BSND", "DTYPE_FP32", "DTYPE_FP16", "DTYPE_BF16"]
 
 LAYOUT_BHSD = 0
@@ -35,6 +45,7 @@ FA_ERR_MISALIGNED = 7
 FA_ERR_ALIAS = 8
 FA_ERR_NOT_DEVICE_MEMORY = 9
 FA_ERR_HIP = 10
+FA_ERR_BAD_RANGE = 11
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -46,7 +57,7 @@ def library_path() -> str:
 
 class FaError(RuntimeError):
     def __init__(self, status: int, message: str):
-        super().__init__("fa_fwd failed with status %d: %s" % (status, message))
+        super().__init__("libfa call failed with status %d: %s" % (status, message))
         self.status = status
 
 
@@ -61,6 +72,12 @@ def load():
         lib.fa_fwd.restype = ctypes.c_int
         lib.fa_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_int,
                                ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
+        lib.fa_fwd_ex.restype = ctypes.c_int
+        lib.fa_fwd_ex.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [ctypes.c_int, ctypes.c_int] +
+                                  [ctypes.c_int64] * 4 + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p])
+        lib.fa_merge.restype = ctypes.c_int
+        lib.fa_merge.argtypes = ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p] +
+                                 [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p])
         lib.fa_status_str.restype = ctypes.c_char_p
         lib.fa_status_str.argtypes = [ctypes.c_int]
         lib.fa_last_error.restype = ctypes.c_char_p
@@ -75,6 +92,19 @@ def fa_fwd(q, k, v, o, lse, B, H, N, D, layout, causal, scale, dtype, stream) ->
     """The C entry point: pointers are ints (0 = NULL), returns the status code."""
     return load().fa_fwd(q or None, k or None, v or None, o or None, lse or None, B, H, N, D,
                          layout, int(causal), scale, dtype, stream or None)
+
+
+def fa_fwd_ex(q, k, v, o, lse, B, H, Nq, Nk, D, layout, causal, window, q_offset, kv_start, kv_len, scale, dtype,
+              stream) -> int:
+    """The generalised C entry point: pointers are ints (0 = NULL), returns the status code."""
+    return load().fa_fwd_ex(q or None, k or None, v or None, o or None, lse or None, B, H, Nq, Nk, D, layout,
+                            int(causal), window, q_offset, kv_start, kv_len, scale, dtype, stream or None)
+
+
+def fa_merge(o_parts, lse_parts, n_parts, o, lse, B, H, N, D, layout, dtype, stream) -> int:
+    """The C merge entry point: pointers are ints (0 = NULL), returns the status code."""
+    return load().fa_merge(o_parts or None, lse_parts or None, n_parts, o or None, lse or None, B, H, N, D,
+                           layout, dtype, stream or None)
 
 
 def status_str(status: int) -> str:
@@ -136,4 +166,80 @@ def attention(q, k, v, *, layout: str = "BHSD", causal: bool = False, scale: flo
         if st == FA_ERR_HIP:
             msg += ": " + last_error()
         raise FaError(st, msg)
+    return out, lse
+
+
+def _raise_on(st):
+    if st != FA_OK:
+        msg = status_str(st)
+        if st == FA_ERR_HIP:
+            msg += ": " + last_error()
+        raise FaError(st, msg)
+
+
+def _bhnd(t, layout):
+    if layout == "BHSD":
+        B, H, N, D = t.shape
+    else:
+        B, N, H, D = t.shape
+    return B, H, N, D
+
+
+def attention_ex(q, k, v, *, layout: str = "BHSD", causal: bool = False, scale: float | None = None,
+                 window: int = -1, q_offset: int = 0, kv_start: int = 0, kv_len: int | None = None,
+                 out=None, lse=None):
+    """fa_fwd_ex for torch device tensors: q [B,H,Nq,D] / [B,Nq,H,D]; k, v [B,H,Nk,D] / [B,Nk,H,D]."""
+    import torch
+    if layout not in _LAYOUTS:
+        raise ValueError("layout must be 'BHSD' or 'BSND'")
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q must be 4-D and k, v 4-D tensors of one shape")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous in the given layout")
+    B, H, Nq, D = _bhnd(q, layout)
+    Bk, Hk, Nk, Dk = _bhnd(k, layout)
+    if (Bk, Hk, Dk) != (B, H, D):
+        raise ValueError("k, v must match q in B, H and D")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if kv_len is None:
+        kv_len = Nk - kv_start
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of shape [B, H, Nq]")
+    stream = torch.cuda.current_stream(q.device).cuda_stream if q.is_cuda else 0
+    _raise_on(fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Nq, Nk, D,
+                        _LAYOUTS[layout], causal, int(window), int(q_offset), int(kv_start), int(kv_len),
+                        float(scale), _dtype_code(q), stream))
+    return out, lse
+
+
+def merge(o_parts, lse_parts, *, layout: str = "BHSD", out=None, lse=None):
+    """fa_merge for torch device tensors: o_parts [S, ...one O...], lse_parts [S, B, H, N] (float32)."""
+    import torch
+    if layout not in _LAYOUTS:
+        raise ValueError("layout must be 'BHSD' or 'BSND'")
+    if o_parts.dim() != 5 or lse_parts.dim() != 4 or lse_parts.dtype != torch.float32:
+        raise ValueError("o_parts must be [S, 4-D O] and lse_parts a float32 [S, B, H, N] tensor")
+    if not o_parts.is_contiguous() or not lse_parts.is_contiguous():
+        raise ValueError("o_parts and lse_parts must be contiguous")
+    S = o_parts.shape[0]
+    B, H, N, D = _bhnd(o_parts[0], layout)
+    if tuple(lse_parts.shape) != (S, B, H, N):
+        raise ValueError("lse_parts must be [S, B, H, N] matching o_parts")
+    if out is None:
+        out = torch.empty_like(o_parts[0])
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=o_parts.device)
+    stream = torch.cuda.current_stream(o_parts.device).cuda_stream if o_parts.is_cuda else 0
+    _raise_on(fa_merge(o_parts.data_ptr(), lse_parts.data_ptr(), S, out.data_ptr(), lse.data_ptr(), B, H, N, D,
+                       _LAYOUTS[layout], _dtype_code(o_parts), stream))
     return out, lse

@@ -7,7 +7,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa.so")
-SOURCES = [os.path.join(CSRC, "fa_kernels.hip"), os.path.join(CSRC, "fa_api.cpp")]
+SOURCES = [os.path.join(CSRC, "fa_kernels.hip"), os.path.join(CSRC, "fa_merge.hip"), os.path.join(CSRC, "fa_api.cpp")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -21,7 +21,10 @@ FLAGS = [
 def build(verbose: bool = False) -> str:
     """Compile every source into libfa.so (always recompiles).  Returns the library path."""
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-x", "hip", SOURCES[0], "-x", "hip", SOURCES[1], "-o", tmp]
+    cmd = [HIPCC] + FLAGS
+    for src in SOURCES:
+        cmd += ["-x", "hip", src]
+    cmd += ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

@@ -26,6 +26,9 @@ void set_error(const char* what, hipError_t e) {
 
 bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
 
+// longest query or key sequence (and largest |q_offset|) accepted
+constexpr int64_t kMaxRows = int64_t(1) << 30;
+
 bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
   const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
   return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
@@ -60,39 +63,45 @@ FA_API const char* fa_status_str(int status) {
     case FA_ERR_ALIAS: return "o and lse must not overlap the inputs or each other";
     case FA_ERR_NOT_DEVICE_MEMORY: return "a pointer is not device memory of the current device";
     case FA_ERR_HIP: return "HIP runtime error";
+    case FA_ERR_BAD_RANGE: return "key chunk outside [0, Nk], window without causal, or q_offset out of range";
     default: return "unknown status";
   }
 }
 
 FA_API const char* fa_last_error(void) { return g_last_error; }
 
-FA_API int fa_version(void) { return 100; }  // 0.1.0
+FA_API int fa_version(void) { return 200; }  // 0.2.0
 
-FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                  int64_t N, int64_t D, int layout, int causal, float scale, int dtype, void* stream) {
+FA_API int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                     int64_t Nq, int64_t Nk, int64_t D, int layout, int causal, int64_t window, int64_t q_offset,
+                     int64_t kv_start, int64_t kv_len, float scale, int dtype, void* stream) {
   // ---- pure argument checks (no HIP calls) ----
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (layout != FA_LAYOUT_BHSD && layout != FA_LAYOUT_BSND) return FA_ERR_BAD_LAYOUT;
   if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_BAD_DTYPE;
-  if (B < 1 || H < 1 || N < 1 || D < 1) return FA_ERR_BAD_DIM;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || D < 1) return FA_ERR_BAD_DIM;
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
-  int64_t bh, rows, elems, bytes, lse_bytes;
+  int64_t bh, rows_q, rows_k, elems_q, elems_k, bytes_q, bytes_k, lse_bytes;
   const int64_t esize = dtype == FA_DTYPE_FP32 ? 4 : 2;
-  if (N > (int64_t(1) << 30) || !mul_ok(B, H, &bh) || bh > INT32_MAX || !mul_ok(bh, N, &rows) ||
-      !mul_ok(rows, D, &elems) || !mul_ok(elems, esize, &bytes) || !mul_ok(rows, 4, &lse_bytes))
+  if (Nq > kMaxRows || Nk > kMaxRows || !mul_ok(B, H, &bh) || bh > INT32_MAX || !mul_ok(bh, Nq, &rows_q) ||
+      !mul_ok(bh, Nk, &rows_k) || !mul_ok(rows_q, D, &elems_q) || !mul_ok(rows_k, D, &elems_k) ||
+      !mul_ok(elems_q, esize, &bytes_q) || !mul_ok(elems_k, esize, &bytes_k) || !mul_ok(rows_q, 4, &lse_bytes))
     return FA_ERR_UNSUPPORTED;
+  if (kv_start < 0 || kv_len < 0 || kv_start > Nk || kv_len > Nk - kv_start) return FA_ERR_BAD_RANGE;
+  if (window >= 0 && !causal) return FA_ERR_BAD_RANGE;
+  if (q_offset < -kMaxRows || q_offset > kMaxRows) return FA_ERR_BAD_RANGE;
   // grid: one workgroup per (b, h, query tile); must fit a 32-bit grid dimension
   const int64_t qpw = fa::queries_per_workgroup(dtype == FA_DTYPE_FP32 ? fa::kDtypeFp32 : fa::kDtypeBf16);
-  if (bh * ((N + qpw - 1) / qpw) > INT32_MAX) return FA_ERR_UNSUPPORTED;
-  // one head's rows, from its first element to the end of its last row, are addressed with 32-bit
+  if (bh * ((Nq + qpw - 1) / qpw) > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  // one head's key rows, from its first element to the end of its last row, are addressed with 32-bit
   // offsets from a per-head buffer descriptor
   const int64_t row_stride_bytes = (layout == FA_LAYOUT_BHSD ? D : H * D) * esize;
-  if ((N - 1) * row_stride_bytes + D * esize > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  if ((Nk - 1) * row_stride_bytes + D * esize > INT32_MAX) return FA_ERR_UNSUPPORTED;
   if (!isfinite(scale) || !isfinite(fabsf(scale) * 1.4426950408889634f)) return FA_ERR_BAD_SCALE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15) return FA_ERR_MISALIGNED;
-  if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes) ||
-      overlaps(lse, lse_bytes, q, bytes) || overlaps(lse, lse_bytes, k, bytes) ||
-      overlaps(lse, lse_bytes, v, bytes) || overlaps(lse, lse_bytes, o, bytes))
+  if (overlaps(o, bytes_q, q, bytes_q) || overlaps(o, bytes_q, k, bytes_k) || overlaps(o, bytes_q, v, bytes_k) ||
+      overlaps(lse, lse_bytes, q, bytes_q) || overlaps(lse, lse_bytes, k, bytes_k) ||
+      overlaps(lse, lse_bytes, v, bytes_k) || overlaps(lse, lse_bytes, o, bytes_q))
     return FA_ERR_ALIAS;
 
   // ---- device residency ----
@@ -118,13 +127,23 @@ FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* l
   p.lse = lse;
   p.B = (int)B;
   p.H = (int)H;
-  p.N = (int)N;
-  p.stride_b = H * N * D;
+  p.Nq = (int)Nq;
+  p.Nkv = (int)kv_len;
+  p.kv_start = kv_start;
+  p.delta = q_offset - kv_start;
+  // a window reaching before every key the queries could see hides nothing
+  p.window = (window < 0 || window >= q_offset + Nq) ? -1 : window;
   if (layout == FA_LAYOUT_BHSD) {
-    p.stride_h = N * D;
+    p.stride_b_q = H * Nq * D;
+    p.stride_h_q = Nq * D;
+    p.stride_b_k = H * Nk * D;
+    p.stride_h_k = Nk * D;
     p.stride_s = D;
   } else {
-    p.stride_h = D;
+    p.stride_b_q = Nq * H * D;
+    p.stride_h_q = D;
+    p.stride_b_k = Nk * H * D;
+    p.stride_h_k = D;
     p.stride_s = H * D;
   }
   // |scale| * log2(e).  The kernels need it positive (masked -inf scores then give exp2(-inf) = 0); a
@@ -134,6 +153,56 @@ FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* l
   p.qsign = scale < 0.0f ? (dtype == FA_DTYPE_FP32 ? 0x80000000u : 0x80008000u) : 0u;
   const int kd = dtype == FA_DTYPE_FP32 ? fa::kDtypeFp32 : dtype == FA_DTYPE_FP16 ? fa::kDtypeFp16 : fa::kDtypeBf16;
   e = fa::launch(p, kd, (int)D, causal != 0, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    set_error("kernel launch", e);
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                  int64_t N, int64_t D, int layout, int causal, float scale, int dtype, void* stream) {
+  // N bounds the key range too, so a bad N reports as a dimension or size error, never as a range error
+  if (N < 1) return (!q || !k || !v || !o || !lse) ? FA_ERR_NULL
+                    : (layout != FA_LAYOUT_BHSD && layout != FA_LAYOUT_BSND) ? FA_ERR_BAD_LAYOUT
+                    : (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) ? FA_ERR_BAD_DTYPE
+                    : FA_ERR_BAD_DIM;
+  return fa_fwd_ex(q, k, v, o, lse, B, H, N, N, D, layout, causal, -1, 0, 0, N, scale, dtype, stream);
+}
+
+FA_API int fa_merge(const void* o_parts, const float* lse_parts, int64_t n_parts, void* o, float* lse, int64_t B,
+                    int64_t H, int64_t N, int64_t D, int layout, int dtype, void* stream) {
+  if (!o_parts || !lse_parts || !o || !lse) return FA_ERR_NULL;
+  if (layout != FA_LAYOUT_BHSD && layout != FA_LAYOUT_BSND) return FA_ERR_BAD_LAYOUT;
+  if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_BAD_DTYPE;
+  if (B < 1 || H < 1 || N < 1 || D < 1 || n_parts < 1) return FA_ERR_BAD_DIM;
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  const int64_t esize = dtype == FA_DTYPE_FP32 ? 4 : 2;
+  int64_t bh, rows, elems, bytes, lse_bytes, all_bytes, all_lse_bytes, threads;
+  if (n_parts > INT32_MAX || !mul_ok(B, H, &bh) || !mul_ok(bh, N, &rows) || !mul_ok(rows, D, &elems) ||
+      !mul_ok(elems, esize, &bytes) || !mul_ok(rows, 4, &lse_bytes) || !mul_ok(bytes, n_parts, &all_bytes) ||
+      !mul_ok(lse_bytes, n_parts, &all_lse_bytes) || !mul_ok(rows, D / 8, &threads) ||
+      (threads + 255) / 256 > INT32_MAX)
+    return FA_ERR_UNSUPPORTED;
+  if (((uintptr_t)o_parts | (uintptr_t)lse_parts | (uintptr_t)o | (uintptr_t)lse) & 15) return FA_ERR_MISALIGNED;
+  if (overlaps(o, bytes, o_parts, all_bytes) || overlaps(o, bytes, lse_parts, all_lse_bytes) ||
+      overlaps(lse, lse_bytes, o_parts, all_bytes) || overlaps(lse, lse_bytes, lse_parts, all_lse_bytes) ||
+      overlaps(lse, lse_bytes, o, bytes))
+    return FA_ERR_ALIAS;
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) {
+    set_error("hipGetDevice", e);
+    return FA_ERR_HIP;
+  }
+  const void* ptrs[4] = {o_parts, lse_parts, o, lse};
+  for (const void* ptr : ptrs) {
+    const int st = check_device(ptr, device);
+    if (st != FA_OK) return st;
+  }
+  const int kd = dtype == FA_DTYPE_FP32 ? fa::kDtypeFp32 : dtype == FA_DTYPE_FP16 ? fa::kDtypeFp16 : fa::kDtypeBf16;
+  e = fa::launch_merge(o_parts, lse_parts, (int)n_parts, o, lse, rows, B, H, N, (int)D,
+                       layout == FA_LAYOUT_BSND ? 1 : 0, kd, (hipStream_t)stream);
   if (e != hipSuccess) {
     set_error("kernel launch", e);
     return FA_ERR_HIP;

@@ -27,7 +27,7 @@
 //   * V^T operand: ds_read_b64_tr_b16 (transposing LDS read) from the row-major V tile.
 //   * exp2 with scale*log2(e) folded into one FMA, against a reference maximum that is only moved when
 //     needed: P is computed against the current reference, and only when some lane's partial sum shows a
-//     probability above 2^8 (a new maximum well above the reference), or on a wave's first tile, is the
+//     probability above 2^8 (a new maximum well above the reference), or on a wave's first active tile, is the
 //     row maximum taken, the state rescaled and P recomputed.  Exact up to rounding either way.
 //   * Row sums: l (for lse) in fp32 from the unrounded P; the normaliser of O from the P.V MFMA itself
 //     against an all-ones operand, i.e. the sum of P exactly as rounded for the P.V product.
@@ -184,7 +184,7 @@ __device__ __forceinline__ void issue_kv_tile(__amdgpu_buffer_rsrc_t kbuf, __amd
   }
 }
 
-template <int D, bool IS_BF16, bool CAUSAL>
+template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
   typedef Tile16<D> T;
   typedef Elem<IS_BF16> E;
@@ -204,24 +204,41 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
   int bh, qt;
   unit_of(blockIdx.x, p.n_units, p.n_qtiles, CAUSAL, bh, qt);
   const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
-  const int N = p.N;
+  const int Nq = p.Nq, Nkv = p.Nkv;
+  const int64_t delta = p.delta, window = p.window;
   const int q_wg = qt * T::BM;
   const int q0 = q_wg + wave * T::QW;
 
-  const uint16_t* __restrict__ qg_ptr = (const uint16_t*)p.q + b * p.stride_b + h * p.stride_h;
-  const uint8_t* __restrict__ kg_ptr = (const uint8_t*)p.k + 2 * (b * p.stride_b + h * p.stride_h);
-  const uint8_t* __restrict__ vg_ptr = (const uint8_t*)p.v + 2 * (b * p.stride_b + h * p.stride_h);
+  const uint16_t* __restrict__ qg_ptr = (const uint16_t*)p.q + b * p.stride_b_q + h * p.stride_h_q;
+  const int64_t kv_base = b * p.stride_b_k + h * p.stride_h_k + p.kv_start * p.stride_s;
+  const uint8_t* __restrict__ kg_ptr = (const uint8_t*)p.k + 2 * kv_base;
+  const uint8_t* __restrict__ vg_ptr = (const uint8_t*)p.v + 2 * kv_base;
 
-  // ---- number of K/V tiles this workgroup visits ----
-  const int last_key = CAUSAL ? min(N - 1, q_wg + T::BM - 1) : N - 1;
-  const int n_kt = last_key / T::BN + 1;
+  // ---- the chunk keys this workgroup visits: from the lowest key inside the window of its first query
+  // (0 without a window) to the last key visible to its last query; tiles of BN keys from k_begin ----
+  const int k_begin = WINDOW ? (int)min((int64_t)Nkv, max((int64_t)0, q_wg + delta - window)) : 0;
+  const int k_last = CAUSAL ? (int)max((int64_t)-1, min((int64_t)Nkv - 1, q_wg + T::BM - 1 + delta)) : Nkv - 1;
+  const int n_kt = k_last >= k_begin ? (k_last - k_begin) / T::BN + 1 : 0;
+  if (n_kt == 0) {  // no query of this workgroup sees any key of the chunk: O = 0, lse = -inf
+    uint16_t* og = (uint16_t*)p.o + b * p.stride_b_q + h * p.stride_h_q;
+#pragma unroll
+    for (int qg = 0; qg < T::QG; ++qg) {
+      const int qi = q0 + 16 * qg + li;
+      if (qi < Nq) {
+#pragma unroll
+        for (int dt = 0; dt < T::DT; ++dt) *(u32x2_t*)(og + qi * p.stride_s + 16 * dt + 4 * g) = u32x2_t{0u, 0u};
+        if (g == 0) p.lse[(int64_t)bh * Nq + qi] = kNegInf;
+      }
+    }
+    return;
+  }
 
   // ---- K/V tile DMA: buffer loads straight into LDS.  The (b, h) base and the valid byte range sit in
   // a buffer descriptor (rows past the sequence end read as zeros and are masked); each lane adds a
   // fixed offset -- the global chunk that belongs at its LDS slot, i.e. the XOR swizzle applied on the
   // global side -- and each tile a uniform one. ----
   const int row_bytes = (int)(2 * p.stride_s);
-  const int span = (N - 1) * row_bytes + T::ROW_BYTES;  // the host keeps this below 2^31
+  const int span = (Nkv - 1) * row_bytes + T::ROW_BYTES;  // the host keeps this below 2^31
   const __amdgpu_buffer_rsrc_t kbuf = __builtin_amdgcn_make_buffer_rsrc((void*)kg_ptr, 0, span, kBufferFlags);
   const __amdgpu_buffer_rsrc_t vbuf = __builtin_amdgcn_make_buffer_rsrc((void*)vg_ptr, 0, span, kBufferFlags);
   int voff_k[T::LOADS], voff_v[T::LOADS];
@@ -233,7 +250,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
     voff_v[i] = row * row_bytes + ((pc ^ T::swz_v(row)) << 4);
   }
   auto issue_tile = [&](int j, uint8_t* kdst, uint8_t* vdst) {
-    issue_kv_tile<T::LOADS, T::NW>(kbuf, vbuf, voff_k, voff_v, j * T::BN * row_bytes, wave, kdst, vdst);
+    issue_kv_tile<T::LOADS, T::NW>(kbuf, vbuf, voff_k, voff_v, (k_begin + j * T::BN) * row_bytes, wave, kdst, vdst);
   };
 
   issue_tile(0, ks0, vs0);
@@ -242,7 +259,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
   vec8 qf[T::QG][T::DC];
 #pragma unroll
   for (int qg = 0; qg < T::QG; ++qg) {
-    const int qrow = min(q0 + 16 * qg + li, N - 1);
+    const int qrow = min(q0 + 16 * qg + li, Nq - 1);
 #pragma unroll
     for (int c = 0; c < T::DC; ++c) {
       u32x4_t raw = *(const u32x4_t*)(qg_ptr + qrow * p.stride_s + 32 * c + 8 * g);
@@ -276,6 +293,8 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
     vb[dt] = vrow * T::ROW_BYTES + (((col >> 3) ^ T::swz_v(vrow)) << 4) + (col & 7) * 2;
   }
 
+  bool first_tile = true;  // wave-uniform: no tile processed yet (a window or chunk can skip the first ones)
+
   // One K/V tile: wait for its DMA, prefetch the next one into the other stage, compute.
   // The last tile is a separate compile-time variant (no prefetch, full wait) so that every wait on
   // the DMA counter is unconditional and the compiler adds none of its own before LDS reads.
@@ -284,8 +303,10 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
     lds_barrier();  // tile j is in LDS for every wave, and every wave is done with tile j-1
     if constexpr (!decltype(last_c)::value) issue_tile(j + 1, kn, vn);  // into tile j-1's stage
 
-    const int key0 = j * T::BN;
-    const bool active = !CAUSAL || key0 <= q0 + T::QW - 1;
+    const int key0 = k_begin + j * T::BN;  // first chunk key of tile j
+    // the wave's 32 queries see some key of this tile (causal: its first key is not after the last
+    // query's position; window: its last key is not before the first query's window)
+    const bool active = (!CAUSAL || key0 <= q0 + T::QW - 1 + delta) && (!WINDOW || key0 + T::BN - 1 >= q0 + delta - window);
     if (active) {
       // ---- S^T = K Q^T : s[qg][kt] holds keys key0 + 16*kt + 4*g + r for query q0 + 16*qg + li ----
       // the K fragments of 16-key tile kt+1 are read while tile kt's MFMAs run
@@ -311,17 +332,24 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
       }
 
       // ---- mask, online softmax, P ----
-      const bool need_mask = (CAUSAL && key0 + T::BN - 1 > q0) || (key0 + T::BN > N);
+      const bool need_mask = (CAUSAL && key0 + T::BN - 1 > q0 + delta) || (key0 + T::BN > Nkv) ||
+                             (WINDOW && key0 < q0 + T::QW - 1 + delta - window);
       if (need_mask) {
         keep_branch();
 #pragma unroll
         for (int qg = 0; qg < T::QG; ++qg) {
-          const int lim = min(CAUSAL ? q0 + 16 * qg + li : N - 1, N - 1) - key0 - 4 * g;  // last valid slot
+          const int qi = q0 + 16 * qg + li;
+          // valid keys of this query lie in [klo, khi] (clamped to the chunk); valid slots 16*kt + r
+          // (key key0 + 16*kt + 4*g + r) in [lo, hi]
+          const int khi = CAUSAL ? (int)max((int64_t)-1, min((int64_t)Nkv - 1, qi + delta)) : Nkv - 1;
+          const int klo = WINDOW ? (int)min((int64_t)Nkv, max((int64_t)0, qi + delta - window)) : 0;
+          const int hi = khi - key0 - 4 * g;
+          const int lo = klo - key0 - 4 * g;
 #pragma unroll
           for (int kt = 0; kt < T::KT; ++kt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              if (16 * kt + r > lim) s[qg][kt][r] = kNegInf;
+              if (16 * kt + r > hi || 16 * kt + r < lo) s[qg][kt][r] = kNegInf;
         }
       }
       // P = exp2(c s - m_ref) against the current reference maximum; valid while no probability exceeds
@@ -344,7 +372,8 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
         }
         part[qg] = acc;
       };
-      bool slow = (j == 0);
+      bool slow = first_tile;  // the wave's first active tile sets the reference maximum
+      first_tile = false;
       if (!slow) {
         bool over = false;
 #pragma unroll
@@ -364,7 +393,10 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[qg][kt][r]);
           mx = quad_max(mx);
-          const float m_new = fmaxf(m_ref[qg], mx * cexp);  // finite: every row has a valid key in its first tile
+          // a row that has seen no visible key yet takes 0 as its reference (its sums stay 0 and any
+          // reference is valid until a probability would exceed 2^8, which the check above catches)
+          float m_new = fmaxf(m_ref[qg], mx * cexp);
+          if (m_new == kNegInf) m_new = 0.0f;
           const float alpha = __builtin_amdgcn_exp2f(m_ref[qg] - m_new);
           l_part[qg] *= alpha;
           uacc[qg] *= alpha;
@@ -429,21 +461,22 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
     step(j, ks0, vs0, ks1, vs1, last);
   }
 
-  // ---- epilogue: O = acc / l, lse = (m + log2 l) ln 2 ----
-  uint16_t* og_ptr = (uint16_t*)p.o + b * p.stride_b + h * p.stride_h;
+  // ---- epilogue: O = acc / u, lse = (m + log2 l) ln 2; a row without any visible key has u = l = 0 and
+  // gets O = 0, lse = -inf ----
+  uint16_t* og_ptr = (uint16_t*)p.o + b * p.stride_b_q + h * p.stride_h_q;
 #pragma unroll
   for (int qg = 0; qg < T::QG; ++qg) {
     const float l = wave_sum_xor16_32(l_part[qg]);
-    const float inv = 1.0f / uacc[qg][0];
+    const float inv = uacc[qg][0] > 0.0f ? 1.0f / uacc[qg][0] : 0.0f;
     const int qi = q0 + 16 * qg + li;
-    if (qi < N) {
+    if (qi < Nq) {
 #pragma unroll
       for (int dt = 0; dt < T::DT; ++dt) {
         const f32x4_t o = oacc[qg][dt] * inv;
         u32x2_t w = {E::pack2(o[0], o[1]), E::pack2(o[2], o[3])};
         *(u32x2_t*)(og_ptr + qi * p.stride_s + 16 * dt + 4 * g) = w;
       }
-      if (g == 0) p.lse[(int64_t)bh * N + qi] = (m_ref[qg] + __builtin_log2f(l)) * kLn2;
+      if (g == 0) p.lse[(int64_t)bh * Nq + qi] = (m_ref[qg] + __builtin_log2f(l)) * kLn2;
     }
   }
 }
@@ -464,7 +497,7 @@ struct Tile32 {
   static constexpr int LD = D + 4;       // padded LDS row (floats)
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(256, 1) void fa_fwd_32(Params p) {
   typedef Tile32<D> T;
   __shared__ float ks[T::BN * T::LD];
@@ -477,24 +510,28 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_32(Params p) {
   int bh, qt;
   unit_of(blockIdx.x, p.n_units, p.n_qtiles, CAUSAL, bh, qt);
   const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
-  const int N = p.N;
+  const int Nq = p.Nq, Nkv = p.Nkv;
+  const int64_t delta = p.delta, window = p.window;
   const int q_wg = qt * T::BM;
   const int q0 = q_wg + wave * T::QW;
-  const float* qg_ptr = (const float*)p.q + b * p.stride_b + h * p.stride_h;
-  const float* kg_ptr = (const float*)p.k + b * p.stride_b + h * p.stride_h;
-  const float* vg_ptr = (const float*)p.v + b * p.stride_b + h * p.stride_h;
+  const float* qg_ptr = (const float*)p.q + b * p.stride_b_q + h * p.stride_h_q;
+  const int64_t kv_base = b * p.stride_b_k + h * p.stride_h_k + p.kv_start * p.stride_s;
+  const float* kg_ptr = (const float*)p.k + kv_base;
+  const float* vg_ptr = (const float*)p.v + kv_base;
   const float qsign = p.qsign ? -1.0f : 1.0f;
 
   // Q^T fragments: lane holds q[q0 + 16*qg + li][4*kk + g]
   float qf[T::QG][T::DK];
 #pragma unroll
   for (int qg = 0; qg < T::QG; ++qg) {
-    const int qrow = min(q0 + 16 * qg + li, N - 1);
+    const int qrow = min(q0 + 16 * qg + li, Nq - 1);
 #pragma unroll
     for (int kk = 0; kk < T::DK; ++kk) qf[qg][kk] = qsign * qg_ptr[qrow * p.stride_s + 4 * kk + g];
   }
-  const int last_key = CAUSAL ? min(N - 1, q_wg + T::BM - 1) : N - 1;
-  const int n_kt = last_key / T::BN + 1;
+  // chunk keys visited: as in the 16-bit kernel (may be none: then O = 0, lse = -inf)
+  const int k_begin = WINDOW ? (int)min((int64_t)Nkv, max((int64_t)0, q_wg + delta - window)) : 0;
+  const int k_last = CAUSAL ? (int)max((int64_t)-1, min((int64_t)Nkv - 1, q_wg + T::BM - 1 + delta)) : Nkv - 1;
+  const int n_kt = k_last >= k_begin ? (k_last - k_begin) / T::BN + 1 : 0;
   const float cexp = p.c;
   float m_ref[T::QG], l_part[T::QG];
   f32x4_t oacc[T::QG][T::DT];
@@ -507,18 +544,19 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_32(Params p) {
   }
 
   for (int j = 0; j < n_kt; ++j) {
-    const int key0 = j * T::BN;
-    // stage K, V tile through registers (16-byte loads, padded rows)
+    const int key0 = k_begin + j * T::BN;
+    // stage K, V tile through registers (16-byte loads, padded rows; rows past the chunk repeat its
+    // last row and are masked)
     for (int idx = threadIdx.x; idx < T::BN * (D / 4); idx += 256) {
       const int row = idx / (D / 4), c4 = idx % (D / 4);
-      const int key = min(key0 + row, N - 1);
+      const int key = min(key0 + row, Nkv - 1);
       const float4 kv = *(const float4*)(kg_ptr + key * p.stride_s + 4 * c4);
       const float4 vv = *(const float4*)(vg_ptr + key * p.stride_s + 4 * c4);
       *(float4*)(ks + row * T::LD + 4 * c4) = kv;
       *(float4*)(vs + row * T::LD + 4 * c4) = vv;
     }
     __syncthreads();
-    const bool active = !CAUSAL || key0 <= q0 + T::QW - 1;
+    const bool active = (!CAUSAL || key0 <= q0 + T::QW - 1 + delta) && (!WINDOW || key0 + T::BN - 1 >= q0 + delta - window);
     if (active) {
       f32x4_t s[T::QG][T::KT];
 #pragma unroll
@@ -532,17 +570,20 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_32(Params p) {
           for (int qg = 0; qg < T::QG; ++qg) s[qg][kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(kf, qf[qg][kk], s[qg][kt], 0, 0, 0);
         }
       }
-      const bool need_mask = (CAUSAL && key0 + T::BN - 1 > q0) || (key0 + T::BN > N);
+      const bool need_mask = (CAUSAL && key0 + T::BN - 1 > q0 + delta) || (key0 + T::BN > Nkv) ||
+                             (WINDOW && key0 < q0 + T::QW - 1 + delta - window);
 #pragma unroll
       for (int qg = 0; qg < T::QG; ++qg) {
         const int qi = q0 + 16 * qg + li;
         if (need_mask) {
+          const int hi = CAUSAL ? (int)max((int64_t)-1, min((int64_t)Nkv - 1, qi + delta)) : Nkv - 1;
+          const int lo = WINDOW ? (int)min((int64_t)Nkv, max((int64_t)0, qi + delta - window)) : 0;
 #pragma unroll
           for (int kt = 0; kt < T::KT; ++kt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int key = key0 + 16 * kt + 4 * g + r;
-              if ((CAUSAL && key > qi) || key >= N) s[qg][kt][r] = kNegInf;
+              if (key > hi || key < lo) s[qg][kt][r] = kNegInf;
             }
         }
         float mx = kNegInf;
@@ -556,7 +597,8 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_32(Params p) {
         const bool move = m_cand > m_ref[qg] + kRescaleThreshold;
         if (__builtin_amdgcn_ballot_w64(move) != 0) {
           const float m_new = move ? m_cand : m_ref[qg];
-          const float alpha = __builtin_amdgcn_exp2f(m_ref[qg] - m_new);
+          // a row that stays put keeps its sums (also when it has seen no visible key: -inf - -inf)
+          const float alpha = move ? __builtin_amdgcn_exp2f(m_ref[qg] - m_new) : 1.0f;
           l_part[qg] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < T::DT; ++dt) oacc[qg][dt] *= alpha;
@@ -592,19 +634,19 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_32(Params p) {
     __syncthreads();
   }
 
-  float* og_ptr = (float*)p.o + b * p.stride_b + h * p.stride_h;
+  float* og_ptr = (float*)p.o + b * p.stride_b_q + h * p.stride_h_q;
 #pragma unroll
   for (int qg = 0; qg < T::QG; ++qg) {
     const float l = wave_sum_xor16_32(l_part[qg]);
-    const float inv = 1.0f / l;
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;  // l = 0: no visible key, O = 0 and lse = -inf
     const int qi = q0 + 16 * qg + li;
-    if (qi < N) {
+    if (qi < Nq) {
 #pragma unroll
       for (int dt = 0; dt < T::DT; ++dt) {
         const f32x4_t o = oacc[qg][dt] * inv;
         *(float4*)(og_ptr + qi * p.stride_s + 16 * dt + 4 * g) = make_float4(o[0], o[1], o[2], o[3]);
       }
-      if (g == 0) p.lse[(int64_t)bh * N + qi] = (m_ref[qg] + __builtin_log2f(l)) * kLn2;
+      if (g == 0) p.lse[(int64_t)bh * Nq + qi] = (m_ref[qg] + __builtin_log2f(l)) * kLn2;
     }
   }
 }
@@ -612,35 +654,41 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_32(Params p) {
 // ------------------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------------------
-template <int D, bool IS_BF16, bool CAUSAL>
+template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW>
 static hipError_t launch16(Params p, hipStream_t stream) {
   typedef Tile16<D> T;
-  p.n_qtiles = (p.N + T::BM - 1) / T::BM;
+  p.n_qtiles = (p.Nq + T::BM - 1) / T::BM;
   p.n_units = p.n_qtiles * p.B * p.H;
-  hipLaunchKernelGGL((fa_fwd_16<D, IS_BF16, CAUSAL>), dim3(p.n_units), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((fa_fwd_16<D, IS_BF16, CAUSAL, WINDOW>), dim3(p.n_units), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool WINDOW>
 static hipError_t launch32(Params p, hipStream_t stream) {
   typedef Tile32<D> T;
-  p.n_qtiles = (p.N + T::BM - 1) / T::BM;
+  p.n_qtiles = (p.Nq + T::BM - 1) / T::BM;
   p.n_units = p.n_qtiles * p.B * p.H;
-  hipLaunchKernelGGL((fa_fwd_32<D, CAUSAL>), dim3(p.n_units), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((fa_fwd_32<D, CAUSAL, WINDOW>), dim3(p.n_units), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
+template <int D, bool IS_BF16>
+static hipError_t launch16_d(const Params& p, bool causal, hipStream_t stream) {
+  if (!causal) return launch16<D, IS_BF16, false, false>(p, stream);
+  return p.window >= 0 ? launch16<D, IS_BF16, true, true>(p, stream) : launch16<D, IS_BF16, true, false>(p, stream);
+}
+
+template <int D>
+static hipError_t launch32_d(const Params& p, bool causal, hipStream_t stream) {
+  if (!causal) return launch32<D, false, false>(p, stream);
+  return p.window >= 0 ? launch32<D, true, true>(p, stream) : launch32<D, true, false>(p, stream);
+}
+
+// A window is only used with causal attention (the entry point rejects it otherwise).
 hipError_t launch(const Params& p, int dtype, int d, bool causal, hipStream_t stream) {
-  if (dtype == kDtypeBf16) {
-    if (d == 128) return causal ? launch16<128, true, true>(p, stream) : launch16<128, true, false>(p, stream);
-    return causal ? launch16<64, true, true>(p, stream) : launch16<64, true, false>(p, stream);
-  }
-  if (dtype == kDtypeFp16) {
-    if (d == 128) return causal ? launch16<128, false, true>(p, stream) : launch16<128, false, false>(p, stream);
-    return causal ? launch16<64, false, true>(p, stream) : launch16<64, false, false>(p, stream);
-  }
-  if (d == 128) return causal ? launch32<128, true>(p, stream) : launch32<128, false>(p, stream);
-  return causal ? launch32<64, true>(p, stream) : launch32<64, false>(p, stream);
+  if (dtype == kDtypeBf16) return d == 128 ? launch16_d<128, true>(p, causal, stream) : launch16_d<64, true>(p, causal, stream);
+  if (dtype == kDtypeFp16) return d == 128 ? launch16_d<128, false>(p, causal, stream) : launch16_d<64, false>(p, causal, stream);
+  return d == 128 ? launch32_d<128>(p, causal, stream) : launch32_d<64>(p, causal, stream);
 }
 
 int queries_per_workgroup(int dtype) { return dtype == kDtypeFp32 ? Tile32<64>::BM : Tile16<64>::BM; }
