@@ -6,18 +6,22 @@ This is the batch-8, 4096-token inference shape of page ai6s.net/6a0d3bfb... (32
 FLOP per step = 4*B*H*N^2*D / 2 (causal) = 1.0995e12.
 
 Prints ONE JSON line.  Besides the contract fields it carries:
-  roofline      - the kernel's achieved TFLOP/s (algorithmic FLOP / mean launch time measured with
-                  HIP events on the launch stream) against the bf16 dense peak 2516.6 TFLOP/s;
+  roofline      - the attention kernel's achieved TFLOP/s (algorithmic FLOP / mean duration of its launches,
+                  measured with HIP events on the launch stream) against the bf16 dense peak 2516.6 TFLOP/s;
                   traffic = HBM bytes per launch from the committed rocprofv3 counter summary
-                  (profiles/traffic_fa_fwd_c3.json) when it was taken on the current kernel source,
-                  else null.
+                  (profiles/traffic_fa_fwd_c3.json) when it was taken on the current kernel source, else null.
   cpu_baseline  - the fp64 oracle timed on a bounded sample of the same workload's rows on the host
                   cores, in the same unit; the sample also checks the timed GPU output (parity_sample).
 
 Defaults: 50 untimed warm-up steps (the GPU clock settles over the first few tens of milliseconds),
 then 100 timed steps.
 Options: --gpus N (only 1 is supported), --steps K, --warmup W, --no-cpu-baseline,
-         --calibrate-copy (after timing, run one plain device copy of 1 GiB for counter calibration).
+         --calibrate-copy (after timing, run one plain device copy of 1 GiB for counter calibration),
+         --workload NAME: c3 (default), or one of the variants of the same C3 tensors:
+           c3_split4      the keys in 4 chunks of 1024 (fa_fwd_ex per chunk) combined by fa_merge
+           c3_window1024  causal with a sliding window of 1024 earlier keys
+           prefill_cache  the last 1024 queries against all 4096 keys (bottom-right causal, q_offset 3072)
+         or c4 / c5 (the plain causal forward on those configurations).
 """
 from __future__ import annotations
 
@@ -33,9 +37,16 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s + % of bf16 MFMA peak, causal B=8 H=32 N=4096 D=128"
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_fwd_c3.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "transformer_attention_fwd_amd", "csrc", f)
                   for f in ("fa_kernels.hip", "fa_launch.h", "fa_api.cpp")]
+VARIANTS = {
+    "c3": dict(desc="causal", window=-1, chunks=1, nq=None),
+    "c3_split4": dict(desc="causal, keys in 4 chunks + lse merge", window=-1, chunks=4, nq=None),
+    "c3_window1024": dict(desc="causal, sliding window 1024", window=1024, chunks=1, nq=None),
+    "prefill_cache": dict(desc="causal, last 1024 queries vs 4096 cached keys", window=-1, chunks=1, nq=1024),
+}
 
 
 def kernel_sha() -> str:
@@ -49,6 +60,15 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def visible_keys(nq, nk, q_offset, window):
+    """Keys each query row sees (causal, optional window): array of length nq."""
+    import numpy as np
+    qpos = q_offset + np.arange(nq, dtype=np.int64)
+    hi = np.minimum(qpos, nk - 1)
+    lo = np.maximum(0, qpos - window) if window >= 0 else np.zeros(nq, dtype=np.int64)
+    return np.maximum(hi - lo + 1, 0)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -56,7 +76,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
-    ap.add_argument("--workload", default="c3", help=argparse.SUPPRESS)
+    ap.add_argument("--workload", default="c3")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -70,48 +90,86 @@ def main():
     import transformer_attention_fwd_amd as fa
     from transformer_attention_fwd_amd import inputs
 
-    w = inputs.WORKLOADS[args.workload]
+    if args.workload in VARIANTS:
+        var = VARIANTS[args.workload]
+        w = inputs.WORKLOADS["c3"]
+    elif args.workload in ("c4", "c5"):
+        var = VARIANTS["c3"]
+        w = inputs.WORKLOADS[args.workload]
+    else:
+        raise SystemExit("unknown workload %s" % args.workload)
     log("bench: generating %s inputs %s" % (w.name, (w.B, w.H, w.N, w.D)))
     qh, kh, vh = inputs.make_workload(w)
-    dev = [torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda") for x in (qh, kh, vh)]
-    q, k, v = dev
+    B, H, N, D = w.B, w.H, w.N, w.D
+    Nk = N
+    Nq = var["nq"] or N
+    q_offset = Nk - Nq
+    if Nq != N:
+        qh = np.ascontiguousarray(qh[:, :, N - Nq:, :])  # BHSD: the last Nq query rows
+    window, chunks = var["window"], var["chunks"]
+    to_dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda")
+    q, k, v = to_dev(qh), to_dev(kh), to_dev(vh)
     o = torch.empty_like(q)
-    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
-    B, H, N, D = w.B, w.H, w.N, w.D
     layout = fa.LAYOUT_BHSD if w.layout == "BHSD" else fa.LAYOUT_BSND
+    bounds = [Nk * c // chunks for c in range(chunks + 1)]
+    if chunks > 1:
+        o_parts = torch.empty((chunks,) + tuple(q.shape), dtype=q.dtype, device="cuda")
+        l_parts = torch.empty((chunks, B, H, Nq), dtype=torch.float32, device="cuda")
 
-    def step():
-        st = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, D,
-                       layout, w.causal, w.scale, fa.DTYPE_BF16, sptr)
+    def check(st, what):
         if st != fa.FA_OK:
-            raise RuntimeError("fa_fwd failed: %s %s" % (fa.status_str(st), fa.last_error()))
+            raise RuntimeError("%s failed: %s %s" % (what, fa.status_str(st), fa.last_error()))
+
+    def attention_launches():
+        if chunks == 1 and window < 0 and Nq == Nk:
+            check(fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, D,
+                            layout, w.causal, w.scale, fa.DTYPE_BF16, sptr), "fa_fwd")
+        elif chunks == 1:
+            check(fa.fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Nq, Nk,
+                               D, layout, w.causal, window, q_offset, 0, Nk, w.scale, fa.DTYPE_BF16, sptr), "fa_fwd_ex")
+        else:
+            for c in range(chunks):
+                check(fa.fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_parts[c].data_ptr(),
+                                   l_parts[c].data_ptr(), B, H, Nq, Nk, D, layout, w.causal, window, q_offset,
+                                   bounds[c], bounds[c + 1] - bounds[c], w.scale, fa.DTYPE_BF16, sptr), "fa_fwd_ex")
+
+    def merge_launch():
+        check(fa.fa_merge(o_parts.data_ptr(), l_parts.data_ptr(), chunks, o.data_ptr(), lse.data_ptr(), B, H, Nq, D,
+                          layout, fa.DTYPE_BF16, sptr), "fa_merge")
 
     log("bench: warmup %d" % args.warmup)
     for _ in range(args.warmup):
-        step()
+        attention_launches()
+        if chunks > 1:
+            merge_launch()
     torch.cuda.synchronize()
 
-    # timed region: K steps, per-launch HIP events on the launch stream
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # timed region: K steps; HIP events on the launch stream around the attention launches and the merge
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    evs[0].record(stream)
     for i in range(args.steps):
-        step()
-        evs[i + 1].record(stream)
+        ev[i][0].record(stream)
+        attention_launches()
+        ev[i][1].record(stream)
+        if chunks > 1:
+            merge_launch()
+        ev[i][2].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    launch_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
-    total_ms = evs[0].elapsed_time(evs[-1])
+    attn_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
+    merge_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]
+    total_ms = ev[0][0].elapsed_time(ev[-1][2])
     ms_per_step = total_ms / args.steps
-    flops = w.flops()
+    flops = float(4.0 * D * B * H * visible_keys(Nq, Nk, q_offset, window).sum()) if w.causal else w.flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
-    mean_launch_ms = float(np.mean(launch_ms))
-    achieved = flops / (mean_launch_ms * 1e-3) / 1e12
-    log("bench: %d steps, %.4f ms/step (wall %.4f), median launch %.4f ms, best %.4f ms, %.1f TFLOP/s"
-        % (args.steps, ms_per_step, (t1 - t0) * 1e3 / args.steps, float(np.median(launch_ms)), min(launch_ms), value))
+    mean_attn_ms = float(np.mean(attn_ms))
+    achieved = flops / (mean_attn_ms * 1e-3) / 1e12
+    log("bench: %d steps, %.4f ms/step (wall %.4f), attention median %.4f ms best %.4f ms, %.1f TFLOP/s"
+        % (args.steps, ms_per_step, (t1 - t0) * 1e3 / args.steps, float(np.median(attn_ms)), min(attn_ms), value))
 
     if args.calibrate_copy:
         n = 1 << 29  # 1 GiB of bf16
@@ -124,14 +182,25 @@ def main():
         del src, dst
 
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
+    if os.path.exists(TRAFFIC_FILE) and args.workload == "c3":
         t = json.load(open(TRAFFIC_FILE))
         if t.get("kernel_sha") == kernel_sha() and t.get("workload") == w.name:
             traffic = t["hbm_bytes_per_launch"]
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "fa_fwd_16<128,bf16,causal>", "mean_launch_ms": round(mean_launch_ms, 5),
+                "kernel": "fa_fwd_16<128,bf16,causal%s>" % (",window" if window >= 0 else ""),
+                "mean_launch_ms": round(mean_attn_ms / chunks, 5), "launches_per_step": chunks,
                 "kernel_sha": kernel_sha()}
+    extra = {}
+    if chunks > 1:
+        # the merge reads every part's O and lse once and writes O and lse once
+        mbytes = (chunks + 1) * (B * H * Nq * D * 2 + B * H * Nq * 4)
+        mean_merge_ms = float(np.mean(merge_ms))
+        gbs = mbytes / (mean_merge_ms * 1e-3) / 1e9
+        extra["merge_roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                   "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                                   "kernel": "fa_merge_kernel<bf16,128>", "mean_launch_ms": round(mean_merge_ms, 5),
+                                   "bytes_per_launch": mbytes}
 
     cpu_baseline = None
     parity = None
@@ -140,19 +209,20 @@ def main():
 
         cores = min(16, os.cpu_count() or 1)
         torch.cuda.synchronize()
+        ref = lambda rows: oracle.attention_rows_ex(qh, kh, vh, dtype="bf16", layout=w.layout, causal=w.causal,
+                                                    scale=w.scale, rows=rows, window=window, q_offset=q_offset,
+                                                    nthreads=cores)
         # bounded sample: seeded rows, sized from a short calibration to about 12 s of wall time
-        cal = inputs.sample_rows(B, H, N, 256, seed=900)
+        cal = inputs.sample_rows(B, H, Nq, 256, seed=900)
         t_a = time.perf_counter()
-        oracle.attention_rows(qh, kh, vh, dtype="bf16", layout=w.layout, causal=w.causal, scale=w.scale,
-                              rows=cal, nthreads=cores)
+        ref(cal)
         t_cal = time.perf_counter() - t_a
-        n_rows = int(min(B * H * N, max(512, 256 * 12.0 / max(t_cal, 1e-3))))
-        rows = inputs.sample_rows(B, H, N, n_rows, seed=901)
+        n_rows = int(min(B * H * Nq, max(512, 256 * 12.0 / max(t_cal, 1e-3))))
+        rows = inputs.sample_rows(B, H, Nq, n_rows, seed=901)
         t_a = time.perf_counter()
-        o_ref, lse_ref = oracle.attention_rows(qh, kh, vh, dtype="bf16", layout=w.layout, causal=w.causal,
-                                               scale=w.scale, rows=rows, nthreads=cores)
+        o_ref, lse_ref = ref(rows)
         t_cpu = time.perf_counter() - t_a
-        keys = (rows[:, 2] + 1) if w.causal else np.full(len(rows), N)
+        keys = visible_keys(Nq, Nk, q_offset, window)[rows[:, 2]] if w.causal else np.full(len(rows), Nk)
         sample_flops = float(np.sum(4.0 * D * keys))
         cpu_tflops = sample_flops / t_cpu / 1e12
         cpu_baseline = {"value": round(cpu_tflops, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
@@ -166,8 +236,19 @@ def main():
         log("bench: oracle %d rows in %.2f s on %d threads; parity max|dO| %.3e max|dlse| %.3e"
             % (len(rows), t_cpu, cores, parity["max_abs_dO"], parity["max_abs_dlse"]))
 
+    if args.workload == "c3":
+        metric = METRIC
+        workload = "causal attention forward bf16 B=%d H=%d N=%d D=%d %s" % (B, H, N, D, w.layout)
+    else:
+        metric = "attention fwd TFLOP/s, %s, B=%d H=%d Nq=%d Nk=%d D=%d" % (var["desc"], B, H, Nq, Nk, D)
+        workload = "attention forward bf16 %s B=%d H=%d Nq=%d Nk=%d D=%d %s" % (var["desc"], B, H, Nq, Nk, D,
+                                                                              w.layout)
+    config = {"workload": workload, "B": B, "H": H, "N": N, "D": D, "layout": w.layout, "causal": w.causal,
+              "scale": w.scale, "flop_per_step": flops}
+    if args.workload != "c3":
+        config.update({"Nq": Nq, "Nk": Nk, "q_offset": q_offset, "window": window, "kv_chunks": chunks})
     line = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -179,14 +260,13 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "causal attention forward bf16 B=%d H=%d N=%d D=%d %s" % (B, H, N, D, w.layout),
-                   "B": B, "H": H, "N": N, "D": D, "layout": w.layout, "causal": w.causal,
-                   "scale": w.scale, "flop_per_step": flops},
+        "config": config,
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline,
         "cpu_baseline": cpu_baseline,
         "parity_sample": parity,
     }
+    line.update(extra)
     print(json.dumps(line), flush=True)
 
 
