@@ -1,4 +1,5 @@
-"""The attention-forward oracle: a plain fp64 two-pass CPU implementation (``fa_oracle.c``).
+"""The attention oracle: a plain fp64 two-pass CPU implementation of the forward pass and its
+gradients (``fa_oracle.c``).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this module.  It shares no code with the HIP library and imports nothing from
@@ -53,6 +54,12 @@ def _load():
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ]
+        lib.fa_oracle_bwd_head.restype = ctypes.c_int
+        lib.fa_oracle_bwd_head.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_double,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ]
         _lib = lib
     return _lib
@@ -189,3 +196,40 @@ def merge(o_parts, lse_parts):
     o = (w[..., None] * o_s).sum(axis=0)
     o = np.where(empty[..., None], 0.0, o)
     return o, lse
+
+
+def attention_bwd(q, k, v, dout, *, dtype: str, layout: str, causal: bool, scale: float, heads=None,
+                  nthreads: int = 1):
+    """Gradients (dQ, dK, dV) of O = Softmax(scale Q K^T [+ causal]) V for upstream gradient ``dout``, in fp64.
+
+    q, k, v, dout: stored elements as in ``attention_rows`` (same shape, dtype and layout).
+    heads: None for every head -> three arrays in the input's layout; or a sequence of (b, h) pairs ->
+    three arrays [len(heads), N, D] in that order.
+    """
+    if dtype not in DTYPES:
+        raise ValueError("dtype must be one of %s" % sorted(DTYPES))
+    B, H, N, D = _dims(q.shape, layout)
+    for t in (q, k, v, dout):
+        if t.shape != q.shape or t.dtype.itemsize != ITEMSIZE[dtype]:
+            raise ValueError("q, k, v, dout must share the shape and have the itemsize of %s" % dtype)
+    q, k, v, dout = (np.ascontiguousarray(t) for t in (q, k, v, dout))
+    sel = [(b, h) for b in range(B) for h in range(H)] if heads is None else [tuple(x) for x in heads]
+    out = [np.empty((len(sel), N, D), dtype=np.float64) for _ in range(3)]
+    for n, (b, h) in enumerate(sel):
+        dq, dk, dv = (np.empty((N, D), dtype=np.float64) for _ in range(3))
+        rc = _load().fa_oracle_bwd_head(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
+                                        DTYPES[dtype], LAYOUTS[layout], B, H, N, D, 1 if causal else 0,
+                                        float(scale), int(b), int(h), dq.ctypes.data, dk.ctypes.data,
+                                        dv.ctypes.data, int(nthreads))
+        if rc != 0:
+            raise ValueError("fa_oracle_bwd_head failed with status %d" % rc)
+        out[0][n], out[1][n], out[2][n] = dq, dk, dv
+    if heads is not None:
+        return tuple(out)
+    res = []
+    for g in out:
+        g = g.reshape(B, H, N, D)
+        if layout == "BSND":
+            g = np.ascontiguousarray(g.transpose(0, 2, 1, 3))
+        res.append(g)
+    return tuple(res)

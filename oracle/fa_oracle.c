@@ -1,5 +1,6 @@
 /*
- * fa_oracle.c -- the attention-forward oracle: a plain, slow, fp64, two-pass CPU implementation.
+ * fa_oracle.c -- the attention oracle: a plain, slow, fp64, two-pass CPU implementation of the
+ * forward pass and (at the end of this file) of its gradients.
  *
  * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg
  * may load this library.  It shares no code, header or constant with the HIP library and includes
@@ -232,4 +233,162 @@ int fa_oracle_rows(const void* q, const void* k, const void* v, int dtype, int l
                    int64_t nrows, double* o_out, double* lse_out, int nthreads) {
     return fa_oracle_rows_ex(q, k, v, dtype, layout, B, H, N, N, D, causal, -1, 0, 0, N, scale, rows, nrows,
                              o_out, lse_out, nthreads);
+}
+
+/*
+ * ---------------------------------------------------------------------------------------------
+ * Backward pass (gradients of the attention forward above, plain case Nq = Nk = N).
+ *
+ * Page ai6s.net/6a0d3bfb..., section "FlashAttention在昇腾NPU上怎么跑？" (item 3, recomputation
+ * instead of storage) says the backward pass needs the forward's intermediate results and that
+ * FlashAttention recomputes them rather than storing the N x N matrices; page
+ * hwcomputing.csdn.net/6a0d4681..., section "反向传播的特殊处理", names the backward's extra
+ * `deterministic` switch.  Neither page prints the gradient formulas, so this oracle writes out
+ * the plain definition: with the upstream gradient dO (same shape as O), it returns the
+ * vector-Jacobian product of O = Softmax(scale Q K^T [+ causal mask]) V, i.e. the gradients of
+ * L = sum_{i,d} dO_id O_id with respect to Q, K and V.  By the chain rule, per row i:
+ *
+ *   s_ij  = scale * q_i . k_j            (visible j only; hidden pairs contribute nothing)
+ *   P_ij  = exp(s_ij - m_i) / l_i        (two-pass softmax, as in the forward)
+ *   dV_j += P_ij dO_i                    (O_i = sum_j P_ij v_j)
+ *   dP_ij = dO_i . v_j
+ *   D_i   = sum_j P_ij dP_ij
+ *   dS_ij = P_ij (dP_ij - D_i)           (softmax Jacobian dP_ij/ds_ik = P_ij (delta_jk - P_ik))
+ *   dQ_i += scale * dS_ij k_j
+ *   dK_j += scale * dS_ij q_i
+ *
+ * Everything is in double.  D_i is taken from P and dP as the chain rule gives it (not from O).
+ * Rows are split among the workers; each worker keeps its own dK and dV accumulators, which are
+ * added in worker order at the end.
+ * ---------------------------------------------------------------------------------------------
+ */
+typedef struct {
+    const void *q, *k, *v, *dout;
+    int dtype, layout, causal;
+    int64_t B, H, N, D, b, h;
+    double scale;
+    double *dq, *dk, *dv; /* dq: N x D shared (rows are disjoint); dk, dv: this worker's N x D */
+    int64_t first, last;
+    int status;
+} orc_bwd_job;
+
+static int64_t orc_bwd_index(const orc_bwd_job* J, int64_t i, int64_t d) {
+    if (J->layout == 0) return ((J->b * J->H + J->h) * J->N + i) * J->D + d;
+    return ((J->b * J->N + i) * J->H + J->h) * J->D + d;
+}
+
+static void* orc_bwd_worker(void* arg) {
+    orc_bwd_job* J = (orc_bwd_job*)arg;
+    const int64_t N = J->N, D = J->D;
+    double* qrow = (double*)malloc(sizeof(double) * (size_t)D);
+    double* dorow = (double*)malloc(sizeof(double) * (size_t)D);
+    double* p = (double*)malloc(sizeof(double) * (size_t)N);
+    double* dp = (double*)malloc(sizeof(double) * (size_t)N);
+    if (!qrow || !dorow || !p || !dp) {
+        free(qrow); free(dorow); free(p); free(dp);
+        J->status = -1;
+        return NULL;
+    }
+    for (int64_t i = J->first; i < J->last; ++i) {
+        const int64_t jend = J->causal ? i + 1 : N; /* visible keys 0 .. jend-1 */
+        for (int64_t d = 0; d < D; ++d) {
+            qrow[d] = orc_load(J->q, J->dtype, orc_bwd_index(J, i, d));
+            dorow[d] = orc_load(J->dout, J->dtype, orc_bwd_index(J, i, d));
+        }
+        /* softmax row, two passes */
+        double m = -INFINITY;
+        for (int64_t j = 0; j < jend; ++j) {
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; ++d) dot += qrow[d] * orc_load(J->k, J->dtype, orc_bwd_index(J, j, d));
+            p[j] = J->scale * dot;
+            if (p[j] > m) m = p[j];
+        }
+        double l = 0.0;
+        for (int64_t j = 0; j < jend; ++j) {
+            p[j] = exp(p[j] - m);
+            l += p[j];
+        }
+        for (int64_t j = 0; j < jend; ++j) p[j] /= l;
+        /* dP and D */
+        double Di = 0.0;
+        for (int64_t j = 0; j < jend; ++j) {
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; ++d) dot += dorow[d] * orc_load(J->v, J->dtype, orc_bwd_index(J, j, d));
+            dp[j] = dot;
+            Di += p[j] * dp[j];
+        }
+        /* dS and the three gradients */
+        double* dqi = J->dq + i * D;
+        for (int64_t d = 0; d < D; ++d) dqi[d] = 0.0;
+        for (int64_t j = 0; j < jend; ++j) {
+            const double ds = p[j] * (dp[j] - Di);
+            double* dkj = J->dk + j * D;
+            double* dvj = J->dv + j * D;
+            for (int64_t d = 0; d < D; ++d) {
+                dqi[d] += J->scale * ds * orc_load(J->k, J->dtype, orc_bwd_index(J, j, d));
+                dkj[d] += J->scale * ds * qrow[d];
+                dvj[d] += p[j] * dorow[d];
+            }
+        }
+    }
+    free(qrow); free(dorow); free(p); free(dp);
+    return NULL;
+}
+
+/*
+ * Gradients dQ, dK, dV (each N x D, row-major, fp64) of head (b, h) for upstream gradient `dout`
+ * (same dtype and layout as q).  Returns 0 on success, -2 on a bad argument, -1 if memory ran out.
+ */
+int fa_oracle_bwd_head(const void* q, const void* k, const void* v, const void* dout, int dtype, int layout,
+                       int64_t B, int64_t H, int64_t N, int64_t D, int causal, double scale, int64_t b,
+                       int64_t h, double* dq, double* dk, double* dv, int nthreads) {
+    if (!q || !k || !v || !dout || !dq || !dk || !dv) return -2;
+    if (dtype < 0 || dtype > 3 || layout < 0 || layout > 1) return -2;
+    if (B < 1 || H < 1 || N < 1 || D < 1 || b < 0 || b >= B || h < 0 || h >= H) return -2;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 512) nthreads = 512;
+    if (N < nthreads) nthreads = (int)N;
+    orc_bwd_job* jobs = (orc_bwd_job*)calloc((size_t)nthreads, sizeof(orc_bwd_job));
+    pthread_t* tids = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    char* running = (char*)calloc((size_t)nthreads, 1);
+    double* part = (double*)calloc((size_t)nthreads * 2 * (size_t)(N * D), sizeof(double));
+    if (!jobs || !tids || !running || !part) {
+        free(jobs); free(tids); free(running); free(part);
+        return -1;
+    }
+    for (int t = 0; t < nthreads; ++t) {
+        orc_bwd_job* J = &jobs[t];
+        J->q = q; J->k = k; J->v = v; J->dout = dout;
+        J->dtype = dtype; J->layout = layout; J->causal = causal ? 1 : 0;
+        J->B = B; J->H = H; J->N = N; J->D = D; J->b = b; J->h = h;
+        J->scale = scale;
+        J->dq = dq;
+        J->dk = part + (size_t)(2 * t) * (size_t)(N * D);
+        J->dv = part + (size_t)(2 * t + 1) * (size_t)(N * D);
+        J->first = N * t / nthreads;
+        J->last = N * (t + 1) / nthreads;
+    }
+    for (int t = 1; t < nthreads; ++t) {
+        if (pthread_create(&tids[t], NULL, orc_bwd_worker, &jobs[t]) == 0)
+            running[t] = 1;
+        else
+            orc_bwd_worker(&jobs[t]);
+    }
+    orc_bwd_worker(&jobs[0]);
+    for (int t = 1; t < nthreads; ++t)
+        if (running[t]) pthread_join(tids[t], NULL);
+    int status = 0;
+    for (int t = 0; t < nthreads; ++t)
+        if (jobs[t].status) status = jobs[t].status;
+    for (int64_t e = 0; e < N * D; ++e) {
+        double sk = 0.0, sv = 0.0;
+        for (int t = 0; t < nthreads; ++t) {
+            sk += jobs[t].dk[e];
+            sv += jobs[t].dv[e];
+        }
+        dk[e] = sk;
+        dv[e] = sv;
+    }
+    free(jobs); free(tids); free(running); free(part);
+    return status;
 }

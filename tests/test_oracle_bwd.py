@@ -1,0 +1,150 @@
+"""Pins of the oracle's backward pass (gradients of the forward) against what mathematics fixes.
+
+* central finite differences of the (separately pinned) forward oracle: the gradient is the limit of
+  difference quotients of L = sum(dO * O), whatever formula produced it;
+* torch autograd in float64 on the CPU through the plain definition (explicit scores, mask, softmax,
+  product), an independent library differentiation;
+* identities of softmax attention: sum_j dK_j = 0 (softmax is shift invariant per row), sum_j dV_j =
+  sum_i dO_i (rows of P sum to 1), dQ = dK = 0 when every key has the same value row, dQ of causal row 0
+  is 0 (it sees one key), and the closed form at scale 0 (uniform P);
+* stored 16-bit inputs are read exactly.
+"""
+import numpy as np
+import pytest
+
+import oracle
+
+
+def _rand(rng, shape, s=1.0):
+    return np.ascontiguousarray(rng.standard_normal(shape) * s)
+
+
+def _loss(q, k, v, dout, causal, scale, layout="BHSD"):
+    o, _ = oracle.attention(q, k, v, dtype="fp64", layout=layout, causal=causal, scale=scale)
+    return float((o * dout).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("layout", ["BHSD", "BSND"])
+def test_finite_differences(causal, layout):
+    rng = np.random.default_rng(11 + causal)
+    shape = (1, 2, 6, 3) if layout == "BHSD" else (1, 6, 2, 3)
+    q, k, v, dout = (_rand(rng, shape) for _ in range(4))
+    scale = 0.7
+    dq, dk, dv = oracle.attention_bwd(q, k, v, dout, dtype="fp64", layout=layout, causal=causal, scale=scale)
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = x.copy(); xp[idx] += eps
+            xm = x.copy(); xm[idx] -= eps
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            lp = _loss(args["q"], args["k"], args["v"], dout, causal, scale, layout)
+            args[name] = xm
+            lm = _loss(args["q"], args["k"], args["v"], dout, causal, scale, layout)
+            num[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g, num, atol=2e-8, rtol=0, err_msg=name)
+
+
+def _torch_grads(q, k, v, dout, causal, scale):
+    import torch
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    s = scale * (tq @ tk.transpose(-1, -2))
+    if causal:
+        n = q.shape[2]
+        s = s.masked_fill(torch.triu(torch.ones(n, n, dtype=torch.bool), diagonal=1), float("-inf"))
+    o = torch.softmax(s, dim=-1) @ tv
+    o.backward(torch.tensor(dout, dtype=torch.float64))
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("logit_scale", [1.0, 8.0])
+def test_against_torch_autograd(causal, logit_scale):
+    rng = np.random.default_rng(21 + causal)
+    shape = (2, 3, 37, 16)
+    q, k = _rand(rng, shape, logit_scale), _rand(rng, shape, logit_scale)
+    v, dout = _rand(rng, shape), _rand(rng, shape)
+    scale = 0.25
+    got = oracle.attention_bwd(q, k, v, dout, dtype="fp64", layout="BHSD", causal=causal, scale=scale, nthreads=3)
+    ref = _torch_grads(q, k, v, dout, causal, scale)
+    for name, g, r in zip("qkv", got, ref):
+        np.testing.assert_allclose(g, r, atol=1e-11 * max(1.0, np.abs(r).max()), rtol=0, err_msg=name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identities(causal):
+    rng = np.random.default_rng(31)
+    shape = (1, 2, 19, 8)
+    q, k, v, dout = (_rand(rng, shape) for _ in range(4))
+    dq, dk, dv = oracle.attention_bwd(q, k, v, dout, dtype="fp64", layout="BHSD", causal=causal, scale=0.5)
+    np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)
+    np.testing.assert_allclose(dv.sum(axis=2), dout.sum(axis=2), atol=1e-12)
+    if causal:
+        np.testing.assert_allclose(dq[:, :, 0], 0.0, atol=1e-14)
+        # the last key is seen only by the last query: dV_{N-1} = P_{N-1,N-1} dO_{N-1}
+        o, lse = oracle.attention(q, k, v, dtype="fp64", layout="BHSD", causal=True, scale=0.5)
+        p_last = np.exp(0.5 * (q[:, :, -1] * k[:, :, -1]).sum(-1) - lse[:, :, -1])
+        np.testing.assert_allclose(dv[:, :, -1], p_last[..., None] * dout[:, :, -1], atol=1e-13)
+    # the same value row for every key: O does not depend on Q or K
+    vc = np.ascontiguousarray(np.broadcast_to(v[:, :, :1], shape))
+    dq2, dk2, _ = oracle.attention_bwd(q, k, vc, dout, dtype="fp64", layout="BHSD", causal=causal, scale=0.5)
+    np.testing.assert_allclose(dq2, 0.0, atol=1e-13)
+    np.testing.assert_allclose(dk2, 0.0, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_scale_zero_closed_form(causal):
+    rng = np.random.default_rng(41)
+    shape = (1, 1, 9, 4)
+    q, k, v, dout = (_rand(rng, shape) for _ in range(4))
+    dq, dk, dv = oracle.attention_bwd(q, k, v, dout, dtype="fp64", layout="BHSD", causal=causal, scale=0.0)
+    assert np.all(dq == 0) and np.all(dk == 0)
+    N = shape[2]
+    expect = np.zeros(shape)
+    for i in range(N):
+        vis = range(i + 1) if causal else range(N)
+        for j in vis:
+            expect[0, 0, j] += dout[0, 0, i] / len(vis)
+    np.testing.assert_allclose(dv, expect, atol=1e-14)
+
+
+@pytest.mark.parametrize("dt", ["fp16", "bf16", "fp32"])
+def test_stored_types_read_exactly(dt):
+    rng = np.random.default_rng(51)
+    shape = (1, 2, 11, 8)
+    x = [rng.standard_normal(shape).astype(np.float32) for _ in range(4)]
+    if dt == "fp16":
+        stored = [a.astype(np.float16) for a in x]
+        wide = [a.astype(np.float64) for a in stored]
+    elif dt == "bf16":
+        stored = [(a.view(np.uint32) >> 16).astype(np.uint16) for a in x]
+        wide = [(s.astype(np.uint32) << 16).view(np.float32).astype(np.float64) for s in stored]
+    else:
+        stored = x
+        wide = [a.astype(np.float64) for a in x]
+    got = oracle.attention_bwd(*stored, dtype=dt, layout="BHSD", causal=True, scale=0.3)
+    ref = oracle.attention_bwd(*wide, dtype="fp64", layout="BHSD", causal=True, scale=0.3)
+    for g, r in zip(got, ref):
+        assert np.array_equal(g, r)
+
+
+def test_head_selection_and_threads():
+    rng = np.random.default_rng(61)
+    shape = (2, 3, 23, 8)
+    q, k, v, dout = (_rand(rng, shape) for _ in range(4))
+    full = oracle.attention_bwd(q, k, v, dout, dtype="fp64", layout="BHSD", causal=True, scale=0.4)
+    sel = oracle.attention_bwd(q, k, v, dout, dtype="fp64", layout="BHSD", causal=True, scale=0.4,
+                               heads=[(1, 2), (0, 1)], nthreads=5)
+    for f, s in zip(full, sel):
+        np.testing.assert_allclose(s[0], f[1, 2], atol=1e-14)
+        np.testing.assert_allclose(s[1], f[0, 1], atol=1e-14)
+
+
+def test_bad_arguments():
+    q = np.zeros((1, 1, 4, 2))
+    with pytest.raises(ValueError):
+        oracle.attention_bwd(q, q, q, np.zeros((1, 1, 4, 3)), dtype="fp64", layout="BHSD", causal=False, scale=1.0)
+    with pytest.raises(ValueError):
+        oracle.attention_bwd(q, q, q, q, dtype="fp64", layout="BHSD", causal=False, scale=1.0, heads=[(0, 1)])

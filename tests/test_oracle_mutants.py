@@ -149,3 +149,99 @@ def test_mutant_is_caught(name):
     old, new = MUTANTS[name]
     with tempfile.TemporaryDirectory() as tmp:
         assert not _pins_pass(_build(tmp, name, old, new)), "pins missed mutant " + name
+
+
+# ---- backward pass -------------------------------------------------------------------------------
+BWD_MUTANTS = {
+    "bwd_delta_dropped": ("const double ds = p[j] * (dp[j] - Di);", "const double ds = p[j] * dp[j];"),
+    "bwd_delta_sign": ("const double ds = p[j] * (dp[j] - Di);", "const double ds = p[j] * (dp[j] + Di);"),
+    "bwd_dk_unscaled": ("dkj[d] += J->scale * ds * qrow[d];", "dkj[d] += ds * qrow[d];"),
+    "bwd_dq_unscaled": ("dqi[d] += J->scale * ds * orc_load", "dqi[d] += ds * orc_load"),
+    "bwd_dv_uses_ds": ("dvj[d] += p[j] * dorow[d];", "dvj[d] += ds * dorow[d];"),
+    "bwd_dk_uses_k": ("dkj[d] += J->scale * ds * qrow[d];",
+                      "dkj[d] += J->scale * ds * orc_load(J->k, J->dtype, orc_bwd_index(J, j, d));"),
+    "bwd_dp_uses_q": ("dot += dorow[d] * orc_load(J->v", "dot += qrow[d] * orc_load(J->v"),
+    "bwd_unnormalised_p": ("for (int64_t j = 0; j < jend; ++j) p[j] /= l;", "for (int64_t j = 0; j < jend; ++j) p[j] /= 1.0;"),
+    "bwd_causal_extra_key": ("const int64_t jend = J->causal ? i + 1 : N;",
+                             "const int64_t jend = J->causal ? (i + 2 < N ? i + 2 : N) : N;"),
+    "bwd_causal_not_applied": ("const int64_t jend = J->causal ? i + 1 : N;", "const int64_t jend = N;"),
+    "bwd_no_max_subtraction": ("p[j] = exp(p[j] - m);", "p[j] = exp(p[j]);"),
+    "bwd_dv_row_is_query": ("double* dvj = J->dv + j * D;", "double* dvj = J->dv + i * D;"),
+    "bwd_partials_last_worker_only": ("sk += jobs[t].dk[e];", "sk = jobs[t].dk[e];"),
+    "bwd_bsnd_read_as_bhsd": ("if (J->layout == 0) return ((J->b * J->H + J->h) * J->N + i) * J->D + d;",
+                              "return ((J->b * J->H + J->h) * J->N + i) * J->D + d;"),
+}
+
+
+def _build_bwd(tmp, name, old, new):
+    src = open(SRC).read()
+    assert old == "" or src.count(old) == 1, name
+    path = os.path.join(tmp, name + ".c")
+    open(path, "w").write(src.replace(old, new) if old else src)
+    lib = os.path.join(tmp, name + ".so")
+    subprocess.check_call(["gcc", "-O1", "-shared", "-fPIC", "-pthread", path, "-o", lib, "-lm"])
+    f = ctypes.CDLL(lib).fa_oracle_bwd_head
+    f.restype = ctypes.c_int
+    f.argtypes = ([ctypes.c_void_p] * 4 + [ctypes.c_int] * 2 + [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_double]
+                  + [ctypes.c_int64] * 2 + [ctypes.c_void_p] * 3 + [ctypes.c_int])
+    return f
+
+
+def _bwd_call(f, q, k, v, dout, layout, causal, scale, nthreads):
+    if layout == 0:
+        B, H, N, D = q.shape
+    else:
+        B, N, H, D = q.shape
+    outs = [np.empty((B, H, N, D)) for _ in range(3)]
+    for b in range(B):
+        for h in range(H):
+            g = [np.empty((N, D)) for _ in range(3)]
+            rc = f(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data, 3, layout, B, H, N, D, causal,
+                   scale, b, h, g[0].ctypes.data, g[1].ctypes.data, g[2].ctypes.data, nthreads)
+            assert rc == 0
+            for o, x in zip(outs, g):
+                o[b, h] = x
+    return outs
+
+
+def _torch_ref(q, k, v, dout, causal, scale):
+    import torch
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    s = scale * (tq @ tk.transpose(-1, -2))
+    if causal:
+        n = q.shape[2]
+        s = s.masked_fill(torch.triu(torch.ones(n, n, dtype=torch.bool), diagonal=1), float("-inf"))
+    (torch.softmax(s, dim=-1) @ tv).backward(torch.tensor(dout))
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+def _bwd_pins_pass(f):
+    rng = np.random.default_rng(8)
+    t = lambda x: np.ascontiguousarray(x.transpose(0, 2, 1, 3))
+    for causal in (0, 1):
+        q, k, v, dout = (np.ascontiguousarray(rng.standard_normal((1, 2, 9, 4))) for _ in range(4))
+        ref = _torch_ref(q, k, v, dout, causal, 0.6)
+        for layout, args, back in ((0, (q, k, v, dout), lambda x: x), (1, tuple(map(t, (q, k, v, dout))), lambda x: x)):
+            got = _bwd_call(f, *args, layout, causal, 0.6, 3)
+            for g, r in zip(got, ref):
+                if not np.allclose(g, r, atol=1e-11):
+                    return False
+    # large logits: exponentials without the maximum overflow
+    q = np.zeros((1, 1, 5, 2)); k = np.zeros((1, 1, 5, 2))
+    v = np.ascontiguousarray(rng.standard_normal((1, 1, 5, 2))); dout = np.ascontiguousarray(rng.standard_normal((1, 1, 5, 2)))
+    q[..., 0] = 100.0; k[0, 0, :, 0] = np.arange(5) * 2.0 + np.array([0, 0, 0, 5.0, 3.001])
+    got = _bwd_call(f, q, k, v, dout, 0, 0, 1.0, 1)
+    ref = _torch_ref(q, k, v, dout, 0, 1.0)
+    return all(np.all(np.isfinite(g)) and np.allclose(g, r, atol=1e-9) for g, r in zip(got, ref))
+
+
+def test_unmutated_copy_passes_backward_pins():
+    with tempfile.TemporaryDirectory() as tmp:
+        assert _bwd_pins_pass(_build_bwd(tmp, "original_bwd", "", ""))
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_backward_mutant_is_caught(name):
+    old, new = BWD_MUTANTS[name]
+    with tempfile.TemporaryDirectory() as tmp:
+        assert not _bwd_pins_pass(_build_bwd(tmp, name, old, new)), "backward pins missed mutant " + name
