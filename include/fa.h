@@ -134,6 +134,27 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
 int fa_merge(const void* o_parts, const float* lse_parts, int64_t n_parts, void* o, float* lse, int64_t B,
              int64_t H, int64_t N, int64_t D, int layout, int dtype, void* stream);
 
+/*
+ * fa_bwd -- gradients of the attention forward: for O = softmax(scale * Q K^T [+ causal]) V (the call
+ * fa_fwd(q, k, v, o, lse, B, H, N, D, layout, causal, scale, dtype, ...) made) and the upstream gradient
+ * dout = dL/dO, writes dq = dL/dQ, dk = dL/dK, dv = dL/dV.  The N x N probabilities are recomputed from
+ * lse instead of being stored (page ai6s.net/6a0d3bfb..., section "FlashAttention在昇腾NPU上怎么跑？",
+ * item 3).  No atomics: the result is the same bit for bit on every run, i.e. the deterministic mode of
+ * page hwcomputing.csdn.net/6a0d4681..., section "反向传播的特殊处理"; there is no atomic mode.
+ *
+ * q, k, v, o, dout: same shape, layout and dtype as in fa_fwd; o is the forward's output.  Read only.
+ * lse   : the forward's [B][H][N] fp32 log-sum-exp (natural log).  Read only.
+ * dq, dk, dv: outputs, shaped like q, in `dtype`; fully overwritten.
+ * delta : caller-owned fp32 workspace of B*H*N floats; on return it holds D_i = sum_d dout_id o_id.
+ * Outputs and workspace must not overlap each other or any input.
+ * dtype : FA_DTYPE_FP16 or FA_DTYPE_BF16 (FA_DTYPE_FP32 returns FA_ERR_UNSUPPORTED).  D in {64, 128}.
+ * The call enqueues two kernels on `stream`; results are valid after the stream synchronises.  The
+ * library allocates nothing.  Check order and error codes as fa_fwd.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+           void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t N, int64_t D, int layout,
+           int causal, float scale, int dtype, void* stream);
+
 /* Static description of a status code ("ok", "null pointer", ...).  Never NULL. */
 const char* fa_status_str(int status);
 

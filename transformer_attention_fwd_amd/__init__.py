@@ -18,6 +18,10 @@ There is no CPU or framework fallback: if ``libfa.so`` is missing the first call
         the same for fa_fwd_ex (q [B,H,Nq,D] / [B,Nq,H,D], k and v [B,H,Nk,D] / [B,Nk,H,D]).
     merge(o_parts, lse_parts, *, layout, out=None, lse=None) -> (o, lse)
         fa_merge on torch tensors stacked along a leading parts dimension.
+    fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, D, layout, causal, scale, dtype, stream) -> status
+        the backward C entry point, same conventions.
+    attention_bwd(q, k, v, o, lse, dout, *, layout="BHSD", causal=False, scale=None, delta=None) -> (dq, dk, dv)
+        fa_bwd on torch tensors: allocates dq, dk, dv (and the delta workspace unless given).
 """
 from __future__ import annotations
 
@@ -25,7 +29,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "fa_fwd_ex", "fa_merge", "attention", "attention_ex", "merge", "FaError", "library_path",
+__all__ = ["fa_fwd", "fa_fwd_ex", "fa_merge", "fa_bwd", "attention", "attention_ex", "merge", "attention_bwd", "FaError", "library_path",
            "load", "status_str", "version",
            "LAYOUT_BHSD", "LAYOUT_BSND", "DTYPE_FP32", "DTYPE_FP16", "DTYPE_BF16"]
 
@@ -78,6 +82,9 @@ def load():
         lib.fa_merge.restype = ctypes.c_int
         lib.fa_merge.argtypes = ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p] +
                                  [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p])
+        lib.fa_bwd.restype = ctypes.c_int
+        lib.fa_bwd.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_int,
+                               ctypes.c_float, ctypes.c_int, ctypes.c_void_p])
         lib.fa_status_str.restype = ctypes.c_char_p
         lib.fa_status_str.argtypes = [ctypes.c_int]
         lib.fa_last_error.restype = ctypes.c_char_p
@@ -105,6 +112,13 @@ def fa_merge(o_parts, lse_parts, n_parts, o, lse, B, H, N, D, layout, dtype, str
     """The C merge entry point: pointers are ints (0 = NULL), returns the status code."""
     return load().fa_merge(o_parts or None, lse_parts or None, n_parts, o or None, lse or None, B, H, N, D,
                            layout, dtype, stream or None)
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, D, layout, causal, scale, dtype, stream) -> int:
+    """The backward C entry point: pointers are ints (0 = NULL), returns the status code."""
+    return load().fa_bwd(q or None, k or None, v or None, o or None, lse or None, dout or None, dq or None,
+                         dk or None, dv or None, delta or None, B, H, N, D, layout, int(causal), scale, dtype,
+                         stream or None)
 
 
 def status_str(status: int) -> str:
@@ -243,3 +257,33 @@ def merge(o_parts, lse_parts, *, layout: str = "BHSD", out=None, lse=None):
     _raise_on(fa_merge(o_parts.data_ptr(), lse_parts.data_ptr(), S, out.data_ptr(), lse.data_ptr(), B, H, N, D,
                        _LAYOUTS[layout], _dtype_code(o_parts), stream))
     return out, lse
+
+
+def attention_bwd(q, k, v, o, lse, dout, *, layout: str = "BHSD", causal: bool = False, scale: float | None = None,
+                  delta=None):
+    """dQ, dK, dV for torch device tensors (q, k, v, o, dout of one shape; lse [B, H, N] fp32 from the forward)."""
+    import torch
+    if layout not in _LAYOUTS:
+        raise ValueError("layout must be 'BHSD' or 'BSND'")
+    if q.dim() != 4 or any(t.shape != q.shape for t in (k, v, o, dout)):
+        raise ValueError("q, k, v, o, dout must be 4-D tensors of one shape")
+    if any(t.dtype != q.dtype for t in (k, v, o, dout)):
+        raise TypeError("q, k, v, o, dout must share a dtype")
+    for t in (q, k, v, o, dout):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v, o, dout must be contiguous in the given layout")
+    B, H, N, D = _bhnd(q, layout)
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of shape [B, H, N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if delta is None:
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if delta.shape != (B, H, N) or delta.dtype != torch.float32 or not delta.is_contiguous():
+        raise ValueError("delta must be a contiguous float32 tensor of shape [B, H, N]")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    stream = torch.cuda.current_stream(q.device).cuda_stream if q.is_cuda else 0
+    _raise_on(fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, D, _LAYOUTS[layout],
+                     causal, float(scale), _dtype_code(q), stream))
+    return dq, dk, dv

@@ -70,7 +70,7 @@ FA_API const char* fa_status_str(int status) {
 
 FA_API const char* fa_last_error(void) { return g_last_error; }
 
-FA_API int fa_version(void) { return 200; }  // 0.2.0
+FA_API int fa_version(void) { return 300; }  // 0.3.0
 
 FA_API int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                      int64_t Nq, int64_t Nk, int64_t D, int layout, int causal, int64_t window, int64_t q_offset,
@@ -203,6 +203,91 @@ FA_API int fa_merge(const void* o_parts, const float* lse_parts, int64_t n_parts
   const int kd = dtype == FA_DTYPE_FP32 ? fa::kDtypeFp32 : dtype == FA_DTYPE_FP16 ? fa::kDtypeFp16 : fa::kDtypeBf16;
   e = fa::launch_merge(o_parts, lse_parts, (int)n_parts, o, lse, rows, B, H, N, (int)D,
                        layout == FA_LAYOUT_BSND ? 1 : 0, kd, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    set_error("kernel launch", e);
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t N, int64_t D,
+                  int layout, int causal, float scale, int dtype, void* stream) {
+  // ---- pure argument checks (no HIP calls) ----
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return FA_ERR_NULL;
+  if (layout != FA_LAYOUT_BHSD && layout != FA_LAYOUT_BSND) return FA_ERR_BAD_LAYOUT;
+  if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_BAD_DTYPE;
+  if (B < 1 || H < 1 || N < 1 || D < 1) return FA_ERR_BAD_DIM;
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_DTYPE_FP32) return FA_ERR_UNSUPPORTED;
+  int64_t bh, rows, elems, bytes, row_bytes;
+  if (N > kMaxRows || !mul_ok(B, H, &bh) || bh > INT32_MAX || !mul_ok(bh, N, &rows) || !mul_ok(rows, D, &elems) ||
+      !mul_ok(elems, 2, &bytes) || !mul_ok(rows, 4, &row_bytes))
+    return FA_ERR_UNSUPPORTED;
+  const int64_t rpw = fa::bwd_rows_per_workgroup();
+  if (bh * ((N + rpw - 1) / rpw) > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  const int64_t stride_bytes = (layout == FA_LAYOUT_BHSD ? D : H * D) * 2;
+  if ((N - 1) * stride_bytes + D * 2 > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  if (!isfinite(scale) || !isfinite(fabsf(scale) * 1.4426950408889634f)) return FA_ERR_BAD_SCALE;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse | (uintptr_t)dout |
+       (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)delta) & 15)
+    return FA_ERR_MISALIGNED;
+  const void* ins[6] = {q, k, v, o, lse, dout};
+  const int64_t in_bytes[6] = {bytes, bytes, bytes, bytes, row_bytes, bytes};
+  const void* outs[4] = {dq, dk, dv, delta};
+  const int64_t out_bytes[4] = {bytes, bytes, bytes, row_bytes};
+  for (int a = 0; a < 4; ++a) {
+    for (int i = 0; i < 6; ++i)
+      if (overlaps(outs[a], out_bytes[a], ins[i], in_bytes[i])) return FA_ERR_ALIAS;
+    for (int c = a + 1; c < 4; ++c)
+      if (overlaps(outs[a], out_bytes[a], outs[c], out_bytes[c])) return FA_ERR_ALIAS;
+  }
+
+  // ---- device residency ----
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) {
+    set_error("hipGetDevice", e);
+    return FA_ERR_HIP;
+  }
+  for (const void* ptr : ins) {
+    const int st = check_device(ptr, device);
+    if (st != FA_OK) return st;
+  }
+  for (const void* ptr : outs) {
+    const int st = check_device(ptr, device);
+    if (st != FA_OK) return st;
+  }
+
+  // ---- launch ----
+  fa::BwdParams p;
+  memset(&p, 0, sizeof p);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.delta = delta;
+  p.B = (int)B;
+  p.H = (int)H;
+  p.N = (int)N;
+  if (layout == FA_LAYOUT_BHSD) {
+    p.stride_b = H * N * D;
+    p.stride_h = N * D;
+    p.stride_s = D;
+  } else {
+    p.stride_b = N * H * D;
+    p.stride_h = D;
+    p.stride_s = H * D;
+  }
+  p.c = scale * 1.4426950408889634f;
+  p.scale = scale;
+  e = fa::launch_bwd(p, dtype == FA_DTYPE_FP16 ? fa::kDtypeFp16 : fa::kDtypeBf16, (int)D, causal != 0,
+                     (hipStream_t)stream);
   if (e != hipSuccess) {
     set_error("kernel launch", e);
     return FA_ERR_HIP;

@@ -1,0 +1,497 @@
+// fa_bwd.hip -- attention backward kernels for gfx950 (MI355X, CDNA4), 16-bit inputs.
+//
+// What is computed: for O = softmax(scale * Q K^T [+ causal mask]) V and an upstream gradient dO, the
+// gradients dQ, dK, dV (the vector-Jacobian product).  With P the softmax probabilities,
+//     dV = P^T dO,   dP = dO V^T,   D_i = sum_d dO_id O_id,   dS = P o (dP - D),
+//     dQ = scale * dS K,   dK = scale * dS^T Q.
+// P is never stored: it is recomputed tile by tile from the forward's per-row lse as
+// exp(scale * q.k - lse).  Pages: ai6s.net/6a0d3bfb..., section "FlashAttention在昇腾NPU上怎么跑？",
+// item 3 (the backward recomputes the forward's intermediates instead of storing the N x N matrices);
+// hwcomputing.csdn.net/6a0d4681..., section "反向传播的特殊处理" (a deterministic mode next to one that
+// accumulates with atomics).  D_i = rowsum(dO o O) equals sum_j P_ij dP_ij because O_i = sum_j P_ij v_j.
+//
+// Deterministic by construction: no atomics.  Two kernels, run in this order on one stream:
+//   fa_bwd_dq   one workgroup per (b, h, 128-query tile); walks the K/V tiles (keys up to the tile's
+//               last query when causal).  Computes D for its rows (stored to the caller's workspace),
+//               then per K/V tile S^T = K Q^T, dP^T = V dO^T, dS^T, and dQ^T += K^T dS^T.
+//   fa_bwd_dkdv one workgroup per (b, h, 128-key tile); K and V stay in registers; walks the Q/dO
+//               tiles (queries from the tile's first key on when causal).  Per 32-query step S = Q K^T,
+//               dP = dO V^T, P, dS, then dV^T += dO^T P and dK^T += Q^T dS.
+//
+// gfx950 mapping (both kernels): v_mfma_f32_16x16x32_{bf16,f16}; the streamed operand arrives by
+// buffer_load ... lds into a 2-stage LDS ring.  A tensor read both as rows (ds_read_b128, 16 consecutive
+// rows at one logical 16-byte chunk) and transposed (ds_read_b64_tr_b16, 4 consecutive rows x 2 adjacent
+// chunks) uses one XOR swizzle of the chunk index that keeps both access patterns free of bank conflicts.
+// MFMA accumulator tiles are reused as the next product's operands without leaving registers: a 16x16
+// C tile holds column j in lane j, which is the lane layout of both A rows and B columns.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kPosInf = __builtin_inff();
+
+template <int D>
+struct BwdTile {
+  static constexpr int NW = 4;            // waves per workgroup
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int CHUNKS = D / 8;    // 16-byte chunks per row
+  static constexpr int DC = D / 32;       // 32-wide d chunks: k dimension of the S and dP products
+  static constexpr int DT = D / 16;       // 16-wide d tiles: rows of dQ^T, dK^T, dV^T
+  // Chunk swizzle for tiles read both ways.  Row reads: the 16 rows r..r+15 at one logical chunk land on
+  // 16 (D = 128) or, per row parity, 8 (D = 64) different physical chunks.  Transposing reads: rows
+  // 4e..4e+3 at logical chunks 2t, 2t+1 land on 8 different physical chunks (per row parity for D = 64).
+  // Depends on the row only through its low 4 bits, so a 16-row step keeps a lane's offset.
+  __device__ static __forceinline__ int swz(int row) {
+    return D == 128 ? (((row & 7) << 1) | ((row >> 3) & 1)) : ((((row >> 1) & 3) << 1) | ((row >> 3) & 1));
+  }
+};
+
+// 8 consecutive elements of a row held in LDS (row read): base + lane offset + row step.
+template <typename vec8>
+__device__ __forceinline__ vec8 row_frag(const uint8_t* base, int lane_off, int step) {
+  return *(const vec8*)(base + lane_off + step);
+}
+
+// Transposing read of a 32-row x 16-column block: lane li of group g receives column li of rows
+// 4g..4g+3 and 16+4g..16+4g+3 (relative to `step`), the A-operand layout of a product whose k index runs
+// over those rows.
+template <int ROW_BYTES, typename vec8>
+__device__ __forceinline__ vec8 tr_frag(const uint8_t* base, int lane_off, int step) {
+  const uint8_t* a0 = base + lane_off + step;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a0);
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a0 + 16 * ROW_BYTES));
+  u32x4_t w = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
+               __builtin_bit_cast(u32x2_t, hi)[0], __builtin_bit_cast(u32x2_t, hi)[1]};
+  return __builtin_bit_cast(vec8, w);
+}
+
+template <typename vec8>
+__device__ __forceinline__ vec8 as_vec8(const uint32_t (&w)[4]) {
+  return __builtin_bit_cast(vec8, u32x4_t{w[0], w[1], w[2], w[3]});
+}
+
+template <bool IS_BF16>
+__device__ __forceinline__ float to_f32(typename Elem<IS_BF16>::vec8 x, int e) {
+  return (float)x[e];
+}
+
+// Per-lane LDS offsets: row reads of logical chunk 4c+g of row li, and transposing reads of column
+// 16*dt + 4*(li&3) of row 4g + (li>>2).
+template <int D>
+__device__ __forceinline__ void lane_offsets(int li, int g, int (&rb)[BwdTile<D>::DC], int (&tb)[BwdTile<D>::DT]) {
+  typedef BwdTile<D> T;
+#pragma unroll
+  for (int c = 0; c < T::DC; ++c) rb[c] = li * T::ROW_BYTES + (((4 * c + g) ^ T::swz(li)) << 4);
+#pragma unroll
+  for (int dt = 0; dt < T::DT; ++dt) {
+    const int row = 4 * g + (li >> 2);
+    const int col = 16 * dt + 4 * (li & 3);
+    tb[dt] = row * T::ROW_BYTES + (((col >> 3) ^ T::swz(row)) << 4) + (col & 7) * 2;
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// dQ (and D) : one workgroup per (b, h, 128-query tile)
+// ------------------------------------------------------------------------------------------------
+template <int D, bool IS_BF16, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
+  typedef BwdTile<D> T;
+  typedef Elem<IS_BF16> E;
+  typedef typename E::vec8 vec8;
+  constexpr int NW = T::NW, QW = 32, BM = NW * QW, BN = 64;
+  constexpr int QG = QW / 16, KT = BN / 16, KC = BN / 32;
+  constexpr int TILE_BYTES = BN * T::ROW_BYTES;
+  constexpr int LOADS = TILE_BYTES / (16 * 64 * NW);
+  __shared__ __attribute__((aligned(1024))) uint8_t ks0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs1[TILE_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, li = lane & 15;
+  int bh, qt;
+  unit_of(blockIdx.x, p.n_units, p.n_tiles, CAUSAL, bh, qt);
+  const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
+  const int N = p.N;
+  const int q_wg = qt * BM, q0 = q_wg + wave * QW;
+  const int64_t head = b * p.stride_b + h * p.stride_h;
+  const int64_t ss = p.stride_s;
+
+  // K/V tiles: keys 0 .. k_last
+  const int k_last = CAUSAL ? min(N - 1, q_wg + BM - 1) : N - 1;
+  const int n_kt = k_last / BN + 1;
+  const int row_bytes = (int)(2 * ss);
+  const int span = (N - 1) * row_bytes + T::ROW_BYTES;  // the host keeps this below 2^31
+  const __amdgpu_buffer_rsrc_t kbuf =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.k + head), 0, span, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vbuf =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.v + head), 0, span, kBufferFlags);
+  int voff[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int slot = (i * NW + wave) * 64 + lane;
+    const int row = slot / T::CHUNKS, pc = slot % T::CHUNKS;
+    voff[i] = row * row_bytes + ((pc ^ T::swz(row)) << 4);
+  }
+  auto issue_tile = [&](int j, uint8_t* kdst, uint8_t* vdst) __attribute__((always_inline)) {
+    issue_kv_tile<LOADS, NW>(kbuf, vbuf, voff, voff, j * BN * row_bytes, wave, kdst, vdst);
+  };
+  issue_tile(0, ks0, vs0);
+
+  // Q and dO fragments (B operands of S^T = K Q^T and dP^T = V dO^T): row q0 + 16*qg + li, d 32c+8g..+7.
+  // D_i = sum_d dO_id O_id from the same fragment pattern of O, summed over the 4 lane groups.
+  const uint16_t* qp = (const uint16_t*)p.q + head;
+  const uint16_t* dop = (const uint16_t*)p.dout + head;
+  const uint16_t* op = (const uint16_t*)p.o + head;
+  vec8 qf[QG][T::DC], df[QG][T::DC];
+  float lse2[QG], dlt[QG];
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    const int qi = q0 + 16 * qg + li;
+    const int qrow = min(qi, N - 1);
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < T::DC; ++c) {
+      const int64_t e = qrow * ss + 32 * c + 8 * g;
+      qf[qg][c] = *(const vec8*)(qp + e);
+      df[qg][c] = *(const vec8*)(dop + e);
+      const vec8 of = *(const vec8*)(op + e);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) acc = __builtin_fmaf(to_f32<IS_BF16>(df[qg][c], x), to_f32<IS_BF16>(of, x), acc);
+    }
+    dlt[qg] = wave_sum_xor16_32(acc);
+    lse2[qg] = p.lse[(int64_t)bh * N + qrow] * kLog2e;
+    if (g == 0 && qi < N) p.delta[(int64_t)bh * N + qi] = dlt[qg];
+  }
+
+  const float cexp = p.c;  // scale * log2(e), signed
+  f32x4_t dqa[QG][T::DT];
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg)
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt) dqa[qg][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  int rb[T::DC], tb[T::DT];
+  lane_offsets<D>(li, g, rb, tb);
+
+  auto step = [&](int j, const uint8_t* ks, const uint8_t* vs, uint8_t* kn, uint8_t* vn, auto last_c)
+      __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    lds_barrier();
+    if constexpr (!decltype(last_c)::value) issue_tile(j + 1, kn, vn);
+    const int key0 = j * BN;
+    const bool active = !CAUSAL || key0 <= q0 + QW - 1;
+    if (active) {
+      const bool need_mask = (CAUSAL && key0 + BN - 1 > q0) || (key0 + BN > N);
+      uint32_t dsf[QG][KC][4];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        f32x4_t s[QG], dp[QG];
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) {
+          s[qg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          dp[qg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int c = 0; c < T::DC; ++c) {
+          const vec8 kf = row_frag<vec8>(ks, rb[c], 16 * kt * T::ROW_BYTES);
+          const vec8 vf = row_frag<vec8>(vs, rb[c], 16 * kt * T::ROW_BYTES);
+#pragma unroll
+          for (int qg = 0; qg < QG; ++qg) {
+            s[qg] = E::mfma(kf, qf[qg][c], s[qg]);
+            dp[qg] = E::mfma(vf, df[qg][c], dp[qg]);
+          }
+        }
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg) {
+          // lane holds keys key0 + 16*kt + 4*g + r for query q0 + 16*qg + li
+          int hi = BN;  // slots 16*kt + r above hi are hidden
+          if (need_mask) {
+            const int qi = q0 + 16 * qg + li;
+            hi = (CAUSAL ? min(N - 1, qi) : N - 1) - key0 - 4 * g;
+          }
+          float ds[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float a = __builtin_fmaf(s[qg][r], cexp, -lse2[qg]);
+            if (16 * kt + r > hi) a = kNegInf;
+            ds[r] = __builtin_amdgcn_exp2f(a) * (dp[qg][r] - dlt[qg]);
+          }
+          const int kc = kt >> 1, half = kt & 1;
+          dsf[qg][kc][2 * half + 0] = E::pack2(ds[0], ds[1]);
+          dsf[qg][kc][2 * half + 1] = E::pack2(ds[2], ds[3]);
+        }
+      }
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int dt = 0; dt < T::DT; ++dt) {
+          const vec8 kt_frag = tr_frag<T::ROW_BYTES, vec8>(ks, tb[dt], 32 * kc * T::ROW_BYTES);
+#pragma unroll
+          for (int qg = 0; qg < QG; ++qg) dqa[qg][dt] = E::mfma(kt_frag, as_vec8<vec8>(dsf[qg][kc]), dqa[qg][dt]);
+        }
+    }
+  };
+
+  const std::integral_constant<bool, false> more;
+  const std::integral_constant<bool, true> last;
+  int j = 0;
+  for (; j + 2 < n_kt; j += 2) {
+    step(j, ks0, vs0, ks1, vs1, more);
+    step(j + 1, ks1, vs1, ks0, vs0, more);
+  }
+  if (j + 2 == n_kt) {
+    step(j, ks0, vs0, ks1, vs1, more);
+    step(j + 1, ks1, vs1, ks0, vs0, last);
+  } else {
+    step(j, ks0, vs0, ks1, vs1, last);
+  }
+
+  // dQ = scale * accumulated (dS K); lane holds d = 16*dt + 4*g + r of query q0 + 16*qg + li
+  uint16_t* dqp = (uint16_t*)p.dq + head;
+#pragma unroll
+  for (int qg = 0; qg < QG; ++qg) {
+    const int qi = q0 + 16 * qg + li;
+    if (qi < N) {
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt) {
+        const f32x4_t x = dqa[qg][dt] * p.scale;
+        *(u32x2_t*)(dqp + qi * ss + 16 * dt + 4 * g) = u32x2_t{E::pack2(x[0], x[1]), E::pack2(x[2], x[3])};
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// dK, dV : one workgroup per (b, h, 128-key tile)
+// ------------------------------------------------------------------------------------------------
+template <int D, bool IS_BF16, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void fa_bwd_dkdv(BwdParams p) {
+  typedef BwdTile<D> T;
+  typedef Elem<IS_BF16> E;
+  typedef typename E::vec8 vec8;
+  constexpr int NW = T::NW, KW = 32, BK = NW * KW;  // keys per wave, per workgroup
+  constexpr int BQ = 64, QS = 32;                   // queries per LDS tile, per step
+  constexpr int KG = KW / 16, QGS = QS / 16;
+  constexpr int TILE_BYTES = BQ * T::ROW_BYTES;
+  constexpr int LOADS = TILE_BYTES / (16 * 64 * NW);
+  __shared__ __attribute__((aligned(1024))) uint8_t qs0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t qs1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t os0[TILE_BYTES];  // dO
+  __shared__ __attribute__((aligned(1024))) uint8_t os1[TILE_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, li = lane & 15;
+  int bh, kt;
+  unit_of(blockIdx.x, p.n_units, p.n_tiles, false, bh, kt);  // causal: key tile 0 (most queries) first
+  const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
+  const int N = p.N;
+  const int k_wg = kt * BK, kw0 = k_wg + wave * KW;
+  const int64_t head = b * p.stride_b + h * p.stride_h;
+  const int64_t ss = p.stride_s;
+
+  // K and V of the wave's keys as B operands of S = Q K^T and dP = dO V^T: lane holds key kw0 + 16*kg + li,
+  // d 32c + 8g .. +7; keys past the end are zero (their gradients are not stored)
+  const uint16_t* kp = (const uint16_t*)p.k + head;
+  const uint16_t* vp = (const uint16_t*)p.v + head;
+  vec8 kf[KG][T::DC], vf[KG][T::DC];
+#pragma unroll
+  for (int kg = 0; kg < KG; ++kg) {
+    const int key = kw0 + 16 * kg + li;
+    const int krow = min(key, N - 1);
+#pragma unroll
+    for (int c = 0; c < T::DC; ++c) {
+      const int64_t e = krow * ss + 32 * c + 8 * g;
+      u32x4_t kr = *(const u32x4_t*)(kp + e), vr = *(const u32x4_t*)(vp + e);
+      if (key >= N) kr = vr = u32x4_t{0u, 0u, 0u, 0u};
+      kf[kg][c] = __builtin_bit_cast(vec8, kr);
+      vf[kg][c] = __builtin_bit_cast(vec8, vr);
+    }
+  }
+
+  // Q/dO tiles from the first one holding a query that sees a key of this workgroup
+  const int qt_begin = CAUSAL ? k_wg / BQ : 0;
+  const int n_qt = (N + BQ - 1) / BQ - qt_begin;
+  const int row_bytes = (int)(2 * ss);
+  const int span = (N - 1) * row_bytes + T::ROW_BYTES;
+  const __amdgpu_buffer_rsrc_t qbuf =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.q + head), 0, span, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t obuf =
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.dout + head), 0, span, kBufferFlags);
+  int voff[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int slot = (i * NW + wave) * 64 + lane;
+    const int row = slot / T::CHUNKS, pc = slot % T::CHUNKS;
+    voff[i] = row * row_bytes + ((pc ^ T::swz(row)) << 4);
+  }
+  auto issue_tile = [&](int j, uint8_t* qdst, uint8_t* odst) __attribute__((always_inline)) {
+    issue_kv_tile<LOADS, NW>(qbuf, obuf, voff, voff, (qt_begin + j) * BQ * row_bytes, wave, qdst, odst);
+  };
+  issue_tile(0, qs0, os0);
+
+  const float cexp = p.c;
+  const float* lse_h = p.lse + (int64_t)bh * N;
+  const float* dlt_h = p.delta + (int64_t)bh * N;
+  f32x4_t dka[KG][T::DT], dva[KG][T::DT];
+#pragma unroll
+  for (int kg = 0; kg < KG; ++kg)
+#pragma unroll
+    for (int dt = 0; dt < T::DT; ++dt) {
+      dka[kg][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      dva[kg][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  int rb[T::DC], tb[T::DT];
+  lane_offsets<D>(li, g, rb, tb);
+
+  auto step = [&](int j, const uint8_t* qs, const uint8_t* os, uint8_t* qn, uint8_t* on, auto last_c)
+      __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    lds_barrier();
+    // log2-domain lse and D of the lane's rows of this tile: query tile0 + QS*hh + 16*qq + 4*g + r (past the
+    // end: no weight).  Loaded before the next tile's DMA is issued, so that waiting for them (the
+    // memory counter retires in order) does not also wait for that DMA.
+    const int tile0 = (qt_begin + j) * BQ;
+    float l2[BQ / QS][QGS][4], dl[BQ / QS][QGS][4];
+#pragma unroll
+    for (int hh = 0; hh < BQ / QS; ++hh)
+#pragma unroll
+      for (int qq = 0; qq < QGS; ++qq)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int qi = tile0 + QS * hh + 16 * qq + 4 * g + r;
+          const bool ok = qi < N;
+          const int qc = ok ? qi : N - 1;
+          l2[hh][qq][r] = ok ? lse_h[qc] * kLog2e : kPosInf;
+          dl[hh][qq][r] = ok ? dlt_h[qc] : 0.f;
+        }
+    if constexpr (!decltype(last_c)::value) issue_tile(j + 1, qn, on);
+#pragma unroll
+    for (int hh = 0; hh < BQ / QS; ++hh) {
+      const int qh0 = tile0 + QS * hh;  // first query of this step
+      const bool active = qh0 < N && (!CAUSAL || qh0 + QS - 1 >= kw0);
+      if (active) {
+        const bool need_mask = CAUSAL && qh0 < kw0 + KW - 1;
+        uint32_t pp[KG][4], dsp[KG][4];
+#pragma unroll
+        for (int qq = 0; qq < QGS; ++qq) {
+          f32x4_t s[KG], dp[KG];
+#pragma unroll
+          for (int kg = 0; kg < KG; ++kg) {
+            s[kg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            dp[kg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+          for (int c = 0; c < T::DC; ++c) {
+            const vec8 qa = row_frag<vec8>(qs, rb[c], (QS * hh + 16 * qq) * T::ROW_BYTES);
+            const vec8 oa = row_frag<vec8>(os, rb[c], (QS * hh + 16 * qq) * T::ROW_BYTES);
+#pragma unroll
+            for (int kg = 0; kg < KG; ++kg) {
+              s[kg] = E::mfma(qa, kf[kg][c], s[kg]);
+              dp[kg] = E::mfma(oa, vf[kg][c], dp[kg]);
+            }
+          }
+#pragma unroll
+          for (int kg = 0; kg < KG; ++kg) {
+            // lane holds queries qh0 + 16*qq + 4*g + r for key kw0 + 16*kg + li
+            int lo = 0;  // rows r < lo are hidden (query before key)
+            if (need_mask) lo = kw0 + 16 * kg + li - (qh0 + 16 * qq + 4 * g);
+            float pr[4], ds[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              float a = __builtin_fmaf(s[kg][r], cexp, -l2[hh][qq][r]);
+              if (r < lo) a = kNegInf;
+              pr[r] = __builtin_amdgcn_exp2f(a);
+              ds[r] = pr[r] * (dp[kg][r] - dl[hh][qq][r]);
+            }
+            pp[kg][2 * qq + 0] = E::pack2(pr[0], pr[1]);
+            pp[kg][2 * qq + 1] = E::pack2(pr[2], pr[3]);
+            dsp[kg][2 * qq + 0] = E::pack2(ds[0], ds[1]);
+            dsp[kg][2 * qq + 1] = E::pack2(ds[2], ds[3]);
+          }
+        }
+        // dV^T += dO^T P ;  dK^T += Q^T dS  (k index over this step's 32 queries)
+#pragma unroll
+        for (int dt = 0; dt < T::DT; ++dt) {
+          const vec8 ot = tr_frag<T::ROW_BYTES, vec8>(os, tb[dt], QS * hh * T::ROW_BYTES);
+          const vec8 qtf = tr_frag<T::ROW_BYTES, vec8>(qs, tb[dt], QS * hh * T::ROW_BYTES);
+#pragma unroll
+          for (int kg = 0; kg < KG; ++kg) {
+            dva[kg][dt] = E::mfma(ot, as_vec8<vec8>(pp[kg]), dva[kg][dt]);
+            dka[kg][dt] = E::mfma(qtf, as_vec8<vec8>(dsp[kg]), dka[kg][dt]);
+          }
+        }
+      }
+    }
+  };
+
+  const std::integral_constant<bool, false> more;
+  const std::integral_constant<bool, true> last;
+  int j = 0;
+  for (; j + 2 < n_qt; j += 2) {
+    step(j, qs0, os0, qs1, os1, more);
+    step(j + 1, qs1, os1, qs0, os0, more);
+  }
+  if (j + 2 == n_qt) {
+    step(j, qs0, os0, qs1, os1, more);
+    step(j + 1, qs1, os1, qs0, os0, last);
+  } else {
+    step(j, qs0, os0, qs1, os1, last);
+  }
+
+  // dK = scale * accumulated (dS^T Q), dV: lane holds d = 16*dt + 4*g + r of key kw0 + 16*kg + li
+  uint16_t* dkp = (uint16_t*)p.dk + head;
+  uint16_t* dvp = (uint16_t*)p.dv + head;
+#pragma unroll
+  for (int kg = 0; kg < KG; ++kg) {
+    const int key = kw0 + 16 * kg + li;
+    if (key < N) {
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt) {
+        const f32x4_t x = dka[kg][dt] * p.scale;
+        const f32x4_t y = dva[kg][dt];
+        *(u32x2_t*)(dkp + key * ss + 16 * dt + 4 * g) = u32x2_t{E::pack2(x[0], x[1]), E::pack2(x[2], x[3])};
+        *(u32x2_t*)(dvp + key * ss + 16 * dt + 4 * g) = u32x2_t{E::pack2(y[0], y[1]), E::pack2(y[2], y[3])};
+      }
+    }
+  }
+}
+
+template <int D, bool IS_BF16, bool CAUSAL>
+hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
+  p.n_tiles = (p.N + 127) / 128;
+  p.n_units = p.B * p.H * p.n_tiles;
+  hipLaunchKernelGGL((fa_bwd_dq<D, IS_BF16, CAUSAL>), dim3(p.n_units), dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fa_bwd_dkdv<D, IS_BF16, CAUSAL>), dim3(p.n_units), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, bool IS_BF16>
+hipError_t launch_bwd_c(const BwdParams& p, bool causal, hipStream_t stream) {
+  return causal ? launch_bwd_t<D, IS_BF16, true>(p, stream) : launch_bwd_t<D, IS_BF16, false>(p, stream);
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdParams& p, int dtype, int d, bool causal, hipStream_t stream) {
+  const bool bf = dtype == kDtypeBf16;
+  if (d == 128) return bf ? launch_bwd_c<128, true>(p, causal, stream) : launch_bwd_c<128, false>(p, causal, stream);
+  return bf ? launch_bwd_c<64, true>(p, causal, stream) : launch_bwd_c<64, false>(p, causal, stream);
+}
+
+int bwd_rows_per_workgroup() { return 128; }
+
+}  // namespace fa

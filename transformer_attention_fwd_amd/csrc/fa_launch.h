@@ -36,12 +36,38 @@ struct Params {
   uint32_t qsign;   // XOR mask applied to Q's stored bits: flips the sign when scale < 0
 };
 
+// Backward kernel arguments (Nq = Nk = N; all ten tensors share the layout's strides, in elements).
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;   // [B][H][N], natural log, from the forward
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;       // [B][H][N] workspace: D_i = sum_d dO_id O_id, written by the dQ kernel
+  int64_t stride_b, stride_h, stride_s;
+  int B, H, N;
+  int n_tiles;        // filled by the launcher
+  int n_units;        // filled by the launcher
+  float c;            // scale * log2(e), signed
+  float scale;
+};
+
 // Enqueue the attention kernel for (dtype, d, causal, window >= 0) on `stream`.
 hipError_t launch(const Params& p, int dtype, int d, bool causal, hipStream_t stream);
 
 // Enqueue the combination of n_parts partial results (see fa_merge in fa.h).
 hipError_t launch_merge(const void* o_parts, const float* lse_parts, int n_parts, void* o, float* lse, int64_t rows,
                         int64_t B, int64_t H, int64_t N, int D, int layout_bsnd, int dtype, hipStream_t stream);
+
+// Enqueue the two backward kernels (dQ and D, then dK and dV) for a 16-bit dtype on `stream`.
+hipError_t launch_bwd(const BwdParams& p, int dtype, int d, bool causal, hipStream_t stream);
+
+// Query (and key) rows handled by one backward workgroup.
+int bwd_rows_per_workgroup();
 
 // Queries handled by one workgroup for a dtype (for callers that size grids or count work).
 int queries_per_workgroup(int dtype);

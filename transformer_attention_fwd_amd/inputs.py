@@ -18,7 +18,9 @@ so Gaussian activations of the same attention shapes stand in for them:
 
 Draw recipe: ``numpy.random.default_rng([42, c])``; Q, K, V = ``standard_normal((B, H, N, D), float32)``
 in that order, in logical [B, H, N, D] order, multiplied by the config's factor, rounded to the
-config's dtype (nearest-even), then stored in the config's layout.
+config's dtype (nearest-even), then stored in the config's layout.  The upstream gradient dO of the
+backward pass comes from its own stream, ``default_rng([42, c, 7])``, as one more standard normal draw
+of the same shape, rounded and stored the same way.
 """
 from __future__ import annotations
 
@@ -127,6 +129,12 @@ def make(B: int, H: int, N: int, D: int, *, layout: str, dtype: str, seed, qk_mu
     """Stored Q, K, V (element bits of ``dtype``, packed in ``layout``) for generator seed ``[42, seed]``."""
     q, k, v = draw_f32(B, H, N, D, seed, qk_mult)
     return tuple(to_layout(cast_bits(t, dtype), layout) for t in (q, k, v))
+
+
+def make_grad(B: int, H: int, N: int, D: int, *, layout: str, dtype: str, seed):
+    """Stored upstream gradient dO (element bits of ``dtype``, packed in ``layout``) for ``[42, seed, 7]``."""
+    rng = np.random.default_rng([42] + ([seed] if np.isscalar(seed) else list(seed)) + [7])
+    return to_layout(cast_bits(rng.standard_normal((B, H, N, D), dtype=np.float32), dtype), layout)
 
 
 def make_workload(w: Workload, dtype: str | None = None):
