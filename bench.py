@@ -21,7 +21,10 @@ Options: --gpus N (only 1 is supported), --steps K, --warmup W, --no-cpu-baselin
            c3_split4      the keys in 4 chunks of 1024 (fa_fwd_ex per chunk) combined by fa_merge
            c3_window1024  causal with a sliding window of 1024 earlier keys
            prefill_cache  the last 1024 queries against all 4096 keys (bottom-right causal, q_offset 3072)
-         or c4 / c5 (the plain causal forward on those configurations).
+         or c4 / c5 (the plain causal forward on those configurations),
+         or c3_bwd: one step = one fa_bwd (dQ, dK, dV) on the C3 tensors with a seeded upstream gradient
+           (O and lse from one fa_fwd before timing).  FLOP per step = the five products of the backward
+           (recomputed S, dP, dV, dK, dQ) over the visible pairs, 10*D per pair = 2.5 x the forward's.
 """
 from __future__ import annotations
 
@@ -40,7 +43,7 @@ PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_fwd_c3.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "transformer_attention_fwd_amd", "csrc", f)
-                  for f in ("fa_kernels.hip", "fa_launch.h", "fa_api.cpp")]
+                  for f in ("fa_kernels.hip", "fa_device.h", "fa_launch.h")]
 VARIANTS = {
     "c3": dict(desc="causal", window=-1, chunks=1, nq=None),
     "c3_split4": dict(desc="causal, keys in 4 chunks + lse merge", window=-1, chunks=4, nq=None),
@@ -90,6 +93,8 @@ def main():
     import transformer_attention_fwd_amd as fa
     from transformer_attention_fwd_amd import inputs
 
+    if args.workload == "c3_bwd":
+        return bench_bwd(args)
     if args.workload in VARIANTS:
         var = VARIANTS[args.workload]
         w = inputs.WORKLOADS["c3"]
@@ -267,6 +272,117 @@ def main():
         "parity_sample": parity,
     }
     line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+def bench_bwd(args):
+    """One step = fa_bwd over the C3 batch; see the module notes."""
+    import numpy as np
+    import torch
+
+    import transformer_attention_fwd_amd as fa
+    from transformer_attention_fwd_amd import inputs
+
+    w = inputs.WORKLOADS["c3"]
+    B, H, N, D = w.B, w.H, w.N, w.D
+    log("bench: generating c3 inputs and dO %s" % ((B, H, N, D),))
+    qh, kh, vh = inputs.make_workload(w)
+    doh = inputs.make_grad(B, H, N, D, layout=w.layout, dtype="bf16", seed=w.seed)
+    to_dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda")
+    q, k, v, do = to_dev(qh), to_dev(kh), to_dev(vh), to_dev(doh)
+    o, lse = fa.attention(q, k, v, layout=w.layout, causal=True, scale=w.scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    layout = fa.LAYOUT_BHSD
+
+    def step():
+        st = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, D, layout, True,
+                       w.scale, fa.DTYPE_BF16, stream.cuda_stream)
+        if st != fa.FA_OK:
+            raise RuntimeError("fa_bwd failed: %s %s" % (fa.status_str(st), fa.last_error()))
+
+    log("bench: warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    call_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
+    ms_per_step = ev[0][0].elapsed_time(ev[-1][1]) / args.steps
+    pairs = float(B * H * visible_keys(N, N, 0, -1).sum())
+    flops = 10.0 * D * pairs
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    mean_ms = float(np.mean(call_ms))
+    achieved = flops / (mean_ms * 1e-3) / 1e12
+    log("bench: %d steps, %.4f ms/step (wall %.4f), fa_bwd median %.4f ms best %.4f ms, %.1f TFLOP/s"
+        % (args.steps, ms_per_step, (t1 - t0) * 1e3 / args.steps, float(np.median(call_ms)), min(call_ms), value))
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "fa_bwd_dq<128,bf16,causal> + fa_bwd_dkdv<128,bf16,causal> (one fa_bwd call)",
+                "mean_launch_ms": round(mean_ms, 5), "launches_per_step": 2}
+
+    cpu_baseline = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        cores = min(16, os.cpu_count() or 1)
+        rng = np.random.default_rng([4242, 3, 9])
+        order = [divmod(int(x), H) for x in rng.permutation(B * H)]
+        heads, t_cpu, got, ref = [], 0.0, [], []
+        while len(heads) < len(order) and (t_cpu < 10.0 or not heads):
+            hd = order[len(heads)]
+            t_a = time.perf_counter()
+            r = oracle.attention_bwd(qh, kh, vh, doh, dtype="bf16", layout=w.layout, causal=True, scale=w.scale,
+                                     heads=[hd], nthreads=cores)
+            t_cpu += time.perf_counter() - t_a
+            heads.append(hd)
+            ref.append([x[0] for x in r])
+            got.append([t[hd[0], hd[1]].double().cpu().numpy() for t in (dq, dk, dv)])
+        sample_flops = flops / (B * H) * len(heads)
+        cpu_tflops = sample_flops / t_cpu / 1e12
+        cpu_baseline = {"value": round(cpu_tflops, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                        "sample": "%d whole heads of the same workload (dQ, dK, dV; %.3e FLOP, %.1f s); full-step "
+                                  "time at this rate %.0f s" % (len(heads), sample_flops, t_cpu,
+                                                                 flops / (cpu_tflops * 1e12))}
+        parity = {"heads": [list(h) for h in heads]}
+        for n, name in enumerate(("dQ", "dK", "dV")):
+            err = max(float(np.abs(g[n] - r_[n]).max()) for g, r_ in zip(got, ref))
+            mag = max(float(np.abs(r_[n]).max()) for r_ in ref)
+            parity["max_abs_err_" + name] = err
+            parity["max_abs_ref_" + name] = mag
+        log("bench: oracle %d heads in %.2f s on %d threads; parity %s" % (len(heads), t_cpu, cores, parity))
+
+    line = {
+        "metric": "attention bwd TFLOP/s (dQ, dK, dV), causal B=8 H=32 N=4096 D=128",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "causal attention backward bf16 B=%d H=%d N=%d D=%d %s" % (B, H, N, D, w.layout),
+                   "B": B, "H": H, "N": N, "D": D, "layout": w.layout, "causal": True, "scale": w.scale,
+                   "flop_per_step": flops},
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu_baseline,
+        "parity_sample": parity,
+    }
     print(json.dumps(line), flush=True)
 
 

@@ -14,9 +14,10 @@
 //   fa_bwd_dq   one workgroup per (b, h, 128-query tile); walks the K/V tiles (keys up to the tile's
 //               last query when causal).  Computes D for its rows (stored to the caller's workspace),
 //               then per K/V tile S^T = K Q^T, dP^T = V dO^T, dS^T, and dQ^T += K^T dS^T.
-//   fa_bwd_dkdv one workgroup per (b, h, 128-key tile); K and V stay in registers; walks the Q/dO
-//               tiles (queries from the tile's first key on when causal).  Per 32-query step S = Q K^T,
-//               dP = dO V^T, P, dS, then dV^T += dO^T P and dK^T += Q^T dS.
+//   fa_bwd_dkdv one workgroup per (b, h, 128-key tile): 8 waves of 16 keys, two waves per SIMD; K and V
+//               stay in registers; walks the 64-query Q/dO tiles (from the tile's first key on when
+//               causal) with their rows' lse and D staged in LDS next to them.  Per 32-query step
+//               S = Q K^T, dP = dO V^T, P, dS, then dV^T += dO^T P and dK^T += Q^T dS.
 //
 // gfx950 mapping (both kernels): v_mfma_f32_16x16x32_{bf16,f16}; the streamed operand arrives by
 // buffer_load ... lds into a 2-stage LDS ring.  A tensor read both as rows (ds_read_b128, 16 consecutive
@@ -38,6 +39,9 @@ namespace {
 
 constexpr float kLog2e = 1.44269504088896341f;
 constexpr float kPosInf = __builtin_inff();
+// dK/dV workgroup: waves, keys per wave (their product is 128, the tile of the launch grid), and the
+// workgroups per CU the register budget is sized for
+constexpr int kDkdvWaves = 8, kDkdvKeys = 16, kDkdvMinBlocks = 1;
 
 template <int D>
 struct BwdTile {
@@ -46,13 +50,13 @@ struct BwdTile {
   static constexpr int CHUNKS = D / 8;    // 16-byte chunks per row
   static constexpr int DC = D / 32;       // 32-wide d chunks: k dimension of the S and dP products
   static constexpr int DT = D / 16;       // 16-wide d tiles: rows of dQ^T, dK^T, dV^T
-  // Chunk swizzle for tiles read both ways.  Row reads: the 16 rows r..r+15 at one logical chunk land on
-  // 16 (D = 128) or, per row parity, 8 (D = 64) different physical chunks.  Transposing reads: rows
-  // 4e..4e+3 at logical chunks 2t, 2t+1 land on 8 different physical chunks (per row parity for D = 64).
-  // Depends on the row only through its low 4 bits, so a 16-row step keeps a lane's offset.
-  __device__ static __forceinline__ int swz(int row) {
-    return D == 128 ? (((row & 7) << 1) | ((row >> 3) & 1)) : ((((row >> 1) & 3) << 1) | ((row >> 3) & 1));
-  }
+  // Chunk swizzle for tiles read both ways.  LDS serves these reads 128 bytes (8 chunks) at a time, so
+  // the 8 chunks one service touches must differ modulo 8.  Row reads (8 lanes: rows 8m..8m+7 at one
+  // logical chunk): the low 3 bits of the swizzle take 8 different values over 8 aligned rows.
+  // Transposing reads (16 lanes: rows 4e..4e+3 at logical chunks 2t, 2t+1): bits 1-2 take 4 different
+  // values over 4 aligned rows, and the chunk's own bit 0 separates 2t from 2t+1.  Depends on the row only
+  // through its low 3 bits, so 8-, 16- and 32-row steps keep a lane's offset.
+  __device__ static __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 };
 
 // 8 consecutive elements of a row held in LDS (row read): base + lane offset + row step.
@@ -211,21 +215,28 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
             dp[qg] = E::mfma(vf, df[qg][c], dp[qg]);
           }
         }
+        // lane holds keys key0 + 16*kt + 4*g + r for query q0 + 16*qg + li
+        float a[QG][4];
+#pragma unroll
+        for (int qg = 0; qg < QG; ++qg)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) a[qg][r] = __builtin_fmaf(s[qg][r], cexp, -lse2[qg]);
+        if (need_mask) {
+          keep_branch();
+#pragma unroll
+          for (int qg = 0; qg < QG; ++qg) {
+            const int qi = q0 + 16 * qg + li;
+            const int hi = (CAUSAL ? min(N - 1, qi) : N - 1) - key0 - 4 * g;  // slots 16*kt + r above: hidden
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (16 * kt + r > hi) a[qg][r] = kNegInf;
+          }
+        }
 #pragma unroll
         for (int qg = 0; qg < QG; ++qg) {
-          // lane holds keys key0 + 16*kt + 4*g + r for query q0 + 16*qg + li
-          int hi = BN;  // slots 16*kt + r above hi are hidden
-          if (need_mask) {
-            const int qi = q0 + 16 * qg + li;
-            hi = (CAUSAL ? min(N - 1, qi) : N - 1) - key0 - 4 * g;
-          }
           float ds[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float a = __builtin_fmaf(s[qg][r], cexp, -lse2[qg]);
-            if (16 * kt + r > hi) a = kNegInf;
-            ds[r] = __builtin_amdgcn_exp2f(a) * (dp[qg][r] - dlt[qg]);
-          }
+          for (int r = 0; r < 4; ++r) ds[r] = __builtin_amdgcn_exp2f(a[qg][r]) * (dp[qg][r] - dlt[qg]);
           const int kc = kt >> 1, half = kt & 1;
           dsf[qg][kc][2 * half + 0] = E::pack2(ds[0], ds[1]);
           dsf[qg][kc][2 * half + 1] = E::pack2(ds[2], ds[3]);
@@ -275,12 +286,13 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
 // ------------------------------------------------------------------------------------------------
 // dK, dV : one workgroup per (b, h, 128-key tile)
 // ------------------------------------------------------------------------------------------------
-template <int D, bool IS_BF16, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void fa_bwd_dkdv(BwdParams p) {
+template <int D, bool IS_BF16, bool CAUSAL, int NW, int KW, int MINB>
+__global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
   typedef BwdTile<D> T;
   typedef Elem<IS_BF16> E;
   typedef typename E::vec8 vec8;
-  constexpr int NW = T::NW, KW = 32, BK = NW * KW;  // keys per wave, per workgroup
+  constexpr int BK = NW * KW;                       // keys per workgroup (NW waves of KW keys)
+  static_assert(BK == 128, "the launch grid has one workgroup per 128 keys");
   constexpr int BQ = 64, QS = 32;                   // queries per LDS tile, per step
   constexpr int KG = KW / 16, QGS = QS / 16;
   constexpr int TILE_BYTES = BQ * T::ROW_BYTES;
@@ -289,6 +301,10 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t qs1[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t os0[TILE_BYTES];  // dO
   __shared__ __attribute__((aligned(1024))) uint8_t os1[TILE_BYTES];
+  // per-row values of a Q tile: lse * log2(e) in [0, BQ), D in [BQ, 2 BQ); +inf / 0 past the end
+  __shared__ __attribute__((aligned(16))) float rv0[2 * BQ];
+  __shared__ __attribute__((aligned(16))) float rv1[2 * BQ];
+  static_assert(BQ == 64, "one lane of one wave loads each row value");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -344,6 +360,23 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv(BwdParams p) {
   const float cexp = p.c;
   const float* lse_h = p.lse + (int64_t)bh * N;
   const float* dlt_h = p.delta + (int64_t)bh * N;
+  // row values of tile jt for this lane's row (wave 0 only)
+  auto load_rows = [&](int jt, float& l2v, float& dv) __attribute__((always_inline)) {
+    const int qi = (qt_begin + jt) * BQ + lane;
+    if (qi < N) {
+      l2v = lse_h[qi] * kLog2e;
+      dv = dlt_h[qi];
+    } else {
+      l2v = kPosInf;
+      dv = 0.f;
+    }
+  };
+  if (wave == 0) {
+    float a, d;
+    load_rows(0, a, d);
+    rv0[lane] = a;
+    rv0[BQ + lane] = d;
+  }
   f32x4_t dka[KG][T::DT], dva[KG][T::DT];
 #pragma unroll
   for (int kg = 0; kg < KG; ++kg)
@@ -355,28 +388,18 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv(BwdParams p) {
   int rb[T::DC], tb[T::DT];
   lane_offsets<D>(li, g, rb, tb);
 
-  auto step = [&](int j, const uint8_t* qs, const uint8_t* os, uint8_t* qn, uint8_t* on, auto last_c)
-      __attribute__((always_inline)) {
+  auto step = [&](int j, const uint8_t* qs, const uint8_t* os, const float* rv, uint8_t* qn, uint8_t* on, float* rvn,
+                  auto last_c) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     lds_barrier();
-    // log2-domain lse and D of the lane's rows of this tile: query tile0 + QS*hh + 16*qq + 4*g + r (past the
-    // end: no weight).  Loaded before the next tile's DMA is issued, so that waiting for them (the
-    // memory counter retires in order) does not also wait for that DMA.
+    // the next tile's row values are loaded before its DMA is issued (the memory counter retires in
+    // order) and stored to LDS after this tile's work, for the next barrier to publish
+    float nl = 0.f, nd = 0.f;
+    if constexpr (!decltype(last_c)::value) {
+      if (wave == 0) load_rows(j + 1, nl, nd);
+      issue_tile(j + 1, qn, on);
+    }
     const int tile0 = (qt_begin + j) * BQ;
-    float l2[BQ / QS][QGS][4], dl[BQ / QS][QGS][4];
-#pragma unroll
-    for (int hh = 0; hh < BQ / QS; ++hh)
-#pragma unroll
-      for (int qq = 0; qq < QGS; ++qq)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int qi = tile0 + QS * hh + 16 * qq + 4 * g + r;
-          const bool ok = qi < N;
-          const int qc = ok ? qi : N - 1;
-          l2[hh][qq][r] = ok ? lse_h[qc] * kLog2e : kPosInf;
-          dl[hh][qq][r] = ok ? dlt_h[qc] : 0.f;
-        }
-    if constexpr (!decltype(last_c)::value) issue_tile(j + 1, qn, on);
 #pragma unroll
     for (int hh = 0; hh < BQ / QS; ++hh) {
       const int qh0 = tile0 + QS * hh;  // first query of this step
@@ -402,18 +425,31 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv(BwdParams p) {
               dp[kg] = E::mfma(oa, vf[kg][c], dp[kg]);
             }
           }
+          // lane holds queries qh0 + 16*qq + 4*g + r for key kw0 + 16*kg + li
+          const f32x4_t l2 = *(const f32x4_t*)(rv + QS * hh + 16 * qq + 4 * g);
+          const f32x4_t dl = *(const f32x4_t*)(rv + BQ + QS * hh + 16 * qq + 4 * g);
+          float a[KG][4];
+#pragma unroll
+          for (int kg = 0; kg < KG; ++kg)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a[kg][r] = __builtin_fmaf(s[kg][r], cexp, -l2[r]);
+          if (need_mask) {
+            keep_branch();
+#pragma unroll
+            for (int kg = 0; kg < KG; ++kg) {
+              const int lo = kw0 + 16 * kg + li - (qh0 + 16 * qq + 4 * g);  // rows r < lo: query before key
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (r < lo) a[kg][r] = kNegInf;
+            }
+          }
 #pragma unroll
           for (int kg = 0; kg < KG; ++kg) {
-            // lane holds queries qh0 + 16*qq + 4*g + r for key kw0 + 16*kg + li
-            int lo = 0;  // rows r < lo are hidden (query before key)
-            if (need_mask) lo = kw0 + 16 * kg + li - (qh0 + 16 * qq + 4 * g);
             float pr[4], ds[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              float a = __builtin_fmaf(s[kg][r], cexp, -l2[hh][qq][r]);
-              if (r < lo) a = kNegInf;
-              pr[r] = __builtin_amdgcn_exp2f(a);
-              ds[r] = pr[r] * (dp[kg][r] - dl[hh][qq][r]);
+              pr[r] = __builtin_amdgcn_exp2f(a[kg][r]);
+              ds[r] = pr[r] * (dp[kg][r] - dl[r]);
             }
             pp[kg][2 * qq + 0] = E::pack2(pr[0], pr[1]);
             pp[kg][2 * qq + 1] = E::pack2(pr[2], pr[3]);
@@ -434,20 +470,26 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv(BwdParams p) {
         }
       }
     }
+    if constexpr (!decltype(last_c)::value) {
+      if (wave == 0) {
+        rvn[lane] = nl;
+        rvn[BQ + lane] = nd;
+      }
+    }
   };
 
   const std::integral_constant<bool, false> more;
   const std::integral_constant<bool, true> last;
   int j = 0;
   for (; j + 2 < n_qt; j += 2) {
-    step(j, qs0, os0, qs1, os1, more);
-    step(j + 1, qs1, os1, qs0, os0, more);
+    step(j, qs0, os0, rv0, qs1, os1, rv1, more);
+    step(j + 1, qs1, os1, rv1, qs0, os0, rv0, more);
   }
   if (j + 2 == n_qt) {
-    step(j, qs0, os0, qs1, os1, more);
-    step(j + 1, qs1, os1, qs0, os0, last);
+    step(j, qs0, os0, rv0, qs1, os1, rv1, more);
+    step(j + 1, qs1, os1, rv1, qs0, os0, rv0, last);
   } else {
-    step(j, qs0, os0, qs1, os1, last);
+    step(j, qs0, os0, rv0, qs1, os1, rv1, last);
   }
 
   // dK = scale * accumulated (dS^T Q), dV: lane holds d = 16*dt + 4*g + r of key kw0 + 16*kg + li
@@ -475,7 +517,8 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
   hipLaunchKernelGGL((fa_bwd_dq<D, IS_BF16, CAUSAL>), dim3(p.n_units), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa_bwd_dkdv<D, IS_BF16, CAUSAL>), dim3(p.n_units), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((fa_bwd_dkdv<D, IS_BF16, CAUSAL, kDkdvWaves, kDkdvKeys, kDkdvMinBlocks>), dim3(p.n_units),
+                     dim3(64 * kDkdvWaves), 0, stream, p);
   return hipGetLastError();
 }
 
