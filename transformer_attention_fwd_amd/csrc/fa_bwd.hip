@@ -50,13 +50,12 @@ struct BwdTile {
   static constexpr int CHUNKS = D / 8;    // 16-byte chunks per row
   static constexpr int DC = D / 32;       // 32-wide d chunks: k dimension of the S and dP products
   static constexpr int DT = D / 16;       // 16-wide d tiles: rows of dQ^T, dK^T, dV^T
-  // Chunk swizzle for tiles read both ways.  LDS serves these reads 128 bytes (8 chunks) at a time, so
-  // the 8 chunks one service touches must differ modulo 8.  Row reads (8 lanes: rows 8m..8m+7 at one
-  // logical chunk): the low 3 bits of the swizzle take 8 different values over 8 aligned rows.
-  // Transposing reads (16 lanes: rows 4e..4e+3 at logical chunks 2t, 2t+1): bits 1-2 take 4 different
-  // values over 4 aligned rows, and the chunk's own bit 0 separates 2t from 2t+1.  Depends on the row only
-  // through its low 3 bits, so 8-, 16- and 32-row steps keep a lane's offset.
-  __device__ static __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+  // Chunk swizzle for tiles read both ways: row reads (ds_read_b128, lane group g reading rows r..r+15 at
+  // one logical chunk) and transposing reads (ds_read_b64_tr_b16, rows 4e..4e+3 at logical chunks 2t,
+  // 2t+1).  Chosen by measurement on gfx950 (SQ_LDS_BANK_CONFLICT of both access patterns over a 64-row
+  // tile, for several candidates): these two are the simplest that are conflict-free for both patterns.
+  // They depend on the row only through its low 3 bits, so 8-, 16- and 32-row steps keep a lane's offset.
+  __device__ static __forceinline__ int swz(int row) { return D == 128 ? (row & 7) << 1 : row & 7; }
 };
 
 // 8 consecutive elements of a row held in LDS (row read): base + lane offset + row step.
