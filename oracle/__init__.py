@@ -233,3 +233,41 @@ def attention_bwd(q, k, v, dout, *, dtype: str, layout: str, causal: bool, scale
             g = np.ascontiguousarray(g.transpose(0, 2, 1, 3))
         res.append(g)
     return tuple(res)
+
+
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, dtype: str, causal: bool, scale: float,
+                     nthreads: int = 1):
+    """O and lse (fp64) of a packed batch of sequences of different lengths.
+
+    q: [total_q, H, D] and k, v: [total_k, H, D] stored elements (sequences one after another, each
+    [len, H, D] as in the BSND layout); cu_seqlens_q / cu_seqlens_k: B + 1 non-decreasing offsets
+    starting at 0.  Sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows
+    cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 and attends only to its own keys.  With causal, the two ends
+    are aligned: query i of a sequence with Nq queries and Nk keys sits at position Nk - Nq + i and sees
+    keys 0 .. Nk - Nq + i (the generalised rule of ``attention_rows_ex``).  A query with no visible key
+    gets O = 0 and lse = -inf.  Returns (O [total_q, H, D], lse [H, total_q]).
+    """
+    cu_q = [int(x) for x in cu_seqlens_q]
+    cu_k = [int(x) for x in cu_seqlens_k]
+    if len(cu_q) != len(cu_k) or len(cu_q) < 2 or cu_q[0] != 0 or cu_k[0] != 0:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must hold B + 1 offsets starting at 0")
+    if any(b < a for a, b in zip(cu_q, cu_q[1:])) or any(b < a for a, b in zip(cu_k, cu_k[1:])):
+        raise ValueError("cu_seqlens must be non-decreasing")
+    if q.ndim != 3 or k.ndim != 3 or v.shape != k.shape or q.shape[1:] != k.shape[1:]:
+        raise ValueError("q must be [total_q, H, D] and k, v [total_k, H, D]")
+    if cu_q[-1] != q.shape[0] or cu_k[-1] != k.shape[0]:
+        raise ValueError("the last offsets must equal total_q and total_k")
+    total_q, H, D = q.shape
+    o = np.zeros((total_q, H, D), dtype=np.float64)
+    lse = np.full((H, total_q), -np.inf, dtype=np.float64)
+    for b in range(len(cu_q) - 1):
+        qs, qe, ks, ke = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        nq, nk = qe - qs, ke - ks
+        if nq == 0 or nk == 0:
+            continue  # no rows, or rows that see no key (O = 0, lse = -inf as initialised)
+        ob, lb = attention_ex(q[qs:qe][None], k[ks:ke][None], v[ks:ke][None], dtype=dtype, layout="BSND",
+                              causal=causal, scale=scale, q_offset=(nk - nq) if causal else 0,
+                              nthreads=nthreads)
+        o[qs:qe] = ob[0]
+        lse[:, qs:qe] = lb[0]
+    return o, lse
