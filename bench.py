@@ -22,6 +22,8 @@ Options: --gpus N (only 1 is supported), --steps K, --warmup W, --no-cpu-baselin
            c3_window1024  causal with a sliding window of 1024 earlier keys
            prefill_cache  the last 1024 queries against all 4096 keys (bottom-right causal, q_offset 3072)
          or c4 / c5 (the plain causal forward on those configurations),
+         or varlen: one step = one fa_fwd_varlen over 8 packed causal sequences (H=32 D=128 bf16) whose
+           lengths are drawn uniformly from [512, 7680] (mean 4096: the C3 batch as a length mix),
          or c3_bwd: one step = one fa_bwd (dQ, dK, dV) on the C3 tensors with a seeded upstream gradient
            (O and lse from one fa_fwd before timing).  FLOP per step = the five products of the backward
            (recomputed S, dP, dV, dK, dQ) over the visible pairs, 10*D per pair = 2.5 x the forward's.
@@ -95,6 +97,8 @@ def main():
 
     if args.workload == "c3_bwd":
         return bench_bwd(args)
+    if args.workload == "varlen":
+        return bench_varlen(args)
     if args.workload in VARIANTS:
         var = VARIANTS[args.workload]
         w = inputs.WORKLOADS["c3"]
@@ -272,6 +276,119 @@ def main():
         "parity_sample": parity,
     }
     line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+def bench_varlen(args):
+    """One step = fa_fwd_varlen over a seeded causal length mix; see the module notes."""
+    import numpy as np
+    import torch
+
+    import transformer_attention_fwd_amd as fa
+    from transformer_attention_fwd_amd import inputs
+
+    B, H, D = 8, 32, 128
+    lens = inputs.varlen_lengths(B, 512, 7680, seed=3)
+    cu = inputs.cu_seqlens(lens)
+    total = int(cu[-1])
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    log("bench: varlen lengths %s (total %d)" % (list(lens), total))
+    qh, kh, vh = inputs.make_varlen(lens, lens, H, D, dtype="bf16", seed=3)
+    to_dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda")
+    q, k, v = to_dev(qh), to_dev(kh), to_dev(vh)
+    cu_d = torch.from_numpy(cu).to("cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((H, total), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    max_q = int(lens.max())
+
+    def step():
+        st = fa.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), cu_d.data_ptr(),
+                              cu_d.data_ptr(), B, H, total, total, max_q, D, True, scale, fa.DTYPE_BF16,
+                              stream.cuda_stream)
+        if st != fa.FA_OK:
+            raise RuntimeError("fa_fwd_varlen failed: %s %s" % (fa.status_str(st), fa.last_error()))
+
+    log("bench: warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    call_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
+    ms_per_step = ev[0][0].elapsed_time(ev[-1][1]) / args.steps
+    pairs = float(H * sum(int(n) * (int(n) + 1) // 2 for n in lens))
+    flops = 4.0 * D * pairs
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    mean_ms = float(np.mean(call_ms))
+    achieved = flops / (mean_ms * 1e-3) / 1e12
+    log("bench: %d steps, %.4f ms/step (wall %.4f), median %.4f ms, %.1f TFLOP/s"
+        % (args.steps, ms_per_step, (t1 - t0) * 1e3 / args.steps, float(np.median(call_ms)), value))
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "fa_fwd_16<128,bf16,causal,varlen>", "mean_launch_ms": round(mean_ms, 5),
+                "launches_per_step": 1}
+    cpu_baseline = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        cores = min(16, os.cpu_count() or 1)
+        rng = np.random.default_rng([4242, 3, 12])
+        t_cpu, n_rows, sample_flops = 0.0, 0, 0.0
+        err_o, err_l = 0.0, 0.0
+        o_h = o.float().cpu().numpy().astype(np.float64)
+        l_h = lse.cpu().numpy().astype(np.float64)
+        for b in range(B):  # seeded rows of every sequence, all heads
+            nb = int(lens[b])
+            rows_i = np.unique(np.concatenate([rng.choice(nb, size=min(nb, 96), replace=False), [0, nb - 1]]))
+            rows = np.stack([np.zeros(len(rows_i) * H, dtype=np.int64), np.repeat(np.arange(H), len(rows_i)),
+                             np.tile(rows_i, H)], axis=1)
+            sl = slice(int(cu[b]), int(cu[b + 1]))
+            t_a = time.perf_counter()
+            ob, lb = oracle.attention_rows_ex(qh[sl][None], kh[sl][None], vh[sl][None], dtype="bf16", layout="BSND",
+                                              causal=True, scale=scale, rows=rows, nthreads=cores)
+            t_cpu += time.perf_counter() - t_a
+            n_rows += len(rows)
+            sample_flops += float(np.sum(4.0 * D * (rows[:, 2] + 1)))
+            got_o = o_h[int(cu[b]) + rows[:, 2], rows[:, 1]]
+            got_l = l_h[rows[:, 1], int(cu[b]) + rows[:, 2]]
+            err_o = max(err_o, float(np.abs(got_o - ob).max()))
+            err_l = max(err_l, float(np.abs(got_l - lb).max()))
+        cpu_tflops = sample_flops / t_cpu / 1e12
+        cpu_baseline = {"value": round(cpu_tflops, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                        "sample": "%d seeded query rows over every sequence and head (%.3e FLOP, %.1f s); full-step "
+                                  "time at this rate %.0f s" % (n_rows, sample_flops, t_cpu, flops / (cpu_tflops * 1e12))}
+        parity = {"rows": n_rows, "max_abs_dO": err_o, "max_abs_dlse": err_l}
+        log("bench: oracle %d rows in %.2f s; parity %s" % (n_rows, t_cpu, parity))
+    line = {
+        "metric": "attention fwd TFLOP/s, packed causal sequences of mixed length, H=32 D=128",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "packed causal attention forward bf16, 8 sequences of lengths %s, H=%d D=%d"
+                               % (list(map(int, lens)), H, D), "B": B, "H": H, "D": D, "total_tokens": total,
+                   "max_seqlen": max_q, "causal": True, "scale": scale, "flop_per_step": flops},
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu_baseline,
+        "parity_sample": parity,
+    }
     print(json.dumps(line), flush=True)
 
 

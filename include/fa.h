@@ -56,7 +56,7 @@ extern "C" {
 #define FA_ERR_NOT_DEVICE_MEMORY 9 /* a pointer is not device memory of the current device */
 #define FA_ERR_HIP 10              /* the HIP runtime reported an error; see fa_last_error() */
 #define FA_ERR_BAD_RANGE 11        /* fa_fwd_ex: key chunk outside [0, Nk], a window without causal, or
-                                      |q_offset| > 2^30 */
+                                      |q_offset| > 2^30; fa_fwd_varlen: max_seqlen_q > total_q */
 
 /* Limits: 1 <= N <= 2^30, B*H <= 2^31 - 1, every tensor's byte size must fit in int64, and one head's
  * span -- (N - 1) * (bytes between consecutive positions) + D * element size -- must be below 2^31
@@ -133,6 +133,32 @@ int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, 
  */
 int fa_merge(const void* o_parts, const float* lse_parts, int64_t n_parts, void* o, float* lse, int64_t B,
              int64_t H, int64_t N, int64_t D, int layout, int dtype, void* stream);
+
+/*
+ * fa_fwd_varlen -- the forward over a packed batch of sequences of different lengths, without padding
+ * (the padding to a multiple of 128 that page hwcomputing.csdn.net/6a0d4444... needs, in its section on
+ * sequence-length alignment, is not needed here).  Sequence b owns the query rows cu_seqlens_q[b] ..
+ * cu_seqlens_q[b+1]-1 of q and o and the key rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of k and v, and
+ * attends only to its own keys.  With causal the two ends are aligned: query i of a sequence with Nq
+ * queries and Nk keys sees its keys 0 .. Nk - Nq + i (a query that sees none gets O = 0, lse = -inf);
+ * with Nq = Nk that is the ordinary causal mask.
+ *
+ * q, o       : [total_q][H][D] of `dtype` (each sequence is a [len][H][D] block, the BSND layout without
+ *              the batch dimension).  k, v: [total_k][H][D].  q, k, v read only; o fully overwritten.
+ * lse        : [H][total_q] fp32, fully overwritten.
+ * cu_seqlens_q, cu_seqlens_k: device int32 arrays of B + 1 offsets; non-decreasing, starting at 0 and
+ *              ending at total_q / total_k.  Read only.  The library cannot check their contents without
+ *              synchronising; a sequence whose offsets fall outside [0, total] or decrease is skipped (its
+ *              rows are left unwritten), so no offset array can cause an access outside the tensors.
+ * max_seqlen_q: at least the longest query count (it sizes the launch grid); query rows of a sequence
+ *              beyond it are left unwritten.  1 <= max_seqlen_q <= total_q.
+ * dtype      : FA_DTYPE_FP16 or FA_DTYPE_BF16 (FA_DTYPE_FP32 returns FA_ERR_UNSUPPORTED).  D in {64, 128}.
+ * total_q, total_k >= 1.  No window.  Ownership, stream semantics and error conventions as fa_fwd
+ * (FA_ERR_BAD_RANGE for max_seqlen_q > total_q; cu arrays must be 4-byte aligned).
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens_q,
+                  const int32_t* cu_seqlens_k, int64_t B, int64_t H, int64_t total_q, int64_t total_k,
+                  int64_t max_seqlen_q, int64_t D, int causal, float scale, int dtype, void* stream);
 
 /*
  * fa_bwd -- gradients of the attention forward: for O = softmax(scale * Q K^T [+ causal]) V (the call

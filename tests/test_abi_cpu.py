@@ -18,7 +18,8 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     declared = _declared()
-    assert declared == ["fa_bwd", "fa_fwd", "fa_fwd_ex", "fa_last_error", "fa_merge", "fa_status_str", "fa_version"]
+    assert declared == ["fa_bwd", "fa_fwd", "fa_fwd_ex", "fa_fwd_varlen", "fa_last_error", "fa_merge", "fa_status_str",
+                        "fa_version"]
     out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], stdout=subprocess.PIPE,
                          text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.split() and l.split()[1] == "T"}
@@ -42,7 +43,7 @@ def test_header_constants_match_binding():
 
 
 def test_status_strings_and_version():
-    assert fa.version() == 300
+    assert fa.version() == 400
     for st in range(12):
         assert fa.status_str(st)
     assert fa.status_str(0) == "ok"
@@ -202,3 +203,33 @@ def test_fa_bwd_argument_checks(kw, status):
 def test_fa_bwd_good_arguments_reach_the_device_check():
     # every pure check passes; the fake pointers then fail the residency check (or HIP is absent)
     assert _call_b() in (fa.FA_ERR_NOT_DEVICE_MEMORY, fa.FA_ERR_HIP)
+
+
+# ---- fa_fwd_varlen: pure argument checks ----
+CQ, CK = 0x10000000000 + 10 * (SZ * 4), 0x10000000000 + 11 * (SZ * 4)
+GOOD_V = dict(q=Q, k=K, v=V, o=O, lse=L, cq=CQ, ck=CK, B=3, H=2, tq=300, tk=500, mq=128, D=128, causal=1,
+              scale=0.088, dtype=2, stream=0)
+
+
+def _call_v(**kw):
+    a = dict(GOOD_V)
+    a.update(kw)
+    return fa.fa_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"], a["B"], a["H"], a["tq"], a["tk"],
+                            a["mq"], a["D"], a["causal"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), fa.FA_ERR_NULL), (dict(cq=0), fa.FA_ERR_NULL), (dict(ck=0), fa.FA_ERR_NULL),
+    (dict(dtype=9), fa.FA_ERR_BAD_DTYPE), (dict(B=0), fa.FA_ERR_BAD_DIM), (dict(tq=0), fa.FA_ERR_BAD_DIM),
+    (dict(tk=0), fa.FA_ERR_BAD_DIM), (dict(mq=0), fa.FA_ERR_BAD_DIM), (dict(D=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=0), fa.FA_ERR_UNSUPPORTED), (dict(tq=(1 << 30) + 1, mq=1), fa.FA_ERR_UNSUPPORTED),
+    (dict(mq=301), fa.FA_ERR_BAD_RANGE), (dict(scale=float("nan")), fa.FA_ERR_BAD_SCALE),
+    (dict(v=V + 8), fa.FA_ERR_MISALIGNED), (dict(cq=CQ + 2), fa.FA_ERR_MISALIGNED),
+    (dict(o=Q + 64), fa.FA_ERR_ALIAS), (dict(lse=CK), fa.FA_ERR_ALIAS), (dict(lse=O + 16), fa.FA_ERR_ALIAS),
+])
+def test_fa_fwd_varlen_argument_checks(kw, status):
+    assert _call_v(**kw) == status
+
+
+def test_fa_fwd_varlen_good_arguments_reach_the_device_check():
+    assert _call_v() in (fa.FA_ERR_NOT_DEVICE_MEMORY, fa.FA_ERR_HIP)

@@ -18,6 +18,11 @@ There is no CPU or framework fallback: if ``libfa.so`` is missing the first call
         the same for fa_fwd_ex (q [B,H,Nq,D] / [B,Nq,H,D], k and v [B,H,Nk,D] / [B,Nk,H,D]).
     merge(o_parts, lse_parts, *, layout, out=None, lse=None) -> (o, lse)
         fa_merge on torch tensors stacked along a leading parts dimension.
+    fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, total_q, total_k, max_seqlen_q, D, causal,
+                  scale, dtype, stream) -> status
+    attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, *, causal=False, scale=None, out=None,
+                     lse=None) -> (o [total_q, H, D], lse [H, total_q])
+        packed sequences of different lengths (int32 offset tensors on the device).
     fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, D, layout, causal, scale, dtype, stream) -> status
         the backward C entry point, same conventions.
     attention_bwd(q, k, v, o, lse, dout, *, layout="BHSD", causal=False, scale=None, delta=None) -> (dq, dk, dv)
@@ -29,7 +34,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "fa_fwd_ex", "fa_merge", "fa_bwd", "attention", "attention_ex", "merge", "attention_bwd", "FaError", "library_path",
+__all__ = ["fa_fwd", "fa_fwd_ex", "fa_fwd_varlen", "fa_merge", "fa_bwd", "attention", "attention_ex",
+           "attention_varlen", "merge", "attention_bwd", "FaError", "library_path",
            "load", "status_str", "version",
            "LAYOUT_BHSD", "LAYOUT_BSND", "DTYPE_FP32", "DTYPE_FP16", "DTYPE_BF16"]
 
@@ -82,6 +88,9 @@ def load():
         lib.fa_merge.restype = ctypes.c_int
         lib.fa_merge.argtypes = ([ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p] +
                                  [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_int, ctypes.c_void_p])
+        lib.fa_fwd_varlen.restype = ctypes.c_int
+        lib.fa_fwd_varlen.argtypes = ([ctypes.c_void_p] * 7 + [ctypes.c_int64] * 6 + [ctypes.c_int, ctypes.c_float,
+                                      ctypes.c_int, ctypes.c_void_p])
         lib.fa_bwd.restype = ctypes.c_int
         lib.fa_bwd.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_int,
                                ctypes.c_float, ctypes.c_int, ctypes.c_void_p])
@@ -112,6 +121,14 @@ def fa_merge(o_parts, lse_parts, n_parts, o, lse, B, H, N, D, layout, dtype, str
     """The C merge entry point: pointers are ints (0 = NULL), returns the status code."""
     return load().fa_merge(o_parts or None, lse_parts or None, n_parts, o or None, lse or None, B, H, N, D,
                            layout, dtype, stream or None)
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, total_q, total_k, max_seqlen_q, D, causal,
+                  scale, dtype, stream) -> int:
+    """The packed variable-length C entry point: pointers are ints (0 = NULL), returns the status code."""
+    return load().fa_fwd_varlen(q or None, k or None, v or None, o or None, lse or None, cu_seqlens_q or None,
+                                cu_seqlens_k or None, B, H, total_q, total_k, max_seqlen_q, D, int(causal), scale,
+                                dtype, stream or None)
 
 
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, D, layout, causal, scale, dtype, stream) -> int:
@@ -287,3 +304,39 @@ def attention_bwd(q, k, v, o, lse, dout, *, layout: str = "BHSD", causal: bool =
                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, D, _LAYOUTS[layout],
                      causal, float(scale), _dtype_code(q), stream))
     return dq, dk, dv
+
+
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, *, causal: bool = False,
+                     scale: float | None = None, out=None, lse=None):
+    """fa_fwd_varlen for torch device tensors: q [total_q, H, D], k and v [total_k, H, D], int32 offsets."""
+    import torch
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or q.shape[1:] != k.shape[1:]:
+        raise ValueError("q must be [total_q, H, D] and k, v [total_k, H, D]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous")
+    for t in (cu_seqlens_q, cu_seqlens_k):
+        if t.dim() != 1 or t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError("cu_seqlens must be contiguous 1-D int32 tensors")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must hold B + 1 offsets")
+    total_q, H, D = q.shape
+    total_k = k.shape[0]
+    B = cu_seqlens_q.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (H, total_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of shape [H, total_q]")
+    stream = torch.cuda.current_stream(q.device).cuda_stream if q.is_cuda else 0
+    _raise_on(fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                            cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, total_q, total_k, int(max_seqlen_q),
+                            D, causal, float(scale), _dtype_code(q), stream))
+    return out, lse

@@ -63,14 +63,14 @@ FA_API const char* fa_status_str(int status) {
     case FA_ERR_ALIAS: return "o and lse must not overlap the inputs or each other";
     case FA_ERR_NOT_DEVICE_MEMORY: return "a pointer is not device memory of the current device";
     case FA_ERR_HIP: return "HIP runtime error";
-    case FA_ERR_BAD_RANGE: return "key chunk outside [0, Nk], window without causal, or q_offset out of range";
+    case FA_ERR_BAD_RANGE: return "key chunk outside [0, Nk], window without causal, q_offset out of range, or max_seqlen_q > total_q";
     default: return "unknown status";
   }
 }
 
 FA_API const char* fa_last_error(void) { return g_last_error; }
 
-FA_API int fa_version(void) { return 300; }  // 0.3.0
+FA_API int fa_version(void) { return 400; }  // 0.4.0
 
 FA_API int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                      int64_t Nq, int64_t Nk, int64_t D, int layout, int causal, int64_t window, int64_t q_offset,
@@ -168,6 +168,79 @@ FA_API int fa_fwd(const void* q, const void* k, const void* v, void* o, float* l
                     : (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) ? FA_ERR_BAD_DTYPE
                     : FA_ERR_BAD_DIM;
   return fa_fwd_ex(q, k, v, o, lse, B, H, N, N, D, layout, causal, -1, 0, 0, N, scale, dtype, stream);
+}
+
+FA_API int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens_q,
+                         const int32_t* cu_seqlens_k, int64_t B, int64_t H, int64_t total_q, int64_t total_k,
+                         int64_t max_seqlen_q, int64_t D, int causal, float scale, int dtype, void* stream) {
+  // ---- pure argument checks (no HIP calls) ----
+  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULL;
+  if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_BAD_DTYPE;
+  if (B < 1 || H < 1 || total_q < 1 || total_k < 1 || max_seqlen_q < 1 || D < 1) return FA_ERR_BAD_DIM;
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_DTYPE_FP32) return FA_ERR_UNSUPPORTED;
+  int64_t rows_q, rows_k, elems_q, elems_k, bytes_q, bytes_k, lse_bytes, bh, cu_bytes;
+  if (total_q > kMaxRows || total_k > kMaxRows || B > kMaxRows || !mul_ok(total_q, H, &rows_q) ||
+      !mul_ok(total_k, H, &rows_k) || !mul_ok(rows_q, D, &elems_q) || !mul_ok(rows_k, D, &elems_k) ||
+      !mul_ok(elems_q, 2, &bytes_q) || !mul_ok(elems_k, 2, &bytes_k) || !mul_ok(rows_q, 4, &lse_bytes) ||
+      !mul_ok(B, H, &bh) || bh > INT32_MAX || !mul_ok(B + 1, 4, &cu_bytes))
+    return FA_ERR_UNSUPPORTED;
+  if (max_seqlen_q > total_q) return FA_ERR_BAD_RANGE;
+  const int64_t qpw = fa::queries_per_workgroup(fa::kDtypeBf16);
+  if ((bh + 7) / 8 * 8 * ((max_seqlen_q + qpw - 1) / qpw) > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  // every sequence's key rows lie inside [0, total_k): its per-head byte range fits a buffer descriptor
+  if ((total_k - 1) * H * D * 2 + D * 2 > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  if (!isfinite(scale) || !isfinite(fabsf(scale) * 1.4426950408889634f)) return FA_ERR_BAD_SCALE;
+  if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15) ||
+      (((uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k) & 3))
+    return FA_ERR_MISALIGNED;
+  const void* ins[5] = {q, k, v, cu_seqlens_q, cu_seqlens_k};
+  const int64_t in_bytes[5] = {bytes_q, bytes_k, bytes_k, cu_bytes, cu_bytes};
+  for (int i = 0; i < 5; ++i)
+    if (overlaps(o, bytes_q, ins[i], in_bytes[i]) || overlaps(lse, lse_bytes, ins[i], in_bytes[i])) return FA_ERR_ALIAS;
+  if (overlaps(lse, lse_bytes, o, bytes_q)) return FA_ERR_ALIAS;
+
+  // ---- device residency ----
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) {
+    set_error("hipGetDevice", e);
+    return FA_ERR_HIP;
+  }
+  const void* ptrs[7] = {q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k};
+  for (const void* ptr : ptrs) {
+    const int st = check_device(ptr, device);
+    if (st != FA_OK) return st;
+  }
+
+  // ---- launch ----
+  fa::Params p;
+  memset(&p, 0, sizeof p);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = (int)B;
+  p.H = (int)H;
+  p.Nq = (int)max_seqlen_q;
+  p.window = -1;
+  p.stride_h_q = D;
+  p.stride_h_k = D;
+  p.stride_s = H * D;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.total_q = total_q;
+  p.total_k = total_k;
+  p.c = scale == 0.0f ? 1.17549435e-38f : fabsf(scale) * 1.4426950408889634f;
+  p.qsign = scale < 0.0f ? 0x80008000u : 0u;
+  e = fa::launch_varlen(p, dtype == FA_DTYPE_FP16 ? fa::kDtypeFp16 : fa::kDtypeBf16, (int)D, causal != 0,
+                        (hipStream_t)stream);
+  if (e != hipSuccess) {
+    set_error("kernel launch", e);
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
 }
 
 FA_API int fa_merge(const void* o_parts, const float* lse_parts, int64_t n_parts, void* o, float* lse, int64_t B,

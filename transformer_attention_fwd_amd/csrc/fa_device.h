@@ -49,6 +49,18 @@ __device__ __forceinline__ void unit_of(int bid, int n_units, int n_qtiles, bool
   qt = causal ? n_qtiles - 1 - r : r;
 }
 
+// Block index -> (b*H + h, q_tile) spreading heads over the XCDs: XCD x (blocks x, x+8, ...) takes heads
+// x, x+8, x+16, ... in turn, each head's tiles heaviest first when causal.  For work that differs from
+// head to head (sequences of different lengths) this gives every XCD an equal share of each sequence.
+// The grid covers ceil(BH/8)*8 heads; blocks that land on a padding head (bh >= BH) have no work.
+__device__ __forceinline__ void unit_of_spread(int bid, int n_qtiles, bool causal, int& bh, int& qt) {
+  constexpr int X = 8;
+  const int x = bid % X, u = bid / X;
+  const int m = u / n_qtiles, r = u - m * n_qtiles;
+  bh = x + X * m;
+  qt = causal ? n_qtiles - 1 - r : r;
+}
+
 __device__ __forceinline__ float wave_max_xor16_32(float x) {
   x = fmaxf(x, __shfl_xor(x, 16));
   x = fmaxf(x, __shfl_xor(x, 32));

@@ -79,7 +79,43 @@ struct Tile16 {
   __device__ static __forceinline__ int swz_v(int row) { return D == 128 ? ((row & 7) << 1) : (((row >> 1) & 3) << 1); }
 };
 
-template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW>
+// Where one workgroup's sequence lies: its query and key counts, the causal offset, the element offsets
+// of its (b, h) rows in Q/O and K/V, and the index of its first row in lse.  For packed variable-length
+// batches these come from the sequence's offsets; offsets outside [0, total] or decreasing leave the
+// sequence untouched (skip), so no offset array can send an access out of the tensors.
+struct SeqGeom {
+  int Nq, Nkv;
+  int64_t delta, window, q_base, kv_base, lse_base;
+  bool skip;
+};
+
+template <bool CAUSAL, bool VARLEN>
+__device__ __forceinline__ SeqGeom seq_geometry(const Params& p, int b, int h, int bh) {
+  SeqGeom sg;
+  if constexpr (VARLEN) {
+    const int qs = p.cu_q[b], qe = p.cu_q[b + 1], ks = p.cu_k[b], ke = p.cu_k[b + 1];
+    sg.skip = qs < 0 || qe < qs || qe > p.total_q || ks < 0 || ke < ks || ke > p.total_k;
+    sg.Nq = qe - qs;
+    sg.Nkv = ke - ks;
+    sg.delta = CAUSAL ? (int64_t)sg.Nkv - sg.Nq : 0;  // the two ends aligned
+    sg.window = -1;
+    sg.q_base = (int64_t)qs * p.stride_s + h * p.stride_h_q;
+    sg.kv_base = (int64_t)ks * p.stride_s + h * p.stride_h_k;
+    sg.lse_base = (int64_t)h * p.total_q + qs;
+  } else {
+    sg.skip = false;
+    sg.Nq = p.Nq;
+    sg.Nkv = p.Nkv;
+    sg.delta = p.delta;
+    sg.window = p.window;
+    sg.q_base = b * p.stride_b_q + h * p.stride_h_q;
+    sg.kv_base = b * p.stride_b_k + h * p.stride_h_k + p.kv_start * p.stride_s;
+    sg.lse_base = (int64_t)bh * p.Nq;
+  }
+  return sg;
+}
+
+template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW, bool VARLEN>
 __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
   typedef Tile16<D> T;
   typedef Elem<IS_BF16> E;
@@ -97,17 +133,23 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
   const int li = lane & 15;   // index within the group
 
   int bh, qt;
-  unit_of(blockIdx.x, p.n_units, p.n_qtiles, CAUSAL, bh, qt);
+  if constexpr (VARLEN) {
+    unit_of_spread(blockIdx.x, p.n_qtiles, CAUSAL, bh, qt);
+    if (bh >= p.B * p.H) return;  // padding head of the grid
+  } else {
+    unit_of(blockIdx.x, p.n_units, p.n_qtiles, CAUSAL, bh, qt);
+  }
   const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
-  const int Nq = p.Nq, Nkv = p.Nkv;
-  const int64_t delta = p.delta, window = p.window;
+  const SeqGeom sg = seq_geometry<CAUSAL, VARLEN>(p, b, h, bh);
   const int q_wg = qt * T::BM;
+  if (VARLEN && (sg.skip || q_wg >= sg.Nq)) return;  // a bad sequence, or a tile past its end
+  const int Nq = sg.Nq, Nkv = sg.Nkv;
+  const int64_t delta = sg.delta, window = sg.window;
   const int q0 = q_wg + wave * T::QW;
 
-  const uint16_t* __restrict__ qg_ptr = (const uint16_t*)p.q + b * p.stride_b_q + h * p.stride_h_q;
-  const int64_t kv_base = b * p.stride_b_k + h * p.stride_h_k + p.kv_start * p.stride_s;
-  const uint8_t* __restrict__ kg_ptr = (const uint8_t*)p.k + 2 * kv_base;
-  const uint8_t* __restrict__ vg_ptr = (const uint8_t*)p.v + 2 * kv_base;
+  const uint16_t* __restrict__ qg_ptr = (const uint16_t*)p.q + sg.q_base;
+  const uint8_t* __restrict__ kg_ptr = (const uint8_t*)p.k + 2 * sg.kv_base;
+  const uint8_t* __restrict__ vg_ptr = (const uint8_t*)p.v + 2 * sg.kv_base;
 
   // ---- the chunk keys this workgroup visits: from the lowest key inside the window of its first query
   // (0 without a window) to the last key visible to its last query; tiles of BN keys from k_begin ----
@@ -115,14 +157,14 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
   const int k_last = CAUSAL ? (int)max((int64_t)-1, min((int64_t)Nkv - 1, q_wg + T::BM - 1 + delta)) : Nkv - 1;
   const int n_kt = k_last >= k_begin ? (k_last - k_begin) / T::BN + 1 : 0;
   if (n_kt == 0) {  // no query of this workgroup sees any key of the chunk: O = 0, lse = -inf
-    uint16_t* og = (uint16_t*)p.o + b * p.stride_b_q + h * p.stride_h_q;
+    uint16_t* og = (uint16_t*)p.o + sg.q_base;
 #pragma unroll
     for (int qg = 0; qg < T::QG; ++qg) {
       const int qi = q0 + 16 * qg + li;
       if (qi < Nq) {
 #pragma unroll
         for (int dt = 0; dt < T::DT; ++dt) *(u32x2_t*)(og + qi * p.stride_s + 16 * dt + 4 * g) = u32x2_t{0u, 0u};
-        if (g == 0) p.lse[(int64_t)bh * Nq + qi] = kNegInf;
+        if (g == 0) p.lse[sg.lse_base + qi] = kNegInf;
       }
     }
     return;
@@ -358,7 +400,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
 
   // ---- epilogue: O = acc / u, lse = (m + log2 l) ln 2; a row without any visible key has u = l = 0 and
   // gets O = 0, lse = -inf ----
-  uint16_t* og_ptr = (uint16_t*)p.o + b * p.stride_b_q + h * p.stride_h_q;
+  uint16_t* og_ptr = (uint16_t*)p.o + sg.q_base;
 #pragma unroll
   for (int qg = 0; qg < T::QG; ++qg) {
     const float l = wave_sum_xor16_32(l_part[qg]);
@@ -371,7 +413,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
         u32x2_t w = {E::pack2(o[0], o[1]), E::pack2(o[2], o[3])};
         *(u32x2_t*)(og_ptr + qi * p.stride_s + 16 * dt + 4 * g) = w;
       }
-      if (g == 0) p.lse[(int64_t)bh * Nq + qi] = (m_ref[qg] + __builtin_log2f(l)) * kLn2;
+      if (g == 0) p.lse[sg.lse_base + qi] = (m_ref[qg] + __builtin_log2f(l)) * kLn2;
     }
   }
 }
@@ -549,12 +591,13 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_32(Params p) {
 // ------------------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------------------
-template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW>
+template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW, bool VARLEN = false>
 static hipError_t launch16(Params p, hipStream_t stream) {
   typedef Tile16<D> T;
   p.n_qtiles = (p.Nq + T::BM - 1) / T::BM;
-  p.n_units = p.n_qtiles * p.B * p.H;
-  hipLaunchKernelGGL((fa_fwd_16<D, IS_BF16, CAUSAL, WINDOW>), dim3(p.n_units), dim3(256), 0, stream, p);
+  // packed sequences: heads spread over the XCDs, the grid padded to a multiple of 8 heads
+  p.n_units = p.n_qtiles * (VARLEN ? (p.B * p.H + 7) / 8 * 8 : p.B * p.H);
+  hipLaunchKernelGGL((fa_fwd_16<D, IS_BF16, CAUSAL, WINDOW, VARLEN>), dim3(p.n_units), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -584,6 +627,17 @@ hipError_t launch(const Params& p, int dtype, int d, bool causal, hipStream_t st
   if (dtype == kDtypeBf16) return d == 128 ? launch16_d<128, true>(p, causal, stream) : launch16_d<64, true>(p, causal, stream);
   if (dtype == kDtypeFp16) return d == 128 ? launch16_d<128, false>(p, causal, stream) : launch16_d<64, false>(p, causal, stream);
   return d == 128 ? launch32_d<128>(p, causal, stream) : launch32_d<64>(p, causal, stream);
+}
+
+template <int D, bool IS_BF16>
+static hipError_t launch_varlen_d(const Params& p, bool causal, hipStream_t stream) {
+  return causal ? launch16<D, IS_BF16, true, false, true>(p, stream) : launch16<D, IS_BF16, false, false, true>(p, stream);
+}
+
+hipError_t launch_varlen(const Params& p, int dtype, int d, bool causal, hipStream_t stream) {
+  if (dtype == kDtypeBf16)
+    return d == 128 ? launch_varlen_d<128, true>(p, causal, stream) : launch_varlen_d<64, true>(p, causal, stream);
+  return d == 128 ? launch_varlen_d<128, false>(p, causal, stream) : launch_varlen_d<64, false>(p, causal, stream);
 }
 
 int queries_per_workgroup(int dtype) { return dtype == kDtypeFp32 ? Tile32<64>::BM : Tile16<64>::BM; }

@@ -34,6 +34,12 @@ struct Params {
   int n_units;      // filled by the launcher
   float c;          // |scale| * log2(e), > 0 (a zero scale is passed as FLT_MIN by the entry point)
   uint32_t qsign;   // XOR mask applied to Q's stored bits: flips the sign when scale < 0
+  // Packed variable-length batches only (null otherwise): sequence b owns query rows cu_q[b] ..
+  // cu_q[b+1]-1 of the [total_q][H][D] tensors and key rows cu_k[b] .. cu_k[b+1]-1 of [total_k][H][D];
+  // Nq then holds the longest query count (grid sizing) and lse is [H][total_q].
+  const int* cu_q;
+  const int* cu_k;
+  int64_t total_q, total_k;
 };
 
 // Backward kernel arguments (Nq = Nk = N; all ten tensors share the layout's strides, in elements).
@@ -58,6 +64,9 @@ struct BwdParams {
 
 // Enqueue the attention kernel for (dtype, d, causal, window >= 0) on `stream`.
 hipError_t launch(const Params& p, int dtype, int d, bool causal, hipStream_t stream);
+
+// Enqueue the packed variable-length forward (16-bit dtypes; Params::cu_q / cu_k set) on `stream`.
+hipError_t launch_varlen(const Params& p, int dtype, int d, bool causal, hipStream_t stream);
 
 // Enqueue the combination of n_parts partial results (see fa_merge in fa.h).
 hipError_t launch_merge(const void* o_parts, const float* lse_parts, int n_parts, void* o, float* lse, int64_t rows,

@@ -21,6 +21,10 @@ in that order, in logical [B, H, N, D] order, multiplied by the config's factor,
 config's dtype (nearest-even), then stored in the config's layout.  The upstream gradient dO of the
 backward pass comes from its own stream, ``default_rng([42, c, 7])``, as one more standard normal draw
 of the same shape, rounded and stored the same way.
+
+Packed variable-length batches (``make_varlen``): Q [total_q, H, D] then K, V [total_k, H, D] from
+``default_rng([42, seed, 11])``, rounded the same way; ``varlen_lengths`` draws the sequence lengths
+uniformly from an inclusive range with ``default_rng([4243, seed])``.
 """
 from __future__ import annotations
 
@@ -135,6 +139,27 @@ def make_grad(B: int, H: int, N: int, D: int, *, layout: str, dtype: str, seed):
     """Stored upstream gradient dO (element bits of ``dtype``, packed in ``layout``) for ``[42, seed, 7]``."""
     rng = np.random.default_rng([42] + ([seed] if np.isscalar(seed) else list(seed)) + [7])
     return to_layout(cast_bits(rng.standard_normal((B, H, N, D), dtype=np.float32), dtype), layout)
+
+
+def varlen_lengths(B: int, lo: int, hi: int, seed) -> np.ndarray:
+    """B seeded sequence lengths, uniform in [lo, hi]."""
+    rng = np.random.default_rng([4243] + ([seed] if np.isscalar(seed) else list(seed)))
+    return rng.integers(lo, hi + 1, size=B).astype(np.int64)
+
+
+def cu_seqlens(lengths) -> np.ndarray:
+    """int32 offsets [0, l0, l0 + l1, ...] of packed sequences."""
+    return np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))]).astype(np.int32)
+
+
+def make_varlen(lens_q, lens_k, H: int, D: int, *, dtype: str, seed):
+    """Stored packed Q [sum(lens_q), H, D] and K, V [sum(lens_k), H, D] for generator ``[42, seed, 11]``."""
+    rng = np.random.default_rng([42] + ([seed] if np.isscalar(seed) else list(seed)) + [11])
+    tq, tk = int(np.sum(lens_q)), int(np.sum(lens_k))
+    q = rng.standard_normal((tq, H, D), dtype=np.float32)
+    k = rng.standard_normal((tk, H, D), dtype=np.float32)
+    v = rng.standard_normal((tk, H, D), dtype=np.float32)
+    return tuple(np.ascontiguousarray(cast_bits(t, dtype)) for t in (q, k, v))
 
 
 def make_workload(w: Workload, dtype: str | None = None):
