@@ -133,6 +133,16 @@ def test_c5_bf16_causal_n65536_sampled():
 
 # ---- ragged sizes, both layouts, all dtypes ----------------------------------------------------------
 
+@pytest.mark.parametrize("N", [200, 256, 456, 384, 385])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_causal_tile_pairing_boundary(N, D, dtype):
+    # whole causal problems run heavy and light query tiles in pairs when the tile count is even and every
+    # tile visits an even number of 64-key tiles: N = 200, 256, 456 pair; 384 (3 tiles) and 385 (a last
+    # tile of one row) run one tile per workgroup
+    full_compare(2, 3, N, D, dtype, "BHSD", True, 1.0 / math.sqrt(D), 300 + N, "pairing N=%d D=%d %s" % (N, D, dtype))
+
+
 @pytest.mark.parametrize("N", [1, 7, 64, 100, 130, 257])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])

@@ -115,7 +115,7 @@ __device__ __forceinline__ SeqGeom seq_geometry(const Params& p, int b, int h, i
   return sg;
 }
 
-template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW, bool VARLEN>
+template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW, bool VARLEN, bool PAIR>
 __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
   typedef Tile16<D> T;
   typedef Elem<IS_BF16> E;
@@ -132,20 +132,28 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
   const int g = lane >> 4;    // lane group 0..3
   const int li = lane & 15;   // index within the group
 
-  int bh, qt;
+  int bh, qt, qt_b = -1;
   if constexpr (VARLEN) {
     unit_of_spread(blockIdx.x, p.n_qtiles, CAUSAL, bh, qt);
     if (bh >= p.B * p.H) return;  // padding head of the grid
+  } else if constexpr (PAIR) {
+    // pair r of a head: its heavy tile n-1-r, then its light tile r (one causal tile of each end, so
+    // every pair has the same work)
+    int r;
+    unit_of(blockIdx.x, p.n_units, p.n_qtiles, false, bh, r);
+    const int n_full = (p.Nq + T::BM - 1) / T::BM;
+    qt = n_full - 1 - r;
+    qt_b = r;  // the launcher pairs only an even number of tiles
   } else {
     unit_of(blockIdx.x, p.n_units, p.n_qtiles, CAUSAL, bh, qt);
   }
   const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
   const SeqGeom sg = seq_geometry<CAUSAL, VARLEN>(p, b, h, bh);
-  const int q_wg = qt * T::BM;
+  int q_wg = qt * T::BM;
   if (VARLEN && (sg.skip || q_wg >= sg.Nq)) return;  // a bad sequence, or a tile past its end
   const int Nq = sg.Nq, Nkv = sg.Nkv;
   const int64_t delta = sg.delta, window = sg.window;
-  const int q0 = q_wg + wave * T::QW;
+  int q0 = q_wg + wave * T::QW;
 
   const uint16_t* __restrict__ qg_ptr = (const uint16_t*)p.q + sg.q_base;
   const uint8_t* __restrict__ kg_ptr = (const uint8_t*)p.k + 2 * sg.kv_base;
@@ -155,7 +163,10 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
   // (0 without a window) to the last key visible to its last query; tiles of BN keys from k_begin ----
   const int k_begin = WINDOW ? (int)min((int64_t)Nkv, max((int64_t)0, q_wg + delta - window)) : 0;
   const int k_last = CAUSAL ? (int)max((int64_t)-1, min((int64_t)Nkv - 1, q_wg + T::BM - 1 + delta)) : Nkv - 1;
-  const int n_kt = k_last >= k_begin ? (k_last - k_begin) / T::BN + 1 : 0;
+  const int n_kt_a = k_last >= k_begin ? (k_last - k_begin) / T::BN + 1 : 0;
+  // the light tile of a pair (PAIR: no window, every tile sees key 0)
+  const int n_kt_b = qt_b >= 0 ? (int)min((int64_t)Nkv - 1, qt_b * T::BM + T::BM - 1 + delta) / T::BN + 1 : 0;
+  const int n_kt = n_kt_a + n_kt_b;
   if (n_kt == 0) {  // no query of this workgroup sees any key of the chunk: O = 0, lse = -inf
     uint16_t* og = (uint16_t*)p.o + sg.q_base;
 #pragma unroll
@@ -186,24 +197,29 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
     voff_k[i] = row * row_bytes + ((pc ^ T::swz_k(row)) << 4);
     voff_v[i] = row * row_bytes + ((pc ^ T::swz_v(row)) << 4);
   }
+  // tile j of the workgroup's sequence of tiles: the first unit's tiles, then the light unit's
+  auto key_of = [&](int j) __attribute__((always_inline)) { return k_begin + (j < n_kt_a ? j : j - n_kt_a) * T::BN; };
   auto issue_tile = [&](int j, uint8_t* kdst, uint8_t* vdst) {
-    issue_kv_tile<T::LOADS, T::NW>(kbuf, vbuf, voff_k, voff_v, (k_begin + j * T::BN) * row_bytes, wave, kdst, vdst);
+    issue_kv_tile<T::LOADS, T::NW>(kbuf, vbuf, voff_k, voff_v, key_of(j) * row_bytes, wave, kdst, vdst);
   };
 
   issue_tile(0, ks0, vs0);
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds q[q0 + 16*qg + li][32*c + 8*g .. +7] ----
   vec8 qf[T::QG][T::DC];
+  auto load_q = [&](int qbase) __attribute__((always_inline)) {
 #pragma unroll
-  for (int qg = 0; qg < T::QG; ++qg) {
-    const int qrow = min(q0 + 16 * qg + li, Nq - 1);
+    for (int qg = 0; qg < T::QG; ++qg) {
+      const int qrow = min(qbase + 16 * qg + li, Nq - 1);
 #pragma unroll
-    for (int c = 0; c < T::DC; ++c) {
-      u32x4_t raw = *(const u32x4_t*)(qg_ptr + qrow * p.stride_s + 32 * c + 8 * g);
-      raw ^= p.qsign;  // exact negation when scale < 0 (the exponent then uses |scale|)
-      qf[qg][c] = __builtin_bit_cast(vec8, raw);
+      for (int c = 0; c < T::DC; ++c) {
+        u32x4_t raw = *(const u32x4_t*)(qg_ptr + qrow * p.stride_s + 32 * c + 8 * g);
+        raw ^= p.qsign;  // exact negation when scale < 0 (the exponent then uses |scale|)
+        qf[qg][c] = __builtin_bit_cast(vec8, raw);
+      }
     }
-  }
+  };
+  load_q(q0);
 
   const float cexp = p.c;  // |scale| * log2(e)
   float m_ref[T::QG], l_part[T::QG];
@@ -235,12 +251,39 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
   // One K/V tile: wait for its DMA, prefetch the next one into the other stage, compute.
   // The last tile is a separate compile-time variant (no prefetch, full wait) so that every wait on
   // the DMA counter is unconditional and the compiler adds none of its own before LDS reads.
-  auto step = [&](int j, const uint8_t* ks, const uint8_t* vs, uint8_t* kn, uint8_t* vn, auto last_c) {
+  // epilogue of the current unit: O = acc / u, lse = (m + log2 l) ln 2; a row without any visible key
+  // has u = l = 0 and gets O = 0, lse = -inf
+  uint16_t* og_ptr = (uint16_t*)p.o + sg.q_base;
+  auto finish = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int qg = 0; qg < T::QG; ++qg) {
+      const float l = wave_sum_xor16_32(l_part[qg]);
+      const float inv = uacc[qg][0] > 0.0f ? 1.0f / uacc[qg][0] : 0.0f;
+      const int qi = q0 + 16 * qg + li;
+      if (qi < Nq) {
+#pragma unroll
+        for (int dt = 0; dt < T::DT; ++dt) {
+          const f32x4_t o = oacc[qg][dt] * inv;
+          u32x2_t w = {E::pack2(o[0], o[1]), E::pack2(o[2], o[3])};
+          *(u32x2_t*)(og_ptr + qi * p.stride_s + 16 * dt + 4 * g) = w;
+        }
+        if (g == 0) p.lse[sg.lse_base + qi] = (m_ref[qg] + __builtin_log2f(l)) * kLn2;
+      }
+    }
+  };
+
+  const std::integral_constant<bool, false> stay;
+  const std::integral_constant<bool, true> switch_c;
+  auto step = [&](int j, const uint8_t* ks, const uint8_t* vs, uint8_t* kn, uint8_t* vn, auto last_c,
+                  auto sw_c) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // this wave's share of tile j has landed
     lds_barrier();  // tile j is in LDS for every wave, and every wave is done with tile j-1
     if constexpr (!decltype(last_c)::value) issue_tile(j + 1, kn, vn);  // into tile j-1's stage
 
-    const int key0 = k_begin + j * T::BN;  // first chunk key of tile j
+    const int key0 = key_of(j);  // first chunk key of tile j
+    // the last tile of the heavy unit of a pair: the light unit's Q is loaded once S^T no longer needs
+    // the heavy unit's (the state moves over to the light unit after this step)
+    constexpr bool switch_unit = decltype(sw_c)::value;
     // the wave's 32 queries see some key of this tile (causal: its first key is not after the last
     // query's position; window: its last key is not before the first query's window)
     const bool active = (!CAUSAL || key0 <= q0 + T::QW - 1 + delta) && (!WINDOW || key0 + T::BN - 1 >= q0 + delta - window);
@@ -267,6 +310,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
 #pragma unroll
           for (int qg = 0; qg < T::QG; ++qg) s[qg][kt] = E::mfma(kf[c], qf[qg][c], s[qg][kt]);
       }
+      if constexpr (switch_unit) load_q(qt_b * T::BM + wave * T::QW);
 
       // ---- mask, online softmax, P ----
       const bool need_mask = (CAUSAL && key0 + T::BN - 1 > q0 + delta) || (key0 + T::BN > Nkv) ||
@@ -381,41 +425,57 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
           oacc[qg][dt] = E::mfma(vf, __builtin_bit_cast(vec8, w), oacc[qg][dt]);
         }
       }
+    } else if constexpr (switch_unit) {
+      load_q(qt_b * T::BM + wave * T::QW);
     }
   };
 
   const std::integral_constant<bool, false> more;
   const std::integral_constant<bool, true> last;
-  int j = 0;
-  for (; j + 2 < n_kt; j += 2) {
-    step(j, ks0, vs0, ks1, vs1, more);
-    step(j + 1, ks1, vs1, ks0, vs0, more);
-  }
-  if (j + 2 == n_kt) {
-    step(j, ks0, vs0, ks1, vs1, more);
-    step(j + 1, ks1, vs1, ks0, vs0, last);
+  if constexpr (PAIR) {
+    // both units have an even number of tiles (the launcher pairs only then), so every tile j sits in
+    // stage j % 2 and the light unit starts in stage 0; the heavy unit's last step prefetches the
+    // light unit's first tile
+    int j = 0;
+    for (; j + 2 < n_kt_a; j += 2) {
+      step(j, ks0, vs0, ks1, vs1, more, stay);
+      step(j + 1, ks1, vs1, ks0, vs0, more, stay);
+    }
+    step(j, ks0, vs0, ks1, vs1, more, stay);
+    step(j + 1, ks1, vs1, ks0, vs0, more, switch_c);  // loads the light unit's Q after its S^T
+    j += 2;
+    finish();
+    q_wg = qt_b * T::BM;
+    q0 = q_wg + wave * T::QW;
+    first_tile = true;
+#pragma unroll
+    for (int qg = 0; qg < T::QG; ++qg) {
+      m_ref[qg] = kNegInf;
+      l_part[qg] = 0.f;
+      uacc[qg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt) oacc[qg][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    for (; j + 2 < n_kt; j += 2) {
+      step(j, ks0, vs0, ks1, vs1, more, stay);
+      step(j + 1, ks1, vs1, ks0, vs0, more, stay);
+    }
+    step(j, ks0, vs0, ks1, vs1, more, stay);
+    step(j + 1, ks1, vs1, ks0, vs0, last, stay);
   } else {
-    step(j, ks0, vs0, ks1, vs1, last);
-  }
-
-  // ---- epilogue: O = acc / u, lse = (m + log2 l) ln 2; a row without any visible key has u = l = 0 and
-  // gets O = 0, lse = -inf ----
-  uint16_t* og_ptr = (uint16_t*)p.o + sg.q_base;
-#pragma unroll
-  for (int qg = 0; qg < T::QG; ++qg) {
-    const float l = wave_sum_xor16_32(l_part[qg]);
-    const float inv = uacc[qg][0] > 0.0f ? 1.0f / uacc[qg][0] : 0.0f;
-    const int qi = q0 + 16 * qg + li;
-    if (qi < Nq) {
-#pragma unroll
-      for (int dt = 0; dt < T::DT; ++dt) {
-        const f32x4_t o = oacc[qg][dt] * inv;
-        u32x2_t w = {E::pack2(o[0], o[1]), E::pack2(o[2], o[3])};
-        *(u32x2_t*)(og_ptr + qi * p.stride_s + 16 * dt + 4 * g) = w;
-      }
-      if (g == 0) p.lse[sg.lse_base + qi] = (m_ref[qg] + __builtin_log2f(l)) * kLn2;
+    int j = 0;
+    for (; j + 2 < n_kt; j += 2) {
+      step(j, ks0, vs0, ks1, vs1, more, stay);
+      step(j + 1, ks1, vs1, ks0, vs0, more, stay);
+    }
+    if (j + 2 == n_kt) {
+      step(j, ks0, vs0, ks1, vs1, more, stay);
+      step(j + 1, ks1, vs1, ks0, vs0, last, stay);
+    } else {
+      step(j, ks0, vs0, ks1, vs1, last, stay);
     }
   }
+  finish();
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -591,13 +651,14 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_32(Params p) {
 // ------------------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------------------
-template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW, bool VARLEN = false>
+template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW, bool VARLEN = false, bool PAIR = false>
 static hipError_t launch16(Params p, hipStream_t stream) {
   typedef Tile16<D> T;
   p.n_qtiles = (p.Nq + T::BM - 1) / T::BM;
+  if (PAIR) p.n_qtiles = (p.n_qtiles + 1) / 2;  // pairs of tiles per head
   // packed sequences: heads spread over the XCDs, the grid padded to a multiple of 8 heads
   p.n_units = p.n_qtiles * (VARLEN ? (p.B * p.H + 7) / 8 * 8 : p.B * p.H);
-  hipLaunchKernelGGL((fa_fwd_16<D, IS_BF16, CAUSAL, WINDOW, VARLEN>), dim3(p.n_units), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((fa_fwd_16<D, IS_BF16, CAUSAL, WINDOW, VARLEN, PAIR>), dim3(p.n_units), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -613,7 +674,13 @@ static hipError_t launch32(Params p, hipStream_t stream) {
 template <int D, bool IS_BF16>
 static hipError_t launch16_d(const Params& p, bool causal, hipStream_t stream) {
   if (!causal) return launch16<D, IS_BF16, false, false>(p, stream);
-  return p.window >= 0 ? launch16<D, IS_BF16, true, true>(p, stream) : launch16<D, IS_BF16, true, false>(p, stream);
+  if (p.window >= 0) return launch16<D, IS_BF16, true, true>(p, stream);
+  // the whole causal problem (every query tile sees key 0): pairs of heavy and light tiles
+  // (an even number of query tiles, each visiting an even number of 64-key tiles)
+  const int n_full = (p.Nq + Tile16<D>::BM - 1) / Tile16<D>::BM, rem = p.Nq % Tile16<D>::BM;
+  if (p.delta == 0 && p.Nq == p.Nkv && p.kv_start == 0 && n_full % 2 == 0 && (rem == 0 || rem > Tile16<D>::BN))
+    return launch16<D, IS_BF16, true, false, false, true>(p, stream);
+  return launch16<D, IS_BF16, true, false>(p, stream);
 }
 
 template <int D>
