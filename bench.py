@@ -55,9 +55,13 @@ VARIANTS = {
 
 
 def kernel_sha() -> str:
+    """Hash of the forward kernel's source with // comments and blank lines removed (code changes only)."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        h.update(open(p, "rb").read())
+        for line in open(p, encoding="utf-8").read().splitlines():
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

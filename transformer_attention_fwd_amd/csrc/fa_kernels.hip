@@ -34,7 +34,10 @@
 //   * Causal: per-wave skip of K tiles wholly above the wave's queries; element mask only on tiles
 //     crossing the diagonal or the sequence end.
 //   * Workgroup -> (head, Q tile) order: every XCD takes a contiguous run of heads (its L2 then holds
-//     those heads' K/V), heaviest causal Q tiles first.
+//     those heads' K/V), heaviest causal Q tiles first.  For the whole causal problem a workgroup runs
+//     a pair of Q tiles of one head, the heaviest and the lightest remaining (equal work per pair), as
+//     one stream of K/V tiles: the light tile's first K/V tile and its Q are fetched during the heavy
+//     tile's last step.  Packed variable-length batches spread each sequence's heads over the XCDs.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
