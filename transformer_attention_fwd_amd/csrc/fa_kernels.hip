@@ -27,8 +27,9 @@
 //   * V^T operand: ds_read_b64_tr_b16 (transposing LDS read) from the row-major V tile.
 //   * exp2 with scale*log2(e) folded into one FMA, against a reference maximum that is only moved when
 //     needed: P is computed against the current reference, and only when some lane's partial sum shows a
-//     probability above 2^8 (a new maximum well above the reference), or on a wave's first active tile, is the
-//     row maximum taken, the state rescaled and P recomputed.  Exact up to rounding either way.
+//     probability above 2^64 (bf16; 2^14 for fp16), i.e. a new maximum far above the reference, or on a
+//     wave's first active tile, is the row maximum taken, the state rescaled and P recomputed.  Exact up
+//     to rounding either way.
 //   * Row sums: l (for lse) in fp32 from the unrounded P; the normaliser of O from the P.V MFMA itself
 //     against an all-ones operand, i.e. the sum of P exactly as rounded for the P.V product.
 //   * Causal: per-wave skip of K tiles wholly above the wave's queries; element mask only on tiles
@@ -49,10 +50,14 @@
 
 namespace fa {
 
-// deferred rescale threshold, in log2 units: probabilities stay below 2^8 before renormalising
+// fp32 kernel: deferred rescale threshold, in log2 units (probabilities stay below 2^8 before renormalising)
 constexpr float kRescaleThreshold = 8.0f;
-// a lane's partial sum of 16 probabilities above this means some probability may exceed 2^8
-constexpr float kPartLimit = 256.0f;
+// 16-bit kernels: a lane's partial sum of 16 probabilities above this limit means some probability may
+// exceed it, and the reference maximum moves.  P is rounded to the input type for the P.V product, so the
+// limit keeps P representable there: 2^14 for fp16 (largest finite 65504); 2^64 for bf16, whose exponent
+// range is fp32's (O, u and l accumulate in fp32: 2^16 keys x 2^64 x |v| stays far from overflow).
+template <bool IS_BF16>
+__device__ constexpr float part_limit() { return IS_BF16 ? 18446744073709551616.0f : 16384.0f; }
 __device__ __forceinline__ float quad_max(float x) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
@@ -337,7 +342,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
         }
       }
       // P = exp2(c s - m_ref) against the current reference maximum; valid while no probability exceeds
-      // 2^8, which each lane checks through its partial sums.  Otherwise (and on a wave's first tile)
+      // the dtype's limit, which each lane checks through its partial sums.  Otherwise (and on a wave's first tile)
       // the reference moves to the running maximum first and P is recomputed.
       uint32_t pf[T::QG][T::KC][4];
       float part[T::QG];
@@ -363,7 +368,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
 #pragma unroll
         for (int qg = 0; qg < T::QG; ++qg) {
           expo(qg);
-          over |= part[qg] > kPartLimit;
+          over |= part[qg] > part_limit<IS_BF16>();
         }
         slow = __builtin_amdgcn_ballot_w64(over) != 0;
       }
@@ -378,7 +383,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
             for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[qg][kt][r]);
           mx = quad_max(mx);
           // a row that has seen no visible key yet takes 0 as its reference (its sums stay 0 and any
-          // reference is valid until a probability would exceed 2^8, which the check above catches)
+          // reference is valid until a probability would exceed the limit, which the check above catches)
           float m_new = fmaxf(m_ref[qg], mx * cexp);
           if (m_new == kNegInf) m_new = 0.0f;
           const float alpha = __builtin_amdgcn_exp2f(m_ref[qg] - m_new);
