@@ -55,6 +55,13 @@ def _load():
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ]
+        lib.fa_oracle_bwd_head_ex.restype = ctypes.c_int
+        lib.fa_oracle_bwd_head_ex.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ]
         lib.fa_oracle_bwd_head.restype = ctypes.c_int
         lib.fa_oracle_bwd_head.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
@@ -271,3 +278,48 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, dtype: str, causal:
         o[qs:qe] = ob[0]
         lse[:, qs:qe] = lb[0]
     return o, lse
+
+
+def attention_bwd_ex(q, k, v, dout, *, dtype: str, layout: str, causal: bool, scale: float, window: int = -1,
+                     q_offset: int = 0, kv_start: int = 0, kv_len=None, heads=None, nthreads: int = 1):
+    """Generalised gradients in fp64, the backward of ``attention_ex``'s rule.
+
+    q, dout: [B,H,Nq,D] / [B,Nq,H,D]; k, v: [B,H,Nk,D] / [B,Nk,H,D].  P and D are those of the softmax over
+    every visible key of [0, Nk) (query i at q_offset + i, causal and window as in ``attention_rows_ex``);
+    the key chunk [kv_start, kv_start + kv_len) restricts what is returned: dQ sums over the chunk's keys
+    only, and dK, dV are 0 outside the chunk.  heads=None -> arrays in the input layout; a sequence of
+    (b, h) -> arrays [len(heads), Nq or Nk, D].
+    """
+    if dtype not in DTYPES:
+        raise ValueError("dtype must be one of %s" % sorted(DTYPES))
+    B, H, Nq, D = _dims(q.shape, layout)
+    Bk, Hk, Nk, Dk = _dims(k.shape, layout)
+    if (Bk, Hk, Dk) != (B, H, D) or v.shape != k.shape or dout.shape != q.shape:
+        raise ValueError("k, v must share a shape matching q in B, H, D; dout must be shaped like q")
+    for t in (q, k, v, dout):
+        if t.dtype.itemsize != ITEMSIZE[dtype]:
+            raise ValueError("q, k, v, dout must have the itemsize of %s" % dtype)
+    if kv_len is None:
+        kv_len = Nk - kv_start
+    q, k, v, dout = (np.ascontiguousarray(t) for t in (q, k, v, dout))
+    sel = [(b, h) for b in range(B) for h in range(H)] if heads is None else [tuple(x) for x in heads]
+    dqs = np.empty((len(sel), Nq, D)); dks = np.empty((len(sel), Nk, D)); dvs = np.empty((len(sel), Nk, D))
+    for n, (b, h) in enumerate(sel):
+        dq, dk, dv = np.empty((Nq, D)), np.empty((Nk, D)), np.empty((Nk, D))
+        rc = _load().fa_oracle_bwd_head_ex(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
+                                           DTYPES[dtype], LAYOUTS[layout], B, H, Nq, Nk, D, 1 if causal else 0,
+                                           int(window), int(q_offset), int(kv_start), int(kv_len), float(scale),
+                                           int(b), int(h), dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
+                                           int(nthreads))
+        if rc != 0:
+            raise ValueError("fa_oracle_bwd_head_ex failed with status %d" % rc)
+        dqs[n], dks[n], dvs[n] = dq, dk, dv
+    if heads is not None:
+        return dqs, dks, dvs
+    out = []
+    for g, n in ((dqs, Nq), (dks, Nk), (dvs, Nk)):
+        g = g.reshape(B, H, n, D)
+        if layout == "BSND":
+            g = np.ascontiguousarray(g.transpose(0, 2, 1, 3))
+        out.append(g)
+    return tuple(out)

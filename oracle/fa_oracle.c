@@ -260,72 +260,90 @@ int fa_oracle_rows(const void* q, const void* k, const void* v, int dtype, int l
  * Everything is in double.  D_i is taken from P and dP as the chain rule gives it (not from O).
  * Rows are split among the workers; each worker keeps its own dK and dV accumulators, which are
  * added in worker order at the end.
+ *
+ * Generalised rows (fa_oracle_bwd_head_ex), matching fa_oracle_rows_ex: query row i of an Nq-row Q
+ * sits at position q_offset + i and sees the keys j of [0, Nk) with j <= q_offset + i (causal) and
+ * j >= q_offset + i - window (window >= 0, causal only); P and D are those of this full softmax.  A
+ * key chunk [kv_start, kv_start + kv_len) restricts what is returned: dQ_i sums dS_ij k_j over the
+ * chunk's keys only, and dK, dV are accumulated for the chunk's rows only (other rows are 0).  Summed
+ * over disjoint chunks covering [0, Nk), the partial dQ give the full dQ: the backward of attention
+ * computed in key chunks whose partial results were merged through their lse (page ai6s.net/
+ * 6a0d3bfb..., section "ops-transformer仓库里还有什么？", ring / block-wise attention).
  * ---------------------------------------------------------------------------------------------
  */
 typedef struct {
     const void *q, *k, *v, *dout;
     int dtype, layout, causal;
-    int64_t B, H, N, D, b, h;
+    int64_t B, H, Nq, Nk, D, b, h;
+    int64_t window, q_offset, kv_start, kv_len;
     double scale;
-    double *dq, *dk, *dv; /* dq: N x D shared (rows are disjoint); dk, dv: this worker's N x D */
+    double *dq, *dk, *dv; /* dq: Nq x D shared (rows are disjoint); dk, dv: this worker's Nk x D */
     int64_t first, last;
     int status;
 } orc_bwd_job;
 
-static int64_t orc_bwd_index(const orc_bwd_job* J, int64_t i, int64_t d) {
-    if (J->layout == 0) return ((J->b * J->H + J->h) * J->N + i) * J->D + d;
-    return ((J->b * J->N + i) * J->H + J->h) * J->D + d;
+/* element index of row i of a tensor with N rows per (b, h) */
+static int64_t orc_bwd_index(const orc_bwd_job* J, int64_t N, int64_t i, int64_t d) {
+    if (J->layout == 0) return ((J->b * J->H + J->h) * N + i) * J->D + d;
+    return ((J->b * N + i) * J->H + J->h) * J->D + d;
 }
 
 static void* orc_bwd_worker(void* arg) {
     orc_bwd_job* J = (orc_bwd_job*)arg;
-    const int64_t N = J->N, D = J->D;
+    const int64_t Nq = J->Nq, Nk = J->Nk, D = J->D;
     double* qrow = (double*)malloc(sizeof(double) * (size_t)D);
     double* dorow = (double*)malloc(sizeof(double) * (size_t)D);
-    double* p = (double*)malloc(sizeof(double) * (size_t)N);
-    double* dp = (double*)malloc(sizeof(double) * (size_t)N);
+    double* p = (double*)malloc(sizeof(double) * (size_t)Nk);
+    double* dp = (double*)malloc(sizeof(double) * (size_t)Nk);
     if (!qrow || !dorow || !p || !dp) {
         free(qrow); free(dorow); free(p); free(dp);
         J->status = -1;
         return NULL;
     }
+    const int64_t c0 = J->kv_start, c1 = J->kv_start + J->kv_len; /* the chunk */
     for (int64_t i = J->first; i < J->last; ++i) {
-        const int64_t jend = J->causal ? i + 1 : N; /* visible keys 0 .. jend-1 */
+        double* dqi = J->dq + i * D;
+        for (int64_t d = 0; d < D; ++d) dqi[d] = 0.0;
+        /* visible keys jbeg .. jend-1 of the full softmax */
+        const int64_t qpos = i + J->q_offset;
+        int64_t jbeg = 0, jend = Nk;
+        if (J->causal && jend > qpos + 1) jend = qpos + 1;
+        if (J->window >= 0 && jbeg < qpos - J->window) jbeg = qpos - J->window;
+        if (jend <= jbeg) continue; /* no visible key: O is constant 0, every gradient from this row is 0 */
         for (int64_t d = 0; d < D; ++d) {
-            qrow[d] = orc_load(J->q, J->dtype, orc_bwd_index(J, i, d));
-            dorow[d] = orc_load(J->dout, J->dtype, orc_bwd_index(J, i, d));
+            qrow[d] = orc_load(J->q, J->dtype, orc_bwd_index(J, Nq, i, d));
+            dorow[d] = orc_load(J->dout, J->dtype, orc_bwd_index(J, Nq, i, d));
         }
         /* softmax row, two passes */
         double m = -INFINITY;
-        for (int64_t j = 0; j < jend; ++j) {
+        for (int64_t j = jbeg; j < jend; ++j) {
             double dot = 0.0;
-            for (int64_t d = 0; d < D; ++d) dot += qrow[d] * orc_load(J->k, J->dtype, orc_bwd_index(J, j, d));
+            for (int64_t d = 0; d < D; ++d) dot += qrow[d] * orc_load(J->k, J->dtype, orc_bwd_index(J, Nk, j, d));
             p[j] = J->scale * dot;
             if (p[j] > m) m = p[j];
         }
         double l = 0.0;
-        for (int64_t j = 0; j < jend; ++j) {
+        for (int64_t j = jbeg; j < jend; ++j) {
             p[j] = exp(p[j] - m);
             l += p[j];
         }
-        for (int64_t j = 0; j < jend; ++j) p[j] /= l;
+        for (int64_t j = jbeg; j < jend; ++j) p[j] /= l;
         /* dP and D */
         double Di = 0.0;
-        for (int64_t j = 0; j < jend; ++j) {
+        for (int64_t j = jbeg; j < jend; ++j) {
             double dot = 0.0;
-            for (int64_t d = 0; d < D; ++d) dot += dorow[d] * orc_load(J->v, J->dtype, orc_bwd_index(J, j, d));
+            for (int64_t d = 0; d < D; ++d) dot += dorow[d] * orc_load(J->v, J->dtype, orc_bwd_index(J, Nk, j, d));
             dp[j] = dot;
             Di += p[j] * dp[j];
         }
-        /* dS and the three gradients */
-        double* dqi = J->dq + i * D;
-        for (int64_t d = 0; d < D; ++d) dqi[d] = 0.0;
-        for (int64_t j = 0; j < jend; ++j) {
+        /* dS and the three gradients, over the visible keys of the chunk */
+        const int64_t kb = jbeg > c0 ? jbeg : c0, ke = jend < c1 ? jend : c1;
+        for (int64_t j = kb; j < ke; ++j) {
             const double ds = p[j] * (dp[j] - Di);
             double* dkj = J->dk + j * D;
             double* dvj = J->dv + j * D;
             for (int64_t d = 0; d < D; ++d) {
-                dqi[d] += J->scale * ds * orc_load(J->k, J->dtype, orc_bwd_index(J, j, d));
+                dqi[d] += J->scale * ds * orc_load(J->k, J->dtype, orc_bwd_index(J, Nk, j, d));
                 dkj[d] += J->scale * ds * qrow[d];
                 dvj[d] += p[j] * dorow[d];
             }
@@ -336,22 +354,26 @@ static void* orc_bwd_worker(void* arg) {
 }
 
 /*
- * Gradients dQ, dK, dV (each N x D, row-major, fp64) of head (b, h) for upstream gradient `dout`
- * (same dtype and layout as q).  Returns 0 on success, -2 on a bad argument, -1 if memory ran out.
+ * Generalised gradients of head (b, h): dq (Nq x D), dk and dv (Nk x D; rows outside the chunk 0),
+ * row-major fp64, under the rule described above.  q, dout: [B][H][Nq][D] or [B][Nq][H][D]; k, v:
+ * [B][H][Nk][D] or [B][Nk][H][D].  Returns 0 on success, -2 on a bad argument, -1 if memory ran out.
  */
-int fa_oracle_bwd_head(const void* q, const void* k, const void* v, const void* dout, int dtype, int layout,
-                       int64_t B, int64_t H, int64_t N, int64_t D, int causal, double scale, int64_t b,
-                       int64_t h, double* dq, double* dk, double* dv, int nthreads) {
+int fa_oracle_bwd_head_ex(const void* q, const void* k, const void* v, const void* dout, int dtype, int layout,
+                          int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal, int64_t window,
+                          int64_t q_offset, int64_t kv_start, int64_t kv_len, double scale, int64_t b, int64_t h,
+                          double* dq, double* dk, double* dv, int nthreads) {
     if (!q || !k || !v || !dout || !dq || !dk || !dv) return -2;
     if (dtype < 0 || dtype > 3 || layout < 0 || layout > 1) return -2;
-    if (B < 1 || H < 1 || N < 1 || D < 1 || b < 0 || b >= B || h < 0 || h >= H) return -2;
+    if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || D < 1 || b < 0 || b >= B || h < 0 || h >= H) return -2;
+    if (kv_start < 0 || kv_len < 0 || kv_start + kv_len > Nk) return -2;
+    if (window >= 0 && !causal) return -2;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 512) nthreads = 512;
-    if (N < nthreads) nthreads = (int)N;
+    if (Nq < nthreads) nthreads = (int)Nq;
     orc_bwd_job* jobs = (orc_bwd_job*)calloc((size_t)nthreads, sizeof(orc_bwd_job));
     pthread_t* tids = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
     char* running = (char*)calloc((size_t)nthreads, 1);
-    double* part = (double*)calloc((size_t)nthreads * 2 * (size_t)(N * D), sizeof(double));
+    double* part = (double*)calloc((size_t)nthreads * 2 * (size_t)(Nk * D), sizeof(double));
     if (!jobs || !tids || !running || !part) {
         free(jobs); free(tids); free(running); free(part);
         return -1;
@@ -360,13 +382,15 @@ int fa_oracle_bwd_head(const void* q, const void* k, const void* v, const void* 
         orc_bwd_job* J = &jobs[t];
         J->q = q; J->k = k; J->v = v; J->dout = dout;
         J->dtype = dtype; J->layout = layout; J->causal = causal ? 1 : 0;
-        J->B = B; J->H = H; J->N = N; J->D = D; J->b = b; J->h = h;
+        J->B = B; J->H = H; J->Nq = Nq; J->Nk = Nk; J->D = D; J->b = b; J->h = h;
+        J->window = window < 0 ? -1 : window;
+        J->q_offset = q_offset; J->kv_start = kv_start; J->kv_len = kv_len;
         J->scale = scale;
         J->dq = dq;
-        J->dk = part + (size_t)(2 * t) * (size_t)(N * D);
-        J->dv = part + (size_t)(2 * t + 1) * (size_t)(N * D);
-        J->first = N * t / nthreads;
-        J->last = N * (t + 1) / nthreads;
+        J->dk = part + (size_t)(2 * t) * (size_t)(Nk * D);
+        J->dv = part + (size_t)(2 * t + 1) * (size_t)(Nk * D);
+        J->first = Nq * t / nthreads;
+        J->last = Nq * (t + 1) / nthreads;
     }
     for (int t = 1; t < nthreads; ++t) {
         if (pthread_create(&tids[t], NULL, orc_bwd_worker, &jobs[t]) == 0)
@@ -380,7 +404,7 @@ int fa_oracle_bwd_head(const void* q, const void* k, const void* v, const void* 
     int status = 0;
     for (int t = 0; t < nthreads; ++t)
         if (jobs[t].status) status = jobs[t].status;
-    for (int64_t e = 0; e < N * D; ++e) {
+    for (int64_t e = 0; e < Nk * D; ++e) {
         double sk = 0.0, sv = 0.0;
         for (int t = 0; t < nthreads; ++t) {
             sk += jobs[t].dk[e];
@@ -391,4 +415,16 @@ int fa_oracle_bwd_head(const void* q, const void* k, const void* v, const void* 
     }
     free(jobs); free(tids); free(running); free(part);
     return status;
+}
+
+/*
+ * Gradients dQ, dK, dV (each N x D, row-major, fp64) of head (b, h) for upstream gradient `dout`
+ * (same dtype and layout as q): the plain case Nq = Nk = N, every key.  Returns 0 on success, -2 on a
+ * bad argument, -1 if memory ran out.
+ */
+int fa_oracle_bwd_head(const void* q, const void* k, const void* v, const void* dout, int dtype, int layout,
+                       int64_t B, int64_t H, int64_t N, int64_t D, int causal, double scale, int64_t b,
+                       int64_t h, double* dq, double* dk, double* dv, int nthreads) {
+    return fa_oracle_bwd_head_ex(q, k, v, dout, dtype, layout, B, H, N, N, D, causal, -1, 0, 0, N, scale, b, h,
+                                 dq, dk, dv, nthreads);
 }

@@ -148,3 +148,104 @@ def test_bad_arguments():
         oracle.attention_bwd(q, q, q, np.zeros((1, 1, 4, 3)), dtype="fp64", layout="BHSD", causal=False, scale=1.0)
     with pytest.raises(ValueError):
         oracle.attention_bwd(q, q, q, q, dtype="fp64", layout="BHSD", causal=False, scale=1.0, heads=[(0, 1)])
+
+
+# ---- generalised rows: query offset, N_q != N_k, window, key chunk ------------------------------------
+
+def _vis(Nq, Nk, causal, window, q_offset):
+    qpos = q_offset + np.arange(Nq)[:, None]
+    kpos = np.arange(Nk)[None, :]
+    vis = np.ones((Nq, Nk), dtype=bool)
+    if causal:
+        vis &= kpos <= qpos
+    if window >= 0:
+        vis &= kpos >= qpos - window
+    return vis
+
+
+def _torch_grads_general(q, k, v, dout, vis, scale):
+    """Autograd of the explicit-mask attention; rows that see no key have O = 0 (their gradients vanish)."""
+    import torch
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    s = scale * (tq @ tk.transpose(-1, -2))
+    m = torch.tensor(vis)
+    s = s.masked_fill(~m, float("-inf"))
+    any_vis = m.any(dim=-1)
+    s = torch.where(any_vis[:, None], s, torch.zeros_like(s))  # keep softmax finite on empty rows
+    p = torch.softmax(s, dim=-1) * any_vis[:, None]
+    (p @ tv).backward(torch.tensor(dout, dtype=torch.float64))
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+def test_ex_defaults_equal_plain():
+    rng = np.random.default_rng(81)
+    q, k, v, dout = (_rand(rng, (1, 2, 21, 8)) for _ in range(4))
+    a = oracle.attention_bwd(q, k, v, dout, dtype="fp64", layout="BHSD", causal=True, scale=0.4)
+    b = oracle.attention_bwd_ex(q, k, v, dout, dtype="fp64", layout="BHSD", causal=True, scale=0.4)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("Nq,Nk,causal,window,q_offset", [
+    (5, 9, True, -1, 4),    # bottom-right causal, prefill with a key cache
+    (7, 7, True, 2, 0),     # sliding window
+    (6, 11, True, 3, 5),    # both
+    (6, 8, True, -1, -2),   # negative offset: the first rows see nothing
+    (5, 7, False, -1, 0),   # N_q != N_k without a mask
+])
+def test_ex_finite_differences_and_autograd(Nq, Nk, causal, window, q_offset):
+    rng = np.random.default_rng([82, Nq, Nk, window + 2, q_offset + 10])
+    q, dout = _rand(rng, (1, 1, Nq, 3)), _rand(rng, (1, 1, Nq, 3))
+    k, v = _rand(rng, (1, 1, Nk, 3)), _rand(rng, (1, 1, Nk, 3))
+    scale = 0.8
+    kw = dict(dtype="fp64", layout="BHSD", causal=causal, scale=scale, window=window, q_offset=q_offset)
+    dq, dk, dv = oracle.attention_bwd_ex(q, k, v, dout, **kw)
+    # torch autograd of the explicit-mask definition
+    ref = _torch_grads_general(q[0, 0], k[0, 0], v[0, 0], dout[0, 0], _vis(Nq, Nk, causal, window, q_offset), scale)
+    for g, r in zip((dq, dk, dv), ref):
+        np.testing.assert_allclose(g[0, 0], r, atol=1e-11)
+    # central differences of the forward oracle's generalised rows
+    eps = 1e-6
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.attention_ex(qq, kk, vv, **{x: kw[x] for x in kw if x != "scale"}, scale=scale)
+        return float((o * dout).sum())
+
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = x.copy(); xp[idx] += eps
+            xm = x.copy(); xm[idx] -= eps
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            lp = loss(args["q"], args["k"], args["v"])
+            args[name] = xm
+            lm = loss(args["q"], args["k"], args["v"])
+            num[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g, num, atol=2e-8, err_msg=name)
+
+
+@pytest.mark.parametrize("cuts", [(0, 4, 9, 13), (0, 1, 13), (0, 7, 7, 13)])
+def test_ex_chunks_add_up(cuts):
+    rng = np.random.default_rng(83)
+    Nq, Nk = 6, 13
+    q, dout = _rand(rng, (1, 2, Nq, 4)), _rand(rng, (1, 2, Nq, 4))
+    k, v = _rand(rng, (1, 2, Nk, 4)), _rand(rng, (1, 2, Nk, 4))
+    kw = dict(dtype="fp64", layout="BHSD", causal=True, scale=0.5, window=5, q_offset=Nk - Nq)
+    full = oracle.attention_bwd_ex(q, k, v, dout, **kw)
+    dq_sum = np.zeros_like(full[0])
+    for a, b in zip(cuts, cuts[1:]):
+        dq, dk, dv = oracle.attention_bwd_ex(q, k, v, dout, **kw, kv_start=a, kv_len=b - a)
+        dq_sum += dq
+        np.testing.assert_allclose(dk[:, :, a:b], full[1][:, :, a:b], atol=1e-14)
+        np.testing.assert_allclose(dv[:, :, a:b], full[2][:, :, a:b], atol=1e-14)
+        assert np.all(dk[:, :, :a] == 0) and np.all(dk[:, :, b:] == 0) and np.all(dv[:, :, :a] == 0)
+    np.testing.assert_allclose(dq_sum, full[0], atol=1e-13)
+
+
+def test_ex_bad_arguments():
+    z = np.zeros((1, 1, 4, 2))
+    with pytest.raises(ValueError):
+        oracle.attention_bwd_ex(z, z, z, z, dtype="fp64", layout="BHSD", causal=False, scale=1.0, window=2)
+    with pytest.raises(ValueError):
+        oracle.attention_bwd_ex(z, z, z, z, dtype="fp64", layout="BHSD", causal=True, scale=1.0, kv_start=3, kv_len=2)

@@ -159,17 +159,25 @@ BWD_MUTANTS = {
     "bwd_dq_unscaled": ("dqi[d] += J->scale * ds * orc_load", "dqi[d] += ds * orc_load"),
     "bwd_dv_uses_ds": ("dvj[d] += p[j] * dorow[d];", "dvj[d] += ds * dorow[d];"),
     "bwd_dk_uses_k": ("dkj[d] += J->scale * ds * qrow[d];",
-                      "dkj[d] += J->scale * ds * orc_load(J->k, J->dtype, orc_bwd_index(J, j, d));"),
+                      "dkj[d] += J->scale * ds * orc_load(J->k, J->dtype, orc_bwd_index(J, Nk, j, d));"),
     "bwd_dp_uses_q": ("dot += dorow[d] * orc_load(J->v", "dot += qrow[d] * orc_load(J->v"),
-    "bwd_unnormalised_p": ("for (int64_t j = 0; j < jend; ++j) p[j] /= l;", "for (int64_t j = 0; j < jend; ++j) p[j] /= 1.0;"),
-    "bwd_causal_extra_key": ("const int64_t jend = J->causal ? i + 1 : N;",
-                             "const int64_t jend = J->causal ? (i + 2 < N ? i + 2 : N) : N;"),
-    "bwd_causal_not_applied": ("const int64_t jend = J->causal ? i + 1 : N;", "const int64_t jend = N;"),
+    "bwd_unnormalised_p": ("for (int64_t j = jbeg; j < jend; ++j) p[j] /= l;",
+                           "for (int64_t j = jbeg; j < jend; ++j) p[j] /= 1.0;"),
+    "bwd_causal_extra_key": ("if (J->causal && jend > qpos + 1) jend = qpos + 1;",
+                             "if (J->causal && jend > qpos + 2) jend = qpos + 2;"),
+    "bwd_causal_not_applied": ("if (J->causal && jend > qpos + 1) jend = qpos + 1;", ""),
     "bwd_no_max_subtraction": ("p[j] = exp(p[j] - m);", "p[j] = exp(p[j]);"),
-    "bwd_dv_row_is_query": ("double* dvj = J->dv + j * D;", "double* dvj = J->dv + i * D;"),
+    "bwd_dv_row_is_query": ("double* dvj = J->dv + j * D;", "double* dvj = J->dv + (i % Nk) * D;"),
     "bwd_partials_last_worker_only": ("sk += jobs[t].dk[e];", "sk = jobs[t].dk[e];"),
-    "bwd_bsnd_read_as_bhsd": ("if (J->layout == 0) return ((J->b * J->H + J->h) * J->N + i) * J->D + d;",
-                              "return ((J->b * J->H + J->h) * J->N + i) * J->D + d;"),
+    "bwd_bsnd_read_as_bhsd": ("if (J->layout == 0) return ((J->b * J->H + J->h) * N + i) * J->D + d;",
+                              "return ((J->b * J->H + J->h) * N + i) * J->D + d;"),
+    # the generalised rule
+    "bwd_q_offset_ignored": ("const int64_t qpos = i + J->q_offset;", "const int64_t qpos = i;"),
+    "bwd_window_edge": ("if (J->window >= 0 && jbeg < qpos - J->window) jbeg = qpos - J->window;",
+                        "if (J->window >= 0 && jbeg < qpos - J->window + 1) jbeg = qpos - J->window + 1;"),
+    "bwd_chunk_restriction_ignored": ("const int64_t kb = jbeg > c0 ? jbeg : c0, ke = jend < c1 ? jend : c1;",
+                                      "const int64_t kb = jbeg, ke = jend;"),
+    "bwd_softmax_over_chunk_only": ("int64_t jbeg = 0, jend = Nk;", "int64_t jbeg = c0, jend = c1;"),
 }
 
 
@@ -180,10 +188,17 @@ def _build_bwd(tmp, name, old, new):
     open(path, "w").write(src.replace(old, new) if old else src)
     lib = os.path.join(tmp, name + ".so")
     subprocess.check_call(["gcc", "-O1", "-shared", "-fPIC", "-pthread", path, "-o", lib, "-lm"])
-    f = ctypes.CDLL(lib).fa_oracle_bwd_head
+    so = ctypes.CDLL(lib)
+    f = so.fa_oracle_bwd_head
     f.restype = ctypes.c_int
     f.argtypes = ([ctypes.c_void_p] * 4 + [ctypes.c_int] * 2 + [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_double]
                   + [ctypes.c_int64] * 2 + [ctypes.c_void_p] * 3 + [ctypes.c_int])
+    fx = so.fa_oracle_bwd_head_ex
+    fx.restype = ctypes.c_int
+    fx.argtypes = ([ctypes.c_void_p] * 4 + [ctypes.c_int] * 2 + [ctypes.c_int64] * 5 + [ctypes.c_int]
+                   + [ctypes.c_int64] * 4 + [ctypes.c_double] + [ctypes.c_int64] * 2 + [ctypes.c_void_p] * 3
+                   + [ctypes.c_int])
+    f.ex = fx
     return f
 
 
@@ -232,7 +247,30 @@ def _bwd_pins_pass(f):
     q[..., 0] = 100.0; k[0, 0, :, 0] = np.arange(5) * 2.0 + np.array([0, 0, 0, 5.0, 3.001])
     got = _bwd_call(f, q, k, v, dout, 0, 0, 1.0, 1)
     ref = _torch_ref(q, k, v, dout, 0, 1.0)
-    return all(np.all(np.isfinite(g)) and np.allclose(g, r, atol=1e-9) for g, r in zip(got, ref))
+    if not all(np.all(np.isfinite(g)) and np.allclose(g, r, atol=1e-9) for g, r in zip(got, ref)):
+        return False
+    # generalised rows: offset + window against the explicit-mask autograd, and chunk partials adding up
+    from tests.test_oracle_bwd import _torch_grads_general, _vis
+    Nq, Nk, qoff, win = 5, 9, 4, 3
+    q, dout = rng.standard_normal((Nq, 4)), rng.standard_normal((Nq, 4))
+    k, v = rng.standard_normal((Nk, 4)), rng.standard_normal((Nk, 4))
+
+    def ex(ks, kl):
+        dq, dk, dv = np.empty((Nq, 4)), np.empty((Nk, 4)), np.empty((Nk, 4))
+        args = [np.ascontiguousarray(x) for x in (q, k, v, dout)]
+        rc = f.ex(*[a.ctypes.data for a in args], 3, 0, 1, 1, Nq, Nk, 4, 1, win, qoff, ks, kl, 0.7, 0, 0,
+                  dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, 2)
+        assert rc == 0
+        return dq, dk, dv
+    full = ex(0, Nk)
+    ref = _torch_grads_general(q, k, v, dout, _vis(Nq, Nk, True, win, qoff), 0.7)
+    if not all(np.allclose(g, r, atol=1e-11) for g, r in zip(full, ref)):
+        return False
+    a, b = ex(0, 5), ex(5, 4)
+    if not (np.allclose(a[0] + b[0], full[0], atol=1e-13) and np.allclose(a[1][:5], full[1][:5], atol=1e-14)
+            and np.allclose(b[1][5:], full[1][5:], atol=1e-14) and np.all(a[1][5:] == 0) and np.all(b[2][:5] == 0)):
+        return False
+    return True
 
 
 def test_unmutated_copy_passes_backward_pins():
