@@ -55,8 +55,8 @@ extern "C" {
 #define FA_ERR_ALIAS 8             /* o or lse overlaps an input, or o overlaps lse */
 #define FA_ERR_NOT_DEVICE_MEMORY 9 /* a pointer is not device memory of the current device */
 #define FA_ERR_HIP 10              /* the HIP runtime reported an error; see fa_last_error() */
-#define FA_ERR_BAD_RANGE 11        /* fa_fwd_ex: key chunk outside [0, Nk], a window without causal, or
-                                      |q_offset| > 2^30; fa_fwd_varlen: max_seqlen_q > total_q */
+#define FA_ERR_BAD_RANGE 11        /* fa_fwd_ex / fa_bwd_ex: key chunk outside [0, Nk], a window without
+                                      causal, or |q_offset| > 2^30; fa_fwd_varlen: max_seqlen_q > total_q */
 
 /* Limits: 1 <= N <= 2^30, B*H <= 2^31 - 1, every tensor's byte size must fit in int64, and one head's
  * span -- (N - 1) * (bytes between consecutive positions) + D * element size -- must be below 2^31
@@ -180,6 +180,26 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
            void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t N, int64_t D, int layout,
            int causal, float scale, int dtype, void* stream);
+
+/*
+ * fa_bwd_ex -- the backward of fa_fwd_ex's rule: query row i at position q_offset + i, key row j at j,
+ * causal hides keys after the query, a window (causal only) keys more than `window` before it.  P and
+ * D are those of the softmax over every visible key of [0, Nk): pass the lse and O of the forward over
+ * all of them (for a forward computed in key chunks, the merged lse and O).  The key chunk
+ * [kv_start, kv_start + kv_len) restricts the work: dq (all Nq rows, overwritten) receives the chunk's
+ * part of dQ, sum_{j in chunk} dS_ij k_j * scale, so the dq of disjoint chunks covering all keys add up
+ * to dQ; dk and dv receive the chunk's rows and are left untouched elsewhere, so successive chunks can
+ * fill one dk/dv.  This is the backward of attention computed in key chunks (page ai6s.net/6a0d3bfb...,
+ * section "ops-transformer仓库里还有什么？", ring / block-wise attention).  fa_bwd(...) is
+ * fa_bwd_ex(..., Nq = Nk = N, window = -1, q_offset = 0, kv_start = 0, kv_len = N, ...).
+ *
+ * q, o, dout, dq: [B][H][Nq][D] or [B][Nq][H][D]; k, v, dk, dv: [B][H][Nk][D] or [B][Nk][H][D]; lse and
+ * delta: [B][H][Nq] fp32.  Checks, ownership and errors as fa_bwd, plus FA_ERR_BAD_RANGE as fa_fwd_ex.
+ */
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+              void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+              int layout, int causal, int64_t window, int64_t q_offset, int64_t kv_start, int64_t kv_len,
+              float scale, int dtype, void* stream);
 
 /* Static description of a status code ("ok", "null pointer", ...).  Never NULL. */
 const char* fa_status_str(int status);

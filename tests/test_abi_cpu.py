@@ -18,8 +18,8 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     declared = _declared()
-    assert declared == ["fa_bwd", "fa_fwd", "fa_fwd_ex", "fa_fwd_varlen", "fa_last_error", "fa_merge", "fa_status_str",
-                        "fa_version"]
+    assert declared == ["fa_bwd", "fa_bwd_ex", "fa_fwd", "fa_fwd_ex", "fa_fwd_varlen", "fa_last_error", "fa_merge",
+                        "fa_status_str", "fa_version"]
     out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], stdout=subprocess.PIPE,
                          text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.split() and l.split()[1] == "T"}
@@ -43,7 +43,7 @@ def test_header_constants_match_binding():
 
 
 def test_status_strings_and_version():
-    assert fa.version() == 400
+    assert fa.version() == 500
     for st in range(12):
         assert fa.status_str(st)
     assert fa.status_str(0) == "ok"
@@ -233,3 +233,32 @@ def test_fa_fwd_varlen_argument_checks(kw, status):
 
 def test_fa_fwd_varlen_good_arguments_reach_the_device_check():
     assert _call_v() in (fa.FA_ERR_NOT_DEVICE_MEMORY, fa.FA_ERR_HIP)
+
+
+# ---- fa_bwd_ex: pure argument checks ----
+GOOD_BX = dict(GOOD_B, Nq=64, Nk=100, window=-1, q_offset=36, kv_start=0, kv_len=100)
+del GOOD_BX["N"]
+
+
+def _call_bx(**kw):
+    a = dict(GOOD_BX)
+    a.update(kw)
+    return fa.fa_bwd_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"], a["delta"], a["B"],
+                        a["H"], a["Nq"], a["Nk"], a["D"], a["layout"], a["causal"], a["window"], a["q_offset"],
+                        a["kv_start"], a["kv_len"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dk=0), fa.FA_ERR_NULL), (dict(Nk=0), fa.FA_ERR_BAD_DIM), (dict(Nq=0), fa.FA_ERR_BAD_DIM),
+    (dict(dtype=0), fa.FA_ERR_UNSUPPORTED), (dict(kv_start=-1), fa.FA_ERR_BAD_RANGE),
+    (dict(kv_start=60, kv_len=41), fa.FA_ERR_BAD_RANGE), (dict(causal=0, window=4), fa.FA_ERR_BAD_RANGE),
+    (dict(q_offset=(1 << 30) + 1), fa.FA_ERR_BAD_RANGE), (dict(D=80, kv_start=-1), fa.FA_ERR_UNSUPPORTED),
+    (dict(dv=V + 32), fa.FA_ERR_ALIAS), (dict(delta=L + 8), fa.FA_ERR_MISALIGNED),
+])
+def test_fa_bwd_ex_argument_checks(kw, status):
+    assert _call_bx(**kw) == status
+
+
+def test_fa_bwd_ex_good_arguments_reach_the_device_check():
+    assert _call_bx() in (fa.FA_ERR_NOT_DEVICE_MEMORY, fa.FA_ERR_HIP)
+    assert _call_bx(kv_start=100, kv_len=0) in (fa.FA_ERR_NOT_DEVICE_MEMORY, fa.FA_ERR_HIP)

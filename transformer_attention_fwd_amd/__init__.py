@@ -27,6 +27,12 @@ There is no CPU or framework fallback: if ``libfa.so`` is missing the first call
         the backward C entry point, same conventions.
     attention_bwd(q, k, v, o, lse, dout, *, layout="BHSD", causal=False, scale=None, delta=None) -> (dq, dk, dv)
         fa_bwd on torch tensors: allocates dq, dk, dv (and the delta workspace unless given).
+    fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Nq, Nk, D, layout, causal, window, q_offset,
+              kv_start, kv_len, scale, dtype, stream) -> status
+    attention_bwd_ex(q, k, v, o, lse, dout, *, layout="BHSD", causal=False, scale=None, window=-1, q_offset=0,
+                     kv_start=0, kv_len=None, dk=None, dv=None, delta=None) -> (dq, dk, dv)
+        the generalised backward (dk, dv rows outside the key chunk keep the given tensors' values; new
+        tensors start at zero).
 """
 from __future__ import annotations
 
@@ -34,8 +40,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "fa_fwd_ex", "fa_fwd_varlen", "fa_merge", "fa_bwd", "attention", "attention_ex",
-           "attention_varlen", "merge", "attention_bwd", "FaError", "library_path",
+__all__ = ["fa_fwd", "fa_fwd_ex", "fa_fwd_varlen", "fa_merge", "fa_bwd", "fa_bwd_ex", "attention", "attention_ex",
+           "attention_varlen", "merge", "attention_bwd", "attention_bwd_ex", "FaError", "library_path",
            "load", "status_str", "version",
            "LAYOUT_BHSD", "LAYOUT_BSND", "DTYPE_FP32", "DTYPE_FP16", "DTYPE_BF16"]
 
@@ -94,6 +100,9 @@ def load():
         lib.fa_bwd.restype = ctypes.c_int
         lib.fa_bwd.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_int,
                                ctypes.c_float, ctypes.c_int, ctypes.c_void_p])
+        lib.fa_bwd_ex.restype = ctypes.c_int
+        lib.fa_bwd_ex.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int64] * 5 + [ctypes.c_int, ctypes.c_int] +
+                                  [ctypes.c_int64] * 4 + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p])
         lib.fa_status_str.restype = ctypes.c_char_p
         lib.fa_status_str.argtypes = [ctypes.c_int]
         lib.fa_last_error.restype = ctypes.c_char_p
@@ -136,6 +145,14 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, D, layout, causal,
     return load().fa_bwd(q or None, k or None, v or None, o or None, lse or None, dout or None, dq or None,
                          dk or None, dv or None, delta or None, B, H, N, D, layout, int(causal), scale, dtype,
                          stream or None)
+
+
+def fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Nq, Nk, D, layout, causal, window, q_offset, kv_start,
+              kv_len, scale, dtype, stream) -> int:
+    """The generalised backward C entry point: pointers are ints (0 = NULL), returns the status code."""
+    return load().fa_bwd_ex(q or None, k or None, v or None, o or None, lse or None, dout or None, dq or None,
+                            dk or None, dv or None, delta or None, B, H, Nq, Nk, D, layout, int(causal), window,
+                            q_offset, kv_start, kv_len, scale, dtype, stream or None)
 
 
 def status_str(status: int) -> str:
@@ -340,3 +357,44 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, *, 
                             cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, total_q, total_k, int(max_seqlen_q),
                             D, causal, float(scale), _dtype_code(q), stream))
     return out, lse
+
+
+def attention_bwd_ex(q, k, v, o, lse, dout, *, layout: str = "BHSD", causal: bool = False, scale: float | None = None,
+                     window: int = -1, q_offset: int = 0, kv_start: int = 0, kv_len: int | None = None, dk=None,
+                     dv=None, delta=None):
+    """fa_bwd_ex for torch device tensors: q, o, dout [B,H,Nq,D] / [B,Nq,H,D]; k, v [B,H,Nk,D] / [B,Nk,H,D];
+    lse [B,H,Nq] of the forward over every key.  Returns (dq partial of the chunk, dk, dv)."""
+    import torch
+    if layout not in _LAYOUTS:
+        raise ValueError("layout must be 'BHSD' or 'BSND'")
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("q, o, dout must share a 4-D shape and k, v another")
+    if any(t.dtype != q.dtype for t in (k, v, o, dout)):
+        raise TypeError("q, k, v, o, dout must share a dtype")
+    for t in (q, k, v, o, dout):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v, o, dout must be contiguous in the given layout")
+    B, H, Nq, D = _bhnd(q, layout)
+    Bk, Hk, Nk, Dk = _bhnd(k, layout)
+    if (Bk, Hk, Dk) != (B, H, D):
+        raise ValueError("k and v must match q in B, H and D")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of shape [B, H, Nq]")
+    if kv_len is None:
+        kv_len = Nk - kv_start
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if delta is None:
+        delta = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    dq = torch.empty_like(q)
+    dk = torch.zeros_like(k) if dk is None else dk
+    dv = torch.zeros_like(v) if dv is None else dv
+    for t in (dk, dv):
+        if t.shape != k.shape or t.dtype != k.dtype or not t.is_contiguous():
+            raise ValueError("dk and dv must be contiguous tensors like k")
+    stream = torch.cuda.current_stream(q.device).cuda_stream if q.is_cuda else 0
+    _raise_on(fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, Nq, Nk, D,
+                        _LAYOUTS[layout], causal, int(window), int(q_offset), int(kv_start), int(kv_len),
+                        float(scale), _dtype_code(q), stream))
+    return dq, dk, dv

@@ -70,7 +70,7 @@ FA_API const char* fa_status_str(int status) {
 
 FA_API const char* fa_last_error(void) { return g_last_error; }
 
-FA_API int fa_version(void) { return 400; }  // 0.4.0
+FA_API int fa_version(void) { return 500; }  // 0.5.0
 
 FA_API int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                      int64_t Nq, int64_t Nk, int64_t D, int layout, int causal, int64_t window, int64_t q_offset,
@@ -283,32 +283,39 @@ FA_API int fa_merge(const void* o_parts, const float* lse_parts, int64_t n_parts
   return FA_OK;
 }
 
-FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-                  void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t N, int64_t D,
-                  int layout, int causal, float scale, int dtype, void* stream) {
+FA_API int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                     void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                     int64_t D, int layout, int causal, int64_t window, int64_t q_offset, int64_t kv_start,
+                     int64_t kv_len, float scale, int dtype, void* stream) {
   // ---- pure argument checks (no HIP calls) ----
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return FA_ERR_NULL;
   if (layout != FA_LAYOUT_BHSD && layout != FA_LAYOUT_BSND) return FA_ERR_BAD_LAYOUT;
   if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_BAD_DTYPE;
-  if (B < 1 || H < 1 || N < 1 || D < 1) return FA_ERR_BAD_DIM;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || D < 1) return FA_ERR_BAD_DIM;
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
   if (dtype == FA_DTYPE_FP32) return FA_ERR_UNSUPPORTED;
-  int64_t bh, rows, elems, bytes, row_bytes;
-  if (N > kMaxRows || !mul_ok(B, H, &bh) || bh > INT32_MAX || !mul_ok(bh, N, &rows) || !mul_ok(rows, D, &elems) ||
-      !mul_ok(elems, 2, &bytes) || !mul_ok(rows, 4, &row_bytes))
+  int64_t bh, rows_q, rows_k, elems_q, elems_k, bytes_q, bytes_k, row_bytes;
+  if (Nq > kMaxRows || Nk > kMaxRows || !mul_ok(B, H, &bh) || bh > INT32_MAX || !mul_ok(bh, Nq, &rows_q) ||
+      !mul_ok(bh, Nk, &rows_k) || !mul_ok(rows_q, D, &elems_q) || !mul_ok(rows_k, D, &elems_k) ||
+      !mul_ok(elems_q, 2, &bytes_q) || !mul_ok(elems_k, 2, &bytes_k) || !mul_ok(rows_q, 4, &row_bytes))
     return FA_ERR_UNSUPPORTED;
+  if (kv_start < 0 || kv_len < 0 || kv_start > Nk || kv_len > Nk - kv_start) return FA_ERR_BAD_RANGE;
+  if (window >= 0 && !causal) return FA_ERR_BAD_RANGE;
+  if (q_offset < -kMaxRows || q_offset > kMaxRows) return FA_ERR_BAD_RANGE;
   const int64_t rpw = fa::bwd_rows_per_workgroup();
-  if (bh * ((N + rpw - 1) / rpw) > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  if (bh * ((Nq + rpw - 1) / rpw) > INT32_MAX || bh * ((Nk + rpw - 1) / rpw) > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  // one head's rows of Q/dO and of K/V are addressed with 32-bit offsets from per-head buffer descriptors
   const int64_t stride_bytes = (layout == FA_LAYOUT_BHSD ? D : H * D) * 2;
-  if ((N - 1) * stride_bytes + D * 2 > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  if ((Nq - 1) * stride_bytes + D * 2 > INT32_MAX || (Nk - 1) * stride_bytes + D * 2 > INT32_MAX)
+    return FA_ERR_UNSUPPORTED;
   if (!isfinite(scale) || !isfinite(fabsf(scale) * 1.4426950408889634f)) return FA_ERR_BAD_SCALE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse | (uintptr_t)dout |
        (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)delta) & 15)
     return FA_ERR_MISALIGNED;
   const void* ins[6] = {q, k, v, o, lse, dout};
-  const int64_t in_bytes[6] = {bytes, bytes, bytes, bytes, row_bytes, bytes};
+  const int64_t in_bytes[6] = {bytes_q, bytes_k, bytes_k, bytes_q, row_bytes, bytes_q};
   const void* outs[4] = {dq, dk, dv, delta};
-  const int64_t out_bytes[4] = {bytes, bytes, bytes, row_bytes};
+  const int64_t out_bytes[4] = {bytes_q, bytes_k, bytes_k, row_bytes};
   for (int a = 0; a < 4; ++a) {
     for (int i = 0; i < 6; ++i)
       if (overlaps(outs[a], out_bytes[a], ins[i], in_bytes[i])) return FA_ERR_ALIAS;
@@ -347,14 +354,24 @@ FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, co
   p.delta = delta;
   p.B = (int)B;
   p.H = (int)H;
-  p.N = (int)N;
+  p.Nq = (int)Nq;
+  p.Nk = (int)Nk;
+  p.q_offset = q_offset;
+  // a window reaching before every key the queries could see hides nothing
+  p.window = (window < 0 || window >= q_offset + Nq) ? -1 : window;
+  p.kv_start = (int)kv_start;
+  p.kv_len = (int)kv_len;
   if (layout == FA_LAYOUT_BHSD) {
-    p.stride_b = H * N * D;
-    p.stride_h = N * D;
+    p.stride_b_q = H * Nq * D;
+    p.stride_h_q = Nq * D;
+    p.stride_b_k = H * Nk * D;
+    p.stride_h_k = Nk * D;
     p.stride_s = D;
   } else {
-    p.stride_b = N * H * D;
-    p.stride_h = D;
+    p.stride_b_q = Nq * H * D;
+    p.stride_h_q = D;
+    p.stride_b_k = Nk * H * D;
+    p.stride_h_k = D;
     p.stride_s = H * D;
   }
   p.c = scale * 1.4426950408889634f;
@@ -366,4 +383,16 @@ FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, co
     return FA_ERR_HIP;
   }
   return FA_OK;
+}
+
+FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t N, int64_t D,
+                  int layout, int causal, float scale, int dtype, void* stream) {
+  // N bounds the key range too, so a bad N reports as a dimension or size error, never as a range error
+  if (N < 1) return (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) ? FA_ERR_NULL
+                    : (layout != FA_LAYOUT_BHSD && layout != FA_LAYOUT_BSND) ? FA_ERR_BAD_LAYOUT
+                    : (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) ? FA_ERR_BAD_DTYPE
+                    : FA_ERR_BAD_DIM;
+  return fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, N, D, layout, causal, -1, 0, 0, N, scale,
+                   dtype, stream);
 }

@@ -105,7 +105,7 @@ __device__ __forceinline__ void lane_offsets(int li, int g, int (&rb)[BwdTile<D>
 // ------------------------------------------------------------------------------------------------
 // dQ (and D) : one workgroup per (b, h, 128-query tile)
 // ------------------------------------------------------------------------------------------------
-template <int D, bool IS_BF16, bool CAUSAL>
+template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW>
 __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
   typedef BwdTile<D> T;
   typedef Elem<IS_BF16> E;
@@ -123,22 +123,33 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, li = lane & 15;
   int bh, qt;
-  unit_of(blockIdx.x, p.n_units, p.n_tiles, CAUSAL, bh, qt);
+  unit_of(blockIdx.x, p.n_units_q, p.n_tiles_q, CAUSAL, bh, qt);
   const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
-  const int N = p.N;
+  const int Nq = p.Nq, Nk = p.Nk;
+  const int64_t qoff = p.q_offset, window = p.window;
+  const int kv0 = p.kv_start, kv1 = p.kv_start + p.kv_len;  // the key chunk [kv0, kv1)
   const int q_wg = qt * BM, q0 = q_wg + wave * QW;
-  const int64_t head = b * p.stride_b + h * p.stride_h;
+  const int64_t qhead = b * p.stride_b_q + h * p.stride_h_q;
+  const int64_t khead = b * p.stride_b_k + h * p.stride_h_k;
   const int64_t ss = p.stride_s;
 
-  // K/V tiles: keys 0 .. k_last
-  const int k_last = CAUSAL ? min(N - 1, q_wg + BM - 1) : N - 1;
-  const int n_kt = k_last / BN + 1;
+  // K/V tiles from k_lo: the chunk's keys that some query of this workgroup sees
+  const int k_lo = WINDOW ? (int)max((int64_t)kv0, q_wg + qoff - window) : kv0;
+  const int k_hi = CAUSAL ? (int)min((int64_t)kv1 - 1, q_wg + BM - 1 + qoff) : kv1 - 1;
+  const int n_kt = k_hi >= k_lo ? (k_hi - k_lo) / BN + 1 : 0;
+  // positions in 32 bits: the workgroup's first query position minus k_lo (and minus the window),
+  // clamped to +-2^26 once.  Rows and keys per head stay below 2^24 (the 32-bit buffer offsets), so
+  // past the clamp every slot of every tile is visible (or, for the window term, none is hidden)
+  // exactly as with the unclamped value.
+  const int64_t base64 = q_wg + qoff - k_lo;
+  const int rbase = (int)max((int64_t)-(1 << 26), min((int64_t)(1 << 26), base64));
+  const int wbase = WINDOW ? (int)max((int64_t)-(1 << 26), min((int64_t)(1 << 26), base64 - window)) : 0;
   const int row_bytes = (int)(2 * ss);
-  const int span = (N - 1) * row_bytes + T::ROW_BYTES;  // the host keeps this below 2^31
+  const int span = (Nk - 1) * row_bytes + T::ROW_BYTES;  // the host keeps this below 2^31
   const __amdgpu_buffer_rsrc_t kbuf =
-      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.k + head), 0, span, kBufferFlags);
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.k + khead), 0, span, kBufferFlags);
   const __amdgpu_buffer_rsrc_t vbuf =
-      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.v + head), 0, span, kBufferFlags);
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.v + khead), 0, span, kBufferFlags);
   int voff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
@@ -147,21 +158,21 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
     voff[i] = row * row_bytes + ((pc ^ T::swz(row)) << 4);
   }
   auto issue_tile = [&](int j, uint8_t* kdst, uint8_t* vdst) __attribute__((always_inline)) {
-    issue_kv_tile<LOADS, NW>(kbuf, vbuf, voff, voff, j * BN * row_bytes, wave, kdst, vdst);
+    issue_kv_tile<LOADS, NW>(kbuf, vbuf, voff, voff, (k_lo + j * BN) * row_bytes, wave, kdst, vdst);
   };
-  issue_tile(0, ks0, vs0);
+  if (n_kt > 0) issue_tile(0, ks0, vs0);
 
   // Q and dO fragments (B operands of S^T = K Q^T and dP^T = V dO^T): row q0 + 16*qg + li, d 32c+8g..+7.
   // D_i = sum_d dO_id O_id from the same fragment pattern of O, summed over the 4 lane groups.
-  const uint16_t* qp = (const uint16_t*)p.q + head;
-  const uint16_t* dop = (const uint16_t*)p.dout + head;
-  const uint16_t* op = (const uint16_t*)p.o + head;
+  const uint16_t* qp = (const uint16_t*)p.q + qhead;
+  const uint16_t* dop = (const uint16_t*)p.dout + qhead;
+  const uint16_t* op = (const uint16_t*)p.o + qhead;
   vec8 qf[QG][T::DC], df[QG][T::DC];
   float lse2[QG], dlt[QG];
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg) {
     const int qi = q0 + 16 * qg + li;
-    const int qrow = min(qi, N - 1);
+    const int qrow = min(qi, Nq - 1);
     float acc = 0.f;
 #pragma unroll
     for (int c = 0; c < T::DC; ++c) {
@@ -173,8 +184,8 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
       for (int x = 0; x < 8; ++x) acc = __builtin_fmaf(to_f32<IS_BF16>(df[qg][c], x), to_f32<IS_BF16>(of, x), acc);
     }
     dlt[qg] = wave_sum_xor16_32(acc);
-    lse2[qg] = p.lse[(int64_t)bh * N + qrow] * kLog2e;
-    if (g == 0 && qi < N) p.delta[(int64_t)bh * N + qi] = dlt[qg];
+    lse2[qg] = p.lse[(int64_t)bh * Nq + qrow] * kLog2e;
+    if (g == 0 && qi < Nq) p.delta[(int64_t)bh * Nq + qi] = dlt[qg];
   }
 
   const float cexp = p.c;  // scale * log2(e), signed
@@ -191,10 +202,14 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     lds_barrier();
     if constexpr (!decltype(last_c)::value) issue_tile(j + 1, kn, vn);
-    const int key0 = j * BN;
-    const bool active = !CAUSAL || key0 <= q0 + QW - 1;
+    const int key0 = k_lo + j * BN;
+    const int dpos = rbase + wave * QW - j * BN;  // the wave's first query position minus key0
+    const int dwin = wbase + wave * QW - j * BN;  // the same minus the window
+    // the wave's 32 queries see some key of this tile; element masks where the causal edge, the window
+    // edge or the chunk's end cross it
+    const bool active = (!CAUSAL || dpos + QW - 1 >= 0) && (!WINDOW || dwin <= BN - 1);
     if (active) {
-      const bool need_mask = (CAUSAL && key0 + BN - 1 > q0) || (key0 + BN > N);
+      const bool need_mask = (CAUSAL && dpos < BN - 1) || (key0 + BN > kv1) || (WINDOW && dwin + QW - 1 > 0);
       uint32_t dsf[QG][KC][4];
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
@@ -222,13 +237,19 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
           for (int r = 0; r < 4; ++r) a[qg][r] = __builtin_fmaf(s[qg][r], cexp, -lse2[qg]);
         if (need_mask) {
           keep_branch();
+          // clamped again: slots span fewer than 128 keys, so values past +-512 hide the same slots
+          const int dq0 = CAUSAL ? max(-512, min(512, dpos)) : 0;
+          const int dw0 = WINDOW ? max(-512, min(512, dwin)) : 0;
+          const int kend = kv1 - key0;  // slots from kend on lie past the chunk
 #pragma unroll
           for (int qg = 0; qg < QG; ++qg) {
-            const int qi = q0 + 16 * qg + li;
-            const int hi = (CAUSAL ? min(N - 1, qi) : N - 1) - key0 - 4 * g;  // slots 16*kt + r above: hidden
+            // visible slots of this query: [lo, hi] (tiles start at the chunk's first visible key, so
+            // only a window needs the lower edge; past the chunk the window is empty anyway)
+            const int hi = (CAUSAL ? min(kend - 1, dq0 + 16 * qg + li) : kend - 1) - 4 * g;
+            const int lo = WINDOW ? dw0 + 16 * qg + li - 4 * g : 0;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              if (16 * kt + r > hi) a[qg][r] = kNegInf;
+              if (16 * kt + r > hi || (WINDOW && 16 * kt + r < lo)) a[qg][r] = kNegInf;
           }
         }
 #pragma unroll
@@ -255,24 +276,27 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
 
   const std::integral_constant<bool, false> more;
   const std::integral_constant<bool, true> last;
-  int j = 0;
-  for (; j + 2 < n_kt; j += 2) {
-    step(j, ks0, vs0, ks1, vs1, more);
-    step(j + 1, ks1, vs1, ks0, vs0, more);
-  }
-  if (j + 2 == n_kt) {
-    step(j, ks0, vs0, ks1, vs1, more);
-    step(j + 1, ks1, vs1, ks0, vs0, last);
-  } else {
-    step(j, ks0, vs0, ks1, vs1, last);
+  if (n_kt > 0) {
+    int j = 0;
+    for (; j + 2 < n_kt; j += 2) {
+      step(j, ks0, vs0, ks1, vs1, more);
+      step(j + 1, ks1, vs1, ks0, vs0, more);
+    }
+    if (j + 2 == n_kt) {
+      step(j, ks0, vs0, ks1, vs1, more);
+      step(j + 1, ks1, vs1, ks0, vs0, last);
+    } else {
+      step(j, ks0, vs0, ks1, vs1, last);
+    }
   }
 
-  // dQ = scale * accumulated (dS K); lane holds d = 16*dt + 4*g + r of query q0 + 16*qg + li
-  uint16_t* dqp = (uint16_t*)p.dq + head;
+  // dQ = scale * accumulated (dS K) over the chunk's keys (0 when it sees none); lane holds d =
+  // 16*dt + 4*g + r of query q0 + 16*qg + li
+  uint16_t* dqp = (uint16_t*)p.dq + qhead;
 #pragma unroll
   for (int qg = 0; qg < QG; ++qg) {
     const int qi = q0 + 16 * qg + li;
-    if (qi < N) {
+    if (qi < Nq) {
 #pragma unroll
       for (int dt = 0; dt < T::DT; ++dt) {
         const f32x4_t x = dqa[qg][dt] * p.scale;
@@ -285,7 +309,7 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
 // ------------------------------------------------------------------------------------------------
 // dK, dV : one workgroup per (b, h, 128-key tile)
 // ------------------------------------------------------------------------------------------------
-template <int D, bool IS_BF16, bool CAUSAL, int NW, int KW, int MINB>
+template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW, int NW, int KW, int MINB>
 __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
   typedef BwdTile<D> T;
   typedef Elem<IS_BF16> E;
@@ -309,41 +333,55 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, li = lane & 15;
   int bh, kt;
-  unit_of(blockIdx.x, p.n_units, p.n_tiles, false, bh, kt);  // causal: key tile 0 (most queries) first
+  unit_of(blockIdx.x, p.n_units_k, p.n_tiles_k, false, bh, kt);  // causal: the chunk's first key tile first
   const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
-  const int N = p.N;
-  const int k_wg = kt * BK, kw0 = k_wg + wave * KW;
-  const int64_t head = b * p.stride_b + h * p.stride_h;
+  const int Nq = p.Nq;
+  const int64_t qoff = p.q_offset, window = p.window;
+  const int kv1 = p.kv_start + p.kv_len;  // keys of the chunk: [p.kv_start, kv1)
+  const int k_wg = p.kv_start + kt * BK, kw0 = k_wg + wave * KW;
+  const int64_t qhead = b * p.stride_b_q + h * p.stride_h_q;
+  const int64_t khead = b * p.stride_b_k + h * p.stride_h_k;
   const int64_t ss = p.stride_s;
 
   // K and V of the wave's keys as B operands of S = Q K^T and dP = dO V^T: lane holds key kw0 + 16*kg + li,
-  // d 32c + 8g .. +7; keys past the end are zero (their gradients are not stored)
-  const uint16_t* kp = (const uint16_t*)p.k + head;
-  const uint16_t* vp = (const uint16_t*)p.v + head;
+  // d 32c + 8g .. +7; keys past the chunk are zero (their gradients are not stored)
+  const uint16_t* kp = (const uint16_t*)p.k + khead;
+  const uint16_t* vp = (const uint16_t*)p.v + khead;
   vec8 kf[KG][T::DC], vf[KG][T::DC];
 #pragma unroll
   for (int kg = 0; kg < KG; ++kg) {
     const int key = kw0 + 16 * kg + li;
-    const int krow = min(key, N - 1);
+    const int krow = min(key, kv1 - 1);
 #pragma unroll
     for (int c = 0; c < T::DC; ++c) {
       const int64_t e = krow * ss + 32 * c + 8 * g;
       u32x4_t kr = *(const u32x4_t*)(kp + e), vr = *(const u32x4_t*)(vp + e);
-      if (key >= N) kr = vr = u32x4_t{0u, 0u, 0u, 0u};
+      if (key >= kv1) kr = vr = u32x4_t{0u, 0u, 0u, 0u};
       kf[kg][c] = __builtin_bit_cast(vec8, kr);
       vf[kg][c] = __builtin_bit_cast(vec8, vr);
     }
   }
 
-  // Q/dO tiles from the first one holding a query that sees a key of this workgroup
-  const int qt_begin = CAUSAL ? k_wg / BQ : 0;
-  const int n_qt = (N + BQ - 1) / BQ - qt_begin;
+  // Q/dO tiles of BQ rows from i_begin: the query rows that see some key of this workgroup (causal: from
+  // the first key's position; window: up to the last key's position plus the window)
+  const int i_begin = CAUSAL ? (int)min((int64_t)Nq, max((int64_t)0, k_wg - qoff)) : 0;
+  const int i_last = WINDOW ? (int)min((int64_t)Nq - 1, k_wg + BK - 1 + window - qoff) : Nq - 1;
+  const int n_qt = i_last >= i_begin ? (i_last - i_begin) / BQ + 1 : 0;
+  // positions in 32 bits: row 0's position minus k_wg, clamped to +-2^26 once, and the window
+  // corrected by what the clamp removed, clamped to +-2^27.  Rows per head stay below 2^24 (the
+  // 32-bit buffer offsets): past +2^26 every row sees every key causally, below -2^26 no row is
+  // processed, and the corrected window compares with the clamped positions as the window with the
+  // exact ones.
+  const int64_t rb64 = qoff - k_wg;
+  const int64_t rbc64 = max((int64_t)-(1 << 26), min((int64_t)(1 << 26), rb64));
+  const int rbase = (int)rbc64;
+  const int wv = WINDOW ? (int)max((int64_t)-(1 << 27), min((int64_t)(1 << 27), window - (rb64 - rbc64))) : 0;
   const int row_bytes = (int)(2 * ss);
-  const int span = (N - 1) * row_bytes + T::ROW_BYTES;
+  const int span = (Nq - 1) * row_bytes + T::ROW_BYTES;
   const __amdgpu_buffer_rsrc_t qbuf =
-      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.q + head), 0, span, kBufferFlags);
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.q + qhead), 0, span, kBufferFlags);
   const __amdgpu_buffer_rsrc_t obuf =
-      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.dout + head), 0, span, kBufferFlags);
+      __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.dout + qhead), 0, span, kBufferFlags);
   int voff[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
@@ -352,17 +390,17 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
     voff[i] = row * row_bytes + ((pc ^ T::swz(row)) << 4);
   }
   auto issue_tile = [&](int j, uint8_t* qdst, uint8_t* odst) __attribute__((always_inline)) {
-    issue_kv_tile<LOADS, NW>(qbuf, obuf, voff, voff, (qt_begin + j) * BQ * row_bytes, wave, qdst, odst);
+    issue_kv_tile<LOADS, NW>(qbuf, obuf, voff, voff, (i_begin + j * BQ) * row_bytes, wave, qdst, odst);
   };
-  issue_tile(0, qs0, os0);
+  if (n_qt > 0) issue_tile(0, qs0, os0);
 
   const float cexp = p.c;
-  const float* lse_h = p.lse + (int64_t)bh * N;
-  const float* dlt_h = p.delta + (int64_t)bh * N;
+  const float* lse_h = p.lse + (int64_t)bh * Nq;
+  const float* dlt_h = p.delta + (int64_t)bh * Nq;
   // row values of tile jt for this lane's row (wave 0 only)
   auto load_rows = [&](int jt, float& l2v, float& dv) __attribute__((always_inline)) {
-    const int qi = (qt_begin + jt) * BQ + lane;
-    if (qi < N) {
+    const int qi = i_begin + jt * BQ + lane;
+    if (qi < Nq) {
       l2v = lse_h[qi] * kLog2e;
       dv = dlt_h[qi];
     } else {
@@ -370,7 +408,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
       dv = 0.f;
     }
   };
-  if (wave == 0) {
+  if (wave == 0 && n_qt > 0) {
     float a, d;
     load_rows(0, a, d);
     rv0[lane] = a;
@@ -398,13 +436,20 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
       if (wave == 0) load_rows(j + 1, nl, nd);
       issue_tile(j + 1, qn, on);
     }
-    const int tile0 = (qt_begin + j) * BQ;
+    const int tile0 = i_begin + j * BQ;
 #pragma unroll
     for (int hh = 0; hh < BQ / QS; ++hh) {
-      const int qh0 = tile0 + QS * hh;  // first query of this step
-      const bool active = qh0 < N && (!CAUSAL || qh0 + QS - 1 >= kw0);
+      const int qh0 = tile0 + QS * hh;  // first query row of this step
+      const int c = qh0 + rbase - wave * KW;  // its position minus the wave's first key
+      // some query of the step sees some key of the wave (causal: the last query is not before the
+      // first key; window: the first query is not past the last key's window)
+      const bool active = qh0 < Nq && (!CAUSAL || c + QS - 1 >= 0) && (!WINDOW || c <= KW - 1 + wv);
       if (active) {
-        const bool need_mask = CAUSAL && qh0 < kw0 + KW - 1;
+        const bool need_mask = (CAUSAL && c < KW - 1) || (WINDOW && c + QS - 1 > wv);
+        // the wave's first key minus the step's first row position (plus the window), clamped: lanes
+        // span fewer than 64 keys and rows, so values past +-512 hide the same rows
+        const int dk0 = CAUSAL ? max(-512, min(512, -c)) : 0;
+        const int dkw = WINDOW ? max(-512, min(512, wv - c)) : 0;
         uint32_t pp[KG][4], dsp[KG][4];
 #pragma unroll
         for (int qq = 0; qq < QGS; ++qq) {
@@ -436,10 +481,14 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
             keep_branch();
 #pragma unroll
             for (int kg = 0; kg < KG; ++kg) {
-              const int lo = kw0 + 16 * kg + li - (qh0 + 16 * qq + 4 * g);  // rows r < lo: query before key
+              // the lane's key minus its first row's position is rel = dk0 + 16 kg + li - 16 qq - 4 g;
+              // hidden rows r: before the key (r < rel, causal) or more than `window` after it
+              const int rl = 16 * kg + li - 16 * qq - 4 * g;
+              const int lo = CAUSAL ? max(-1, min(4, dk0 + rl)) : -1;  // rows r < lo
+              const int hi = WINDOW ? max(-1, min(4, dkw + rl)) : 4;   // rows r > hi
 #pragma unroll
               for (int r = 0; r < 4; ++r)
-                if (r < lo) a[kg][r] = kNegInf;
+                if (r < lo || r > hi) a[kg][r] = kNegInf;
             }
           }
 #pragma unroll
@@ -479,25 +528,28 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
 
   const std::integral_constant<bool, false> more;
   const std::integral_constant<bool, true> last;
-  int j = 0;
-  for (; j + 2 < n_qt; j += 2) {
-    step(j, qs0, os0, rv0, qs1, os1, rv1, more);
-    step(j + 1, qs1, os1, rv1, qs0, os0, rv0, more);
-  }
-  if (j + 2 == n_qt) {
-    step(j, qs0, os0, rv0, qs1, os1, rv1, more);
-    step(j + 1, qs1, os1, rv1, qs0, os0, rv0, last);
-  } else {
-    step(j, qs0, os0, rv0, qs1, os1, rv1, last);
+  if (n_qt > 0) {
+    int j = 0;
+    for (; j + 2 < n_qt; j += 2) {
+      step(j, qs0, os0, rv0, qs1, os1, rv1, more);
+      step(j + 1, qs1, os1, rv1, qs0, os0, rv0, more);
+    }
+    if (j + 2 == n_qt) {
+      step(j, qs0, os0, rv0, qs1, os1, rv1, more);
+      step(j + 1, qs1, os1, rv1, qs0, os0, rv0, last);
+    } else {
+      step(j, qs0, os0, rv0, qs1, os1, rv1, last);
+    }
   }
 
-  // dK = scale * accumulated (dS^T Q), dV: lane holds d = 16*dt + 4*g + r of key kw0 + 16*kg + li
-  uint16_t* dkp = (uint16_t*)p.dk + head;
-  uint16_t* dvp = (uint16_t*)p.dv + head;
+  // dK = scale * accumulated (dS^T Q), dV (0 for keys no query sees): lane holds d = 16*dt + 4*g + r of
+  // key kw0 + 16*kg + li; rows outside the chunk are left as they are
+  uint16_t* dkp = (uint16_t*)p.dk + khead;
+  uint16_t* dvp = (uint16_t*)p.dv + khead;
 #pragma unroll
   for (int kg = 0; kg < KG; ++kg) {
     const int key = kw0 + 16 * kg + li;
-    if (key < N) {
+    if (key < kv1) {
 #pragma unroll
       for (int dt = 0; dt < T::DT; ++dt) {
         const f32x4_t x = dka[kg][dt] * p.scale;
@@ -509,21 +561,24 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
   }
 }
 
-template <int D, bool IS_BF16, bool CAUSAL>
+template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW>
 hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
-  p.n_tiles = (p.N + 127) / 128;
-  p.n_units = p.B * p.H * p.n_tiles;
-  hipLaunchKernelGGL((fa_bwd_dq<D, IS_BF16, CAUSAL>), dim3(p.n_units), dim3(256), 0, stream, p);
+  p.n_tiles_q = (p.Nq + 127) / 128;
+  p.n_units_q = p.B * p.H * p.n_tiles_q;
+  p.n_tiles_k = (p.kv_len + 127) / 128;
+  p.n_units_k = p.B * p.H * p.n_tiles_k;
+  hipLaunchKernelGGL((fa_bwd_dq<D, IS_BF16, CAUSAL, WINDOW>), dim3(p.n_units_q), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa_bwd_dkdv<D, IS_BF16, CAUSAL, kDkdvWaves, kDkdvKeys, kDkdvMinBlocks>), dim3(p.n_units),
-                     dim3(64 * kDkdvWaves), 0, stream, p);
+  if (e != hipSuccess || p.n_units_k == 0) return e;
+  hipLaunchKernelGGL((fa_bwd_dkdv<D, IS_BF16, CAUSAL, WINDOW, kDkdvWaves, kDkdvKeys, kDkdvMinBlocks>),
+                     dim3(p.n_units_k), dim3(64 * kDkdvWaves), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D, bool IS_BF16>
 hipError_t launch_bwd_c(const BwdParams& p, bool causal, hipStream_t stream) {
-  return causal ? launch_bwd_t<D, IS_BF16, true>(p, stream) : launch_bwd_t<D, IS_BF16, false>(p, stream);
+  if (!causal) return launch_bwd_t<D, IS_BF16, false, false>(p, stream);
+  return p.window >= 0 ? launch_bwd_t<D, IS_BF16, true, true>(p, stream) : launch_bwd_t<D, IS_BF16, true, false>(p, stream);
 }
 
 }  // namespace
