@@ -12,7 +12,7 @@
 #include <string.h>
 
 #include "../../include/fa.h"
-#include "fa_launch.h"
+#include "fa_bwd_launch.h"
 
 #define FA_API extern "C" __attribute__((visibility("default")))
 

@@ -32,7 +32,7 @@
 #include <type_traits>
 
 #include "fa_device.h"
-#include "fa_launch.h"
+#include "fa_bwd_launch.h"
 
 namespace fa {
 namespace {

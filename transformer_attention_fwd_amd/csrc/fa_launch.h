@@ -1,4 +1,5 @@
-// fa_launch.h -- internal interface between the C-ABI entry point and the kernels (not installed).
+// fa_launch.h -- internal interface between the C-ABI entry point and the forward and merge kernels
+// (not installed).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -42,33 +43,6 @@ struct Params {
   int64_t total_q, total_k;
 };
 
-// Backward kernel arguments.  Query row i sits at position q_offset + i and key row j at j; key j is
-// visible to query i iff (causal) j <= q_offset + i and (window >= 0) j >= q_offset + i - window.  The
-// key chunk [kv_start, kv_start + kv_len) bounds the keys dQ sums over and the dK/dV rows written.
-// Q, O, dO, dQ rows: base b*stride_b_q + h*stride_h_q; K, V, dK, dV: b*stride_b_k + h*stride_h_k;
-// consecutive rows stride_s apart (elements).
-struct BwdParams {
-  const void* q;
-  const void* k;
-  const void* v;
-  const void* o;
-  const float* lse;   // [B][H][Nq], natural log, of the forward over every visible key
-  const void* dout;
-  void* dq;
-  void* dk;
-  void* dv;
-  float* delta;       // [B][H][Nq] workspace: D_i = sum_d dO_id O_id, written by the dQ kernel
-  int64_t stride_b_q, stride_h_q, stride_b_k, stride_h_k, stride_s;
-  int64_t q_offset;
-  int64_t window;     // < 0: no window
-  int B, H, Nq, Nk;
-  int kv_start, kv_len;
-  int n_tiles_q, n_units_q;  // filled by the launcher
-  int n_tiles_k, n_units_k;  // filled by the launcher
-  float c;            // scale * log2(e), signed
-  float scale;
-};
-
 // Enqueue the attention kernel for (dtype, d, causal, window >= 0) on `stream`.
 hipError_t launch(const Params& p, int dtype, int d, bool causal, hipStream_t stream);
 
@@ -78,13 +52,6 @@ hipError_t launch_varlen(const Params& p, int dtype, int d, bool causal, hipStre
 // Enqueue the combination of n_parts partial results (see fa_merge in fa.h).
 hipError_t launch_merge(const void* o_parts, const float* lse_parts, int n_parts, void* o, float* lse, int64_t rows,
                         int64_t B, int64_t H, int64_t N, int D, int layout_bsnd, int dtype, hipStream_t stream);
-
-// Enqueue the two backward kernels (dQ and D, then dK and dV) for a 16-bit dtype on `stream`; a
-// window is used only with causal.
-hipError_t launch_bwd(const BwdParams& p, int dtype, int d, bool causal, hipStream_t stream);
-
-// Query (and key) rows handled by one backward workgroup.
-int bwd_rows_per_workgroup();
 
 // Queries handled by one workgroup for a dtype (for callers that size grids or count work).
 int queries_per_workgroup(int dtype);
