@@ -325,20 +325,22 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
                              (WINDOW && key0 < q0 + T::QW - 1 + delta - window);
       if (need_mask) {
         keep_branch();
+        // the wave's first query position minus key0 (and minus the window), once per tile in 64 bits,
+        // clamped: the slots span fewer than 64 keys, so values past +-512 hide the same slots
+        const int dq0 = CAUSAL ? (int)max((int64_t)-512, min((int64_t)512, q0 + delta - key0)) : 0;
+        const int dw0 = WINDOW ? (int)max((int64_t)-512, min((int64_t)512, q0 + delta - window - key0)) : 0;
+        const int kend = min(512, Nkv - key0);  // slots from kend on lie past the chunk
 #pragma unroll
         for (int qg = 0; qg < T::QG; ++qg) {
-          const int qi = q0 + 16 * qg + li;
-          // valid keys of this query lie in [klo, khi] (clamped to the chunk); valid slots 16*kt + r
-          // (key key0 + 16*kt + 4*g + r) in [lo, hi]
-          const int khi = CAUSAL ? (int)max((int64_t)-1, min((int64_t)Nkv - 1, qi + delta)) : Nkv - 1;
-          const int klo = WINDOW ? (int)min((int64_t)Nkv, max((int64_t)0, qi + delta - window)) : 0;
-          const int hi = khi - key0 - 4 * g;
-          const int lo = klo - key0 - 4 * g;
+          // visible slots 16*kt + r (key key0 + 16*kt + 4*g + r) of this lane's query: up to hi (causal
+          // edge or chunk end) and, with a window, from lo; keys before the chunk are never in a tile
+          const int hi = (CAUSAL ? min(kend - 1, dq0 + 16 * qg + li) : kend - 1) - 4 * g;
+          const int lo = WINDOW ? dw0 + 16 * qg + li - 4 * g : 0;
 #pragma unroll
           for (int kt = 0; kt < T::KT; ++kt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              if (16 * kt + r > hi || 16 * kt + r < lo) s[qg][kt][r] = kNegInf;
+              if (16 * kt + r > hi || (WINDOW && 16 * kt + r < lo)) s[qg][kt][r] = kNegInf;
         }
       }
       // P = exp2(c s - m_ref) against the current reference maximum; valid while no probability exceeds
