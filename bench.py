@@ -26,7 +26,9 @@ Options: --gpus N (only 1 is supported), --steps K, --warmup W, --no-cpu-baselin
            lengths are drawn uniformly from [512, 7680] (mean 4096: the C3 batch as a length mix),
          or c3_bwd: one step = one fa_bwd (dQ, dK, dV) on the C3 tensors with a seeded upstream gradient
            (O and lse from one fa_fwd before timing).  FLOP per step = the five products of the backward
-           (recomputed S, dP, dV, dK, dQ) over the visible pairs, 10*D per pair = 2.5 x the forward's.
+           (recomputed S, dP, dV, dK, dQ) over the visible pairs, 10*D per pair = 2.5 x the forward's,
+         or c3_bwd_window1024: the same through fa_bwd_ex with a sliding window of 1024 earlier keys
+           (O and lse from fa_fwd_ex with that window).
 """
 from __future__ import annotations
 
@@ -99,8 +101,8 @@ def main():
     import transformer_attention_fwd_amd as fa
     from transformer_attention_fwd_amd import inputs
 
-    if args.workload == "c3_bwd":
-        return bench_bwd(args)
+    if args.workload in ("c3_bwd", "c3_bwd_window1024"):
+        return bench_bwd(args, window=1024 if args.workload == "c3_bwd_window1024" else -1)
     if args.workload == "varlen":
         return bench_varlen(args)
     if args.workload in VARIANTS:
@@ -398,8 +400,8 @@ def bench_varlen(args):
     print(json.dumps(line), flush=True)
 
 
-def bench_bwd(args):
-    """One step = fa_bwd over the C3 batch; see the module notes."""
+def bench_bwd(args, window=-1):
+    """One step = fa_bwd (window < 0) or fa_bwd_ex with that window over the C3 batch; see the module notes."""
     import numpy as np
     import torch
 
@@ -413,16 +415,21 @@ def bench_bwd(args):
     doh = inputs.make_grad(B, H, N, D, layout=w.layout, dtype="bf16", seed=w.seed)
     to_dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda")
     q, k, v, do = to_dev(qh), to_dev(kh), to_dev(vh), to_dev(doh)
-    o, lse = fa.attention(q, k, v, layout=w.layout, causal=True, scale=w.scale)
+    o, lse = fa.attention_ex(q, k, v, layout=w.layout, causal=True, scale=w.scale, window=window)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     layout = fa.LAYOUT_BHSD
 
     def step():
-        st = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
-                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, D, layout, True,
-                       w.scale, fa.DTYPE_BF16, stream.cuda_stream)
+        if window < 0:
+            st = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, D, layout, True,
+                           w.scale, fa.DTYPE_BF16, stream.cuda_stream)
+        else:
+            st = fa.fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                              do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H,
+                              N, N, D, layout, True, window, 0, 0, N, w.scale, fa.DTYPE_BF16, stream.cuda_stream)
         if st != fa.FA_OK:
             raise RuntimeError("fa_bwd failed: %s %s" % (fa.status_str(st), fa.last_error()))
 
@@ -441,7 +448,7 @@ def bench_bwd(args):
     t1 = time.perf_counter()
     call_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
     ms_per_step = ev[0][0].elapsed_time(ev[-1][1]) / args.steps
-    pairs = float(B * H * visible_keys(N, N, 0, -1).sum())
+    pairs = float(B * H * visible_keys(N, N, 0, window).sum())
     flops = 10.0 * D * pairs
     value = flops / (ms_per_step * 1e-3) / 1e12
     mean_ms = float(np.mean(call_ms))
@@ -450,7 +457,8 @@ def bench_bwd(args):
         % (args.steps, ms_per_step, (t1 - t0) * 1e3 / args.steps, float(np.median(call_ms)), min(call_ms), value))
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "kernel": "fa_bwd_dq<128,bf16,causal> + fa_bwd_dkdv<128,bf16,causal> (one fa_bwd call)",
+                "kernel": ("fa_bwd_dq<128,bf16,causal> + fa_bwd_dkdv<128,bf16,causal> (one fa_bwd call)" if window < 0
+                           else "fa_bwd_dq<128,bf16,causal,window> + fa_bwd_dkdv<128,bf16,causal,window> (one fa_bwd_ex call)"),
                 "mean_launch_ms": round(mean_ms, 5), "launches_per_step": 2}
 
     cpu_baseline = None
@@ -465,8 +473,8 @@ def bench_bwd(args):
         while len(heads) < len(order) and (t_cpu < 10.0 or not heads):
             hd = order[len(heads)]
             t_a = time.perf_counter()
-            r = oracle.attention_bwd(qh, kh, vh, doh, dtype="bf16", layout=w.layout, causal=True, scale=w.scale,
-                                     heads=[hd], nthreads=cores)
+            r = oracle.attention_bwd_ex(qh, kh, vh, doh, dtype="bf16", layout=w.layout, causal=True, scale=w.scale,
+                                        window=window, heads=[hd], nthreads=cores)
             t_cpu += time.perf_counter() - t_a
             heads.append(hd)
             ref.append([x[0] for x in r])
@@ -486,7 +494,8 @@ def bench_bwd(args):
         log("bench: oracle %d heads in %.2f s on %d threads; parity %s" % (len(heads), t_cpu, cores, parity))
 
     line = {
-        "metric": "attention bwd TFLOP/s (dQ, dK, dV), causal B=8 H=32 N=4096 D=128",
+        "metric": "attention bwd TFLOP/s (dQ, dK, dV), causal B=8 H=32 N=4096 D=128"
+                  + ("" if window < 0 else ", window %d" % window),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -498,9 +507,10 @@ def bench_bwd(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "causal attention backward bf16 B=%d H=%d N=%d D=%d %s" % (B, H, N, D, w.layout),
+        "config": {"workload": "causal attention backward bf16 B=%d H=%d N=%d D=%d %s%s"
+                               % (B, H, N, D, w.layout, "" if window < 0 else " window %d" % window),
                    "B": B, "H": H, "N": N, "D": D, "layout": w.layout, "causal": True, "scale": w.scale,
-                   "flop_per_step": flops},
+                   "window": window, "flop_per_step": flops},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline,
         "cpu_baseline": cpu_baseline,
