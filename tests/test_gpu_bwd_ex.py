@@ -144,6 +144,19 @@ def test_rows_past_the_window_see_no_key():
     assert bool(torch.isneginf(lse[:, :, 60:]).all())
 
 
+@pytest.mark.parametrize("q_offset,window,chunks", [
+    (1 << 30, -1, [(0, 300)]),                      # every key visible to every query
+    (1 << 30, (1 << 30) - 100, [(0, 140), (140, 300)]),  # a window of 2^30 - 100 starting inside the keys
+    (1 << 30, 500, [(0, 300)]),                     # the window reaches no key: all gradients 0
+    (-(1 << 30), -1, [(0, 300)]),                   # every query before every key: all gradients 0
+])
+def test_offsets_at_the_limits(q_offset, window, chunks):
+    # |q_offset| = 2^30 is the largest the entry point accepts; positions then need more than 31 bits
+    # in the kernels' per-workgroup arithmetic before the clamps
+    compare_chunks(1, 2, 70, 300, 128, window=window, q_offset=q_offset, chunks=chunks, seed=12,
+                   what="bwd_ex limits")
+
+
 def test_rows_outside_the_chunk_untouched_and_empty_chunk():
     B, H, Nq, Nk, D = 1, 2, 160, 400, 128
     q, k, v, do = make_case(B, H, Nq, Nk, D, "bf16", "BHSD", 9)

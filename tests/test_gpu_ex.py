@@ -102,6 +102,12 @@ def test_sliding_window(dtype, window, D):
     dict(nq=257, nk=257, q_offset=0, kv_start=200, kv_len=57, window=-1),
     dict(nq=64, nk=512, q_offset=-40, kv_start=0, kv_len=512, window=-1),
     dict(nq=33, nk=200, q_offset=150, kv_start=0, kv_len=0, window=-1),
+    # offsets at the limits the entry point accepts (+-2^30): every key visible, a window of 2^30 - 100
+    # that starts inside the chunk, a window that reaches no key, and queries before every key
+    dict(nq=70, nk=300, q_offset=1 << 30, kv_start=0, kv_len=300, window=-1),
+    dict(nq=70, nk=300, q_offset=1 << 30, kv_start=40, kv_len=200, window=(1 << 30) - 100),
+    dict(nq=70, nk=300, q_offset=1 << 30, kv_start=0, kv_len=300, window=500),
+    dict(nq=70, nk=300, q_offset=-(1 << 30), kv_start=0, kv_len=300, window=-1),
 ])
 def test_offsets_chunks_windows_combined(dtype, case):
     D = 64
