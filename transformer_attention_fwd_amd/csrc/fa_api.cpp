@@ -388,11 +388,7 @@ FA_API int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
 FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                   void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t N, int64_t D,
                   int layout, int causal, float scale, int dtype, void* stream) {
-  // N bounds the key range too, so a bad N reports as a dimension or size error, never as a range error
-  if (N < 1) return (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) ? FA_ERR_NULL
-                    : (layout != FA_LAYOUT_BHSD && layout != FA_LAYOUT_BSND) ? FA_ERR_BAD_LAYOUT
-                    : (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) ? FA_ERR_BAD_DTYPE
-                    : FA_ERR_BAD_DIM;
+  // the whole key range: a bad N is reported by the dimension and size checks, which come first
   return fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, N, D, layout, causal, -1, 0, 0, N, scale,
                    dtype, stream);
 }
