@@ -28,7 +28,8 @@ Options: --gpus N (only 1 is supported), --steps K, --warmup W, --no-cpu-baselin
            (O and lse from one fa_fwd before timing).  FLOP per step = the five products of the backward
            (recomputed S, dP, dV, dK, dQ) over the visible pairs, 10*D per pair = 2.5 x the forward's,
          or c3_bwd_window1024: the same through fa_bwd_ex with a sliding window of 1024 earlier keys
-           (O and lse from fa_fwd_ex with that window).
+           (O and lse from fa_fwd_ex with that window),
+         or c3_bwd_fp32: fa_bwd on the C3 draws kept in fp32 (roofline against the fp32 MFMA peak).
 """
 from __future__ import annotations
 
@@ -45,6 +46,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s + % of bf16 MFMA peak, causal B=8 H=32 N=4096 D=128"
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_TFLOPS = 157.3  # dense fp32 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_fwd_c3.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "transformer_attention_fwd_amd", "csrc", f)
                   for f in ("fa_kernels.hip", "fa_device.h", "fa_launch.h")]
@@ -101,8 +103,9 @@ def main():
     import transformer_attention_fwd_amd as fa
     from transformer_attention_fwd_amd import inputs
 
-    if args.workload in ("c3_bwd", "c3_bwd_window1024"):
-        return bench_bwd(args, window=1024 if args.workload == "c3_bwd_window1024" else -1)
+    if args.workload in ("c3_bwd", "c3_bwd_window1024", "c3_bwd_fp32"):
+        return bench_bwd(args, window=1024 if args.workload == "c3_bwd_window1024" else -1,
+                         dtype="fp32" if args.workload == "c3_bwd_fp32" else "bf16")
     if args.workload == "varlen":
         return bench_varlen(args)
     if args.workload in VARIANTS:
@@ -400,7 +403,7 @@ def bench_varlen(args):
     print(json.dumps(line), flush=True)
 
 
-def bench_bwd(args, window=-1):
+def bench_bwd(args, window=-1, dtype="bf16"):
     """One step = fa_bwd (window < 0) or fa_bwd_ex with that window over the C3 batch; see the module notes."""
     import numpy as np
     import torch
@@ -411,9 +414,14 @@ def bench_bwd(args, window=-1):
     w = inputs.WORKLOADS["c3"]
     B, H, N, D = w.B, w.H, w.N, w.D
     log("bench: generating c3 inputs and dO %s" % ((B, H, N, D),))
-    qh, kh, vh = inputs.make_workload(w)
-    doh = inputs.make_grad(B, H, N, D, layout=w.layout, dtype="bf16", seed=w.seed)
-    to_dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda")
+    qh, kh, vh = inputs.make_workload(w, dtype)
+    doh = inputs.make_grad(B, H, N, D, layout=w.layout, dtype=dtype, seed=w.seed)
+    if dtype == "fp32":
+        to_dev = lambda x: torch.from_numpy(x).to("cuda")
+    else:
+        to_dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda")
+    dcode = fa.DTYPE_FP32 if dtype == "fp32" else fa.DTYPE_BF16
+    peak = PEAK_FP32_TFLOPS if dtype == "fp32" else PEAK_BF16_TFLOPS
     q, k, v, do = to_dev(qh), to_dev(kh), to_dev(vh), to_dev(doh)
     o, lse = fa.attention_ex(q, k, v, layout=w.layout, causal=True, scale=w.scale, window=window)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -425,11 +433,11 @@ def bench_bwd(args, window=-1):
         if window < 0:
             st = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, D, layout, True,
-                           w.scale, fa.DTYPE_BF16, stream.cuda_stream)
+                           w.scale, dcode, stream.cuda_stream)
         else:
             st = fa.fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                               do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H,
-                              N, N, D, layout, True, window, 0, 0, N, w.scale, fa.DTYPE_BF16, stream.cuda_stream)
+                              N, N, D, layout, True, window, 0, 0, N, w.scale, dcode, stream.cuda_stream)
         if st != fa.FA_OK:
             raise RuntimeError("fa_bwd failed: %s %s" % (fa.status_str(st), fa.last_error()))
 
@@ -455,10 +463,12 @@ def bench_bwd(args, window=-1):
     achieved = flops / (mean_ms * 1e-3) / 1e12
     log("bench: %d steps, %.4f ms/step (wall %.4f), fa_bwd median %.4f ms best %.4f ms, %.1f TFLOP/s"
         % (args.steps, ms_per_step, (t1 - t0) * 1e3 / args.steps, float(np.median(call_ms)), min(call_ms), value))
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "kernel": ("fa_bwd_dq<128,bf16,causal> + fa_bwd_dkdv<128,bf16,causal> (one fa_bwd call)" if window < 0
-                           else "fa_bwd_dq<128,bf16,causal,window> + fa_bwd_dkdv<128,bf16,causal,window> (one fa_bwd_ex call)"),
+    kern = ("fa_bwd_dq<128,bf16,causal> + fa_bwd_dkdv<128,bf16,causal> (one fa_bwd call)" if window < 0
+            else "fa_bwd_dq<128,bf16,causal,window> + fa_bwd_dkdv<128,bf16,causal,window> (one fa_bwd_ex call)")
+    if dtype == "fp32":
+        kern = "fa_bwd_dq32<128,causal> + fa_bwd_dkdv32<128,causal> (one fa_bwd call)"
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None, "kernel": kern,
                 "mean_launch_ms": round(mean_ms, 5), "launches_per_step": 2}
 
     cpu_baseline = None
@@ -473,7 +483,7 @@ def bench_bwd(args, window=-1):
         while len(heads) < len(order) and (t_cpu < 10.0 or not heads):
             hd = order[len(heads)]
             t_a = time.perf_counter()
-            r = oracle.attention_bwd_ex(qh, kh, vh, doh, dtype="bf16", layout=w.layout, causal=True, scale=w.scale,
+            r = oracle.attention_bwd_ex(qh, kh, vh, doh, dtype=dtype, layout=w.layout, causal=True, scale=w.scale,
                                         window=window, heads=[hd], nthreads=cores)
             t_cpu += time.perf_counter() - t_a
             heads.append(hd)
@@ -495,7 +505,7 @@ def bench_bwd(args, window=-1):
 
     line = {
         "metric": "attention bwd TFLOP/s (dQ, dK, dV), causal B=8 H=32 N=4096 D=128"
-                  + ("" if window < 0 else ", window %d" % window),
+                  + ("" if window < 0 else ", window %d" % window) + ("" if dtype == "bf16" else ", " + dtype),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -505,10 +515,10 @@ def bench_bwd(args, window=-1):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": "causal attention backward bf16 B=%d H=%d N=%d D=%d %s%s"
-                               % (B, H, N, D, w.layout, "" if window < 0 else " window %d" % window),
+        "config": {"workload": "causal attention backward %s B=%d H=%d N=%d D=%d %s%s"
+                               % (dtype, B, H, N, D, w.layout, "" if window < 0 else " window %d" % window),
                    "B": B, "H": H, "N": N, "D": D, "layout": w.layout, "causal": True, "scale": w.scale,
                    "window": window, "flop_per_step": flops},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),

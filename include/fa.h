@@ -173,7 +173,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  * dq, dk, dv: outputs, shaped like q, in `dtype`; fully overwritten.
  * delta : caller-owned fp32 workspace of B*H*N floats; on return it holds D_i = sum_d dout_id o_id.
  * Outputs and workspace must not overlap each other or any input.
- * dtype : FA_DTYPE_FP16 or FA_DTYPE_BF16 (FA_DTYPE_FP32 returns FA_ERR_UNSUPPORTED).  D in {64, 128}.
+ * dtype : FA_DTYPE_FP32, FA_DTYPE_FP16 or FA_DTYPE_BF16 (fp32: fp32 MFMA end to end).  D in {64, 128}.
  * The call enqueues two kernels on `stream`; results are valid after the stream synchronises.  The
  * library allocates nothing.  Check order and error codes as fa_fwd.
  */

@@ -190,7 +190,9 @@ def _call_b(**kw):
     (dict(q=0), fa.FA_ERR_NULL), (dict(do=0), fa.FA_ERR_NULL), (dict(delta=0), fa.FA_ERR_NULL),
     (dict(dv=0), fa.FA_ERR_NULL), (dict(layout=2), fa.FA_ERR_BAD_LAYOUT), (dict(dtype=5), fa.FA_ERR_BAD_DTYPE),
     (dict(N=0), fa.FA_ERR_BAD_DIM), (dict(B=0), fa.FA_ERR_BAD_DIM), (dict(D=96), fa.FA_ERR_UNSUPPORTED),
-    (dict(dtype=0), fa.FA_ERR_UNSUPPORTED), (dict(N=(1 << 30) + 1), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=(1 << 30) + 1), fa.FA_ERR_UNSUPPORTED),
+    # fp32: 4-byte elements, so dk 16 KiB after dq (clear of 2 x 64 x 64 bf16 elements) overlaps it
+    (dict(dtype=0, dk=DQ + 2 * 64 * 64 * 2), fa.FA_ERR_ALIAS),
     (dict(scale=float("inf")), fa.FA_ERR_BAD_SCALE), (dict(dk=DK + 2), fa.FA_ERR_MISALIGNED),
     (dict(delta=L + 4), fa.FA_ERR_MISALIGNED),
     (dict(dq=Q), fa.FA_ERR_ALIAS), (dict(dk=O + 64 * 2), fa.FA_ERR_ALIAS), (dict(dv=DO), fa.FA_ERR_ALIAS),
@@ -250,7 +252,7 @@ def _call_bx(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(dk=0), fa.FA_ERR_NULL), (dict(Nk=0), fa.FA_ERR_BAD_DIM), (dict(Nq=0), fa.FA_ERR_BAD_DIM),
-    (dict(dtype=0), fa.FA_ERR_UNSUPPORTED), (dict(kv_start=-1), fa.FA_ERR_BAD_RANGE),
+    (dict(kv_start=-1), fa.FA_ERR_BAD_RANGE),
     (dict(kv_start=60, kv_len=41), fa.FA_ERR_BAD_RANGE), (dict(causal=0, window=4), fa.FA_ERR_BAD_RANGE),
     (dict(q_offset=(1 << 30) + 1), fa.FA_ERR_BAD_RANGE), (dict(D=80, kv_start=-1), fa.FA_ERR_UNSUPPORTED),
     (dict(dv=V + 32), fa.FA_ERR_ALIAS), (dict(delta=L + 8), fa.FA_ERR_MISALIGNED),
@@ -261,4 +263,6 @@ def test_fa_bwd_ex_argument_checks(kw, status):
 
 def test_fa_bwd_ex_good_arguments_reach_the_device_check():
     assert _call_bx() in (fa.FA_ERR_NOT_DEVICE_MEMORY, fa.FA_ERR_HIP)
+    assert _call_bx(dtype=0) in (fa.FA_ERR_NOT_DEVICE_MEMORY, fa.FA_ERR_HIP)
+    assert _call_b(dtype=0, dk=DQ + 2 * 64 * 64 * 4) in (fa.FA_ERR_NOT_DEVICE_MEMORY, fa.FA_ERR_HIP)
     assert _call_bx(kv_start=100, kv_len=0) in (fa.FA_ERR_NOT_DEVICE_MEMORY, fa.FA_ERR_HIP)

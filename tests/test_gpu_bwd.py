@@ -15,6 +15,15 @@ these budgets, while a dropped term, a wrong sign or a wrong mask moves elements
 absolute 1e-5 covers gradients that vanish exactly (one visible key: dQ = dK = 0): P is evaluated in fp32
 as exp2(scale log2(e) q.k - lse log2(e)), whose argument carries an error of about 2^-24 |scale q.k|, so
 such a P is 1 - O(1e-7) and the vanishing dS becomes O(1e-7) instead of 0.
+
+fp32 inputs: max |g_gpu - g_ref| <= 2e-4 * max |g_ref| + 1e-5.  Every factor and sum is fp32 (unit
+roundoff u = 2^-24 = 6.0e-8): a gradient element sums n <= 1024 terms here, each with a few u from its
+factors and, through P = exp2(c s - lse log2 e), an argument error of about |c s| u <= 32 u; recursive
+summation adds at most n u of the sum of magnitudes.  That is < 1.2e-4 of the sum of |terms|, which for
+these inputs stays within about 1.5x the largest |g|; a wrong term or mask still moves elements by O(max).
+The absolute 1e-5 covers gradients that vanish exactly (one visible key): there dS = P (dP - D) is the
+difference of two fp32 evaluations of sum_d dO_d v_d (dP from the products, D from the rounded O),
+about sqrt(D) u |dO| |v| ~ 1e-6, times scale |k|.
 """
 import os
 import sys
@@ -31,6 +40,7 @@ pytestmark = pytest.mark.gpu
 NTHREADS = min(16, os.cpu_count() or 1)
 TOL = 1e-2
 ATOL = 1e-5
+TOL32, ATOL32 = 2e-4, 1e-5
 
 
 def _say(msg):
@@ -39,6 +49,8 @@ def _say(msg):
 
 
 def to_dev(bits, dtype):
+    if dtype == "fp32":
+        return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.float32)).to("cuda")
     t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
         torch.float16 if dtype == "fp16" else torch.bfloat16)
     return t.to("cuda")
@@ -52,13 +64,14 @@ def run(q, k, v, do, dtype, layout, causal, scale):
     return (dq, dk, dv), (o, lse)
 
 
-def check(got, ref, what):
+def check(got, ref, what, dtype="bf16"):
+    tol, atol = (TOL32, ATOL32) if dtype == "fp32" else (TOL, ATOL)
     for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
         assert np.all(np.isfinite(g)), "%s %s: non-finite" % (what, name)
         err = np.abs(g - r).max()
         scale = np.abs(r).max()
         _say("%s %s: max|err|=%.3e max|ref|=%.3e ratio=%.2e" % (what, name, err, scale, err / max(scale, 1e-30)))
-        assert err <= TOL * scale + ATOL, "%s %s: max error %.3e over %.3e" % (what, name, err, TOL * scale + ATOL)
+        assert err <= tol * scale + atol, "%s %s: max error %.3e over %.3e" % (what, name, err, tol * scale + atol)
 
 
 def f64(t):
@@ -71,11 +84,11 @@ def full_compare(B, H, N, D, dtype, layout, causal, scale, seed, what, qk_mult=1
     _say("%s: B=%d H=%d N=%d D=%d %s %s causal=%d" % (what, B, H, N, D, dtype, layout, causal))
     got, _ = run(q, k, v, do, dtype, layout, causal, scale)
     ref = oracle.attention_bwd(q, k, v, do, dtype=dtype, layout=layout, causal=causal, scale=scale, nthreads=NTHREADS)
-    check([f64(t) for t in got], ref, what)
+    check([f64(t) for t in got], ref, what, dtype)
     return got
 
 
-@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp32"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_c2_shape_full(dtype, causal):
     w = inputs.WORKLOADS["c2"]
@@ -90,9 +103,18 @@ def test_ragged_sizes(N, D, causal):
 
 
 @pytest.mark.parametrize("layout", ["BHSD", "BSND"])
-@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp32"])
 def test_layouts_and_dtypes(layout, dtype):
     full_compare(2, 2, 333, 128, dtype, layout, True, 0.0883883461356163, [11, len(layout)], "bwd layout")
+
+
+@pytest.mark.parametrize("N", [1, 31, 32, 33, 127, 128, 129, 300])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp32_ragged_sizes(N, D, causal):
+    # the fp32 kernels tile by 32 keys / query rows: sizes around one and several tiles, and a ragged tail
+    full_compare(2, 2, N, D, "fp32", "BHSD", causal, float(np.float32(1 / np.sqrt(D))), [N, D, causal, 32],
+                 "bwd fp32 ragged")
 
 
 def test_large_logits():

@@ -5,7 +5,7 @@ window) for O and lse, then fa_bwd_ex, possibly once per key chunk; the oracle c
 dQ part and its dK, dV rows from Q, K, V and dO alone (``oracle.attention_bwd_ex``).  Tolerance as for
 fa_bwd: max |g_gpu - g_ref| <= 1e-2 * max |g_ref| + 1e-5 per gradient tensor, for the same reasons (two
 16-bit roundings per term, D taken from the rounded O; the absolute term covers gradients that vanish
-exactly).
+exactly); fp32 inputs: 2e-4 * max |g_ref| + 1e-5, derived in test_gpu_bwd.py.
 """
 import os
 import sys
@@ -22,6 +22,7 @@ pytestmark = pytest.mark.gpu
 NTHREADS = min(16, os.cpu_count() or 1)
 TOL = 1e-2
 ATOL = 1e-5
+TOL32, ATOL32 = 2e-4, 1e-5
 
 
 def _say(msg):
@@ -30,6 +31,8 @@ def _say(msg):
 
 
 def to_dev(bits, dtype):
+    if dtype == "fp32":
+        return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.float32)).to("cuda")
     t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
         torch.float16 if dtype == "fp16" else torch.bfloat16)
     return t.to("cuda")
@@ -39,12 +42,13 @@ def f64(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def check(name, g, r, what):
+def check(name, g, r, what, dtype="bf16"):
+    tol, atol = (TOL32, ATOL32) if dtype == "fp32" else (TOL, ATOL)
     assert np.all(np.isfinite(g)), "%s %s: non-finite" % (what, name)
     err = np.abs(g - r).max() if g.size else 0.0
     scale = np.abs(r).max() if r.size else 0.0
     _say("%s %s: max|err|=%.3e max|ref|=%.3e" % (what, name, err, scale))
-    assert err <= TOL * scale + ATOL, "%s %s: max error %.3e over %.3e" % (what, name, err, TOL * scale + ATOL)
+    assert err <= tol * scale + atol, "%s %s: max error %.3e over %.3e" % (what, name, err, tol * scale + atol)
 
 
 def make_case(B, H, Nq, Nk, D, dtype, layout, seed):
@@ -81,14 +85,14 @@ def compare_chunks(B, H, Nq, Nk, D, *, dtype="bf16", layout="BHSD", causal=True,
         torch.cuda.synchronize()
         ref = oracle.attention_bwd_ex(q, k, v, do, dtype=dtype, layout=layout, causal=causal, scale=scale,
                                       window=window, q_offset=q_offset, kv_start=s, kv_len=e - s, nthreads=NTHREADS)
-        check("dQ[%d:%d]" % (s, e), f64(dq), ref[0], what)
+        check("dQ[%d:%d]" % (s, e), f64(dq), ref[0], what, dtype)
         dq_sum += dq.double()
     full = oracle.attention_bwd_ex(q, k, v, do, dtype=dtype, layout=layout, causal=causal, scale=scale,
                                    window=window, q_offset=q_offset, nthreads=NTHREADS)
     if len(chunks) > 1:
-        check("sum dQ", dq_sum.cpu().numpy(), full[0], what)
-    check("dK", f64(dk), full[1], what)
-    check("dV", f64(dv), full[2], what)
+        check("sum dQ", dq_sum.cpu().numpy(), full[0], what, dtype)
+    check("dK", f64(dk), full[1], what, dtype)
+    check("dV", f64(dv), full[2], what, dtype)
     return dev, o, lse
 
 
@@ -126,10 +130,16 @@ def test_key_chunks_add_up(causal, window, q_offset, D):
 
 
 @pytest.mark.parametrize("layout", ["BHSD", "BSND"])
-@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp32"])
 def test_layouts_and_dtypes(layout, dtype):
     compare_chunks(2, 3, 190, 270, 128, dtype=dtype, layout=layout, q_offset=80, chunks=[(0, 141), (141, 270)],
                    seed=6, what="bwd_ex layout")
+
+
+@pytest.mark.parametrize("causal,window,q_offset", [(False, -1, 0), (True, -1, 120), (True, 90, 30), (True, -1, -50)])
+def test_fp32_chunks_offsets_windows(causal, window, q_offset):
+    compare_chunks(1, 2, 300, 400, 64, dtype="fp32", causal=causal, window=window, q_offset=q_offset,
+                   chunks=[(0, 100), (100, 101), (101, 333), (333, 400)], seed=13, what="bwd_ex fp32")
 
 
 def test_negative_offset_rows_without_keys():

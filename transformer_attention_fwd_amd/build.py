@@ -7,7 +7,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("fa_kernels.hip", "fa_merge.hip", "fa_bwd.hip", "fa_api.cpp")]
+SOURCES = [os.path.join(CSRC, f) for f in ("fa_kernels.hip", "fa_merge.hip", "fa_bwd.hip", "fa_bwd32.hip", "fa_api.cpp")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

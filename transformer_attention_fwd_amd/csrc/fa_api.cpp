@@ -293,11 +293,11 @@ FA_API int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
   if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_BAD_DTYPE;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || D < 1) return FA_ERR_BAD_DIM;
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
-  if (dtype == FA_DTYPE_FP32) return FA_ERR_UNSUPPORTED;
+  const int64_t esize = dtype == FA_DTYPE_FP32 ? 4 : 2;
   int64_t bh, rows_q, rows_k, elems_q, elems_k, bytes_q, bytes_k, row_bytes;
   if (Nq > kMaxRows || Nk > kMaxRows || !mul_ok(B, H, &bh) || bh > INT32_MAX || !mul_ok(bh, Nq, &rows_q) ||
       !mul_ok(bh, Nk, &rows_k) || !mul_ok(rows_q, D, &elems_q) || !mul_ok(rows_k, D, &elems_k) ||
-      !mul_ok(elems_q, 2, &bytes_q) || !mul_ok(elems_k, 2, &bytes_k) || !mul_ok(rows_q, 4, &row_bytes))
+      !mul_ok(elems_q, esize, &bytes_q) || !mul_ok(elems_k, esize, &bytes_k) || !mul_ok(rows_q, 4, &row_bytes))
     return FA_ERR_UNSUPPORTED;
   if (kv_start < 0 || kv_len < 0 || kv_start > Nk || kv_len > Nk - kv_start) return FA_ERR_BAD_RANGE;
   if (window >= 0 && !causal) return FA_ERR_BAD_RANGE;
@@ -305,8 +305,8 @@ FA_API int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
   const int64_t rpw = fa::bwd_rows_per_workgroup();
   if (bh * ((Nq + rpw - 1) / rpw) > INT32_MAX || bh * ((Nk + rpw - 1) / rpw) > INT32_MAX) return FA_ERR_UNSUPPORTED;
   // one head's rows of Q/dO and of K/V are addressed with 32-bit offsets from per-head buffer descriptors
-  const int64_t stride_bytes = (layout == FA_LAYOUT_BHSD ? D : H * D) * 2;
-  if ((Nq - 1) * stride_bytes + D * 2 > INT32_MAX || (Nk - 1) * stride_bytes + D * 2 > INT32_MAX)
+  const int64_t stride_bytes = (layout == FA_LAYOUT_BHSD ? D : H * D) * esize;
+  if ((Nq - 1) * stride_bytes + D * esize > INT32_MAX || (Nk - 1) * stride_bytes + D * esize > INT32_MAX)
     return FA_ERR_UNSUPPORTED;
   if (!isfinite(scale) || !isfinite(fabsf(scale) * 1.4426950408889634f)) return FA_ERR_BAD_SCALE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse | (uintptr_t)dout |
@@ -376,8 +376,8 @@ FA_API int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
   }
   p.c = scale * 1.4426950408889634f;
   p.scale = scale;
-  e = fa::launch_bwd(p, dtype == FA_DTYPE_FP16 ? fa::kDtypeFp16 : fa::kDtypeBf16, (int)D, causal != 0,
-                     (hipStream_t)stream);
+  const int kd = dtype == FA_DTYPE_FP32 ? fa::kDtypeFp32 : dtype == FA_DTYPE_FP16 ? fa::kDtypeFp16 : fa::kDtypeBf16;
+  e = fa::launch_bwd(p, kd, (int)D, causal != 0, (hipStream_t)stream);
   if (e != hipSuccess) {
     set_error("kernel launch", e);
     return FA_ERR_HIP;

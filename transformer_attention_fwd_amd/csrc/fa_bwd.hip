@@ -1,4 +1,4 @@
-// fa_bwd.hip -- attention backward kernels for gfx950 (MI355X, CDNA4), 16-bit inputs.
+// fa_bwd.hip -- attention backward kernels for gfx950 (MI355X, CDNA4), 16-bit inputs (fp32: fa_bwd32.hip).
 //
 // What is computed: for O = softmax(scale * Q K^T [+ causal mask]) V and an upstream gradient dO, the
 // gradients dQ, dK, dV (the vector-Jacobian product).  With P the softmax probabilities,
@@ -584,6 +584,7 @@ hipError_t launch_bwd_c(const BwdParams& p, bool causal, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_bwd(const BwdParams& p, int dtype, int d, bool causal, hipStream_t stream) {
+  if (dtype == kDtypeFp32) return launch_bwd32(p, d, causal, stream);
   const bool bf = dtype == kDtypeBf16;
   if (d == 128) return bf ? launch_bwd_c<128, true>(p, causal, stream) : launch_bwd_c<128, false>(p, causal, stream);
   return bf ? launch_bwd_c<64, true>(p, causal, stream) : launch_bwd_c<64, false>(p, causal, stream);

@@ -35,9 +35,12 @@ struct BwdParams {
   float scale;
 };
 
-// Enqueue the two backward kernels (dQ and D, then dK and dV) for a 16-bit dtype on `stream`; a
-// window is used only with causal.
+// Enqueue the two backward kernels (dQ and D, then dK and dV) for `dtype` on `stream`; a window is used
+// only with causal.
 hipError_t launch_bwd(const BwdParams& p, int dtype, int d, bool causal, hipStream_t stream);
+
+// The fp32 kernels behind launch_bwd.
+hipError_t launch_bwd32(const BwdParams& p, int d, bool causal, hipStream_t stream);
 
 // Query (and key) rows handled by one backward workgroup.
 int bwd_rows_per_workgroup();
