@@ -56,7 +56,8 @@ extern "C" {
 #define FA_ERR_NOT_DEVICE_MEMORY 9 /* a pointer is not device memory of the current device */
 #define FA_ERR_HIP 10              /* the HIP runtime reported an error; see fa_last_error() */
 #define FA_ERR_BAD_RANGE 11        /* fa_fwd_ex / fa_bwd_ex: key chunk outside [0, Nk], a window without
-                                      causal, or |q_offset| > 2^30; fa_fwd_varlen: max_seqlen_q > total_q */
+                                      causal, or |q_offset| > 2^30; fa_fwd_varlen: max_seqlen_q > total_q;
+                                      fa_bwd_varlen: max_seqlen_q > total_q or max_seqlen_k > total_k */
 
 /* Limits: 1 <= N <= 2^30, B*H <= 2^31 - 1, every tensor's byte size must fit in int64, and one head's
  * span -- (N - 1) * (bytes between consecutive positions) + D * element size -- must be below 2^31
@@ -200,6 +201,28 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
               void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
               int layout, int causal, int64_t window, int64_t q_offset, int64_t kv_start, int64_t kv_len,
               float scale, int dtype, void* stream);
+
+/*
+ * fa_bwd_varlen -- the backward of fa_fwd_varlen: dQ, dK, dV of B packed sequences of different lengths
+ * (page ai6s.net/6a0d3bfb..., section "FlashAttention在昇腾NPU上怎么跑？", item 3 for the recomputing
+ * backward; the packed layout and the per-sequence rule are fa_fwd_varlen's).
+ *
+ * q, o, dout, dq: [total_q][H][D]; k, v, dk, dv: [total_k][H][D]; lse (the forward's) and delta (the
+ * caller's fp32 workspace, written with D_i = sum_d dout_id o_id): [H][total_q].  cu_seqlens_q,
+ * cu_seqlens_k: int32 device arrays of B+1 offsets as in fa_fwd_varlen; under causal each sequence's
+ * query and key ends are aligned.  max_seqlen_q and max_seqlen_k bound the sequences' query and key
+ * counts (the launch grid).  A sequence whose offsets fall outside [0, total] or decrease is skipped:
+ * its rows of dq, dk, dv and delta are left untouched.  Rows of a sequence without queries get dK = dV
+ * = 0, rows without keys dQ = 0.
+ * dtype: FA_DTYPE_FP16 or FA_DTYPE_BF16 (FA_DTYPE_FP32 returns FA_ERR_UNSUPPORTED).  D in {64, 128}.
+ * Errors as fa_fwd_varlen, plus the aliasing rules of fa_bwd; FA_ERR_BAD_RANGE when max_seqlen_q >
+ * total_q or max_seqlen_k > total_k.
+ */
+int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, float* delta, const int32_t* cu_seqlens_q,
+                  const int32_t* cu_seqlens_k, int64_t B, int64_t H, int64_t total_q, int64_t total_k,
+                  int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t D, int causal, float scale, int dtype,
+                  void* stream);
 
 /* Static description of a status code ("ok", "null pointer", ...).  Never NULL. */
 const char* fa_status_str(int status);

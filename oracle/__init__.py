@@ -280,6 +280,41 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, dtype: str, causal:
     return o, lse
 
 
+def attention_bwd_varlen(q, k, v, dout, cu_seqlens_q, cu_seqlens_k, *, dtype: str, causal: bool, scale: float,
+                         nthreads: int = 1):
+    """Gradients (dQ, dK, dV) in fp64 of ``attention_varlen``'s packed batch for upstream gradient ``dout``.
+
+    q, dout: [total_q, H, D]; k, v: [total_k, H, D]; offsets as in ``attention_varlen``.  Each sequence is
+    independent: its gradients are ``attention_bwd_ex`` of its own rows (the BSND layout with B = 1) under
+    the aligned-ends rule, query offset Nk - Nq when causal.  A sequence without queries contributes
+    dK = dV = 0 for its keys; queries without keys get dQ = 0.  Returns (dQ [total_q, H, D], dK, dV
+    [total_k, H, D]).
+    """
+    cu_q = [int(x) for x in cu_seqlens_q]
+    cu_k = [int(x) for x in cu_seqlens_k]
+    if len(cu_q) != len(cu_k) or len(cu_q) < 2 or cu_q[0] != 0 or cu_k[0] != 0:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must hold B + 1 offsets starting at 0")
+    if any(b < a for a, b in zip(cu_q, cu_q[1:])) or any(b < a for a, b in zip(cu_k, cu_k[1:])):
+        raise ValueError("cu_seqlens must be non-decreasing")
+    if q.ndim != 3 or k.ndim != 3 or v.shape != k.shape or q.shape[1:] != k.shape[1:] or dout.shape != q.shape:
+        raise ValueError("q, dout must be [total_q, H, D] and k, v [total_k, H, D]")
+    if cu_q[-1] != q.shape[0] or cu_k[-1] != k.shape[0]:
+        raise ValueError("the last offsets must equal total_q and total_k")
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(k.shape, dtype=np.float64)
+    for b in range(len(cu_q) - 1):
+        qs, qe, ks, ke = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        nq, nk = qe - qs, ke - ks
+        if nq == 0 or nk == 0:
+            continue  # no queries (dK = dV = 0) or no keys (dQ = 0), as initialised
+        gq, gk, gv = attention_bwd_ex(q[qs:qe][None], k[ks:ke][None], v[ks:ke][None], dout[qs:qe][None], dtype=dtype,
+                                      layout="BSND", causal=causal, scale=scale, q_offset=(nk - nq) if causal else 0,
+                                      nthreads=nthreads)
+        dq[qs:qe], dk[ks:ke], dv[ks:ke] = gq[0], gk[0], gv[0]
+    return dq, dk, dv
+
+
 def attention_bwd_ex(q, k, v, dout, *, dtype: str, layout: str, causal: bool, scale: float, window: int = -1,
                      q_offset: int = 0, kv_start: int = 0, kv_len=None, heads=None, nthreads: int = 1):
     """Generalised gradients in fp64, the backward of ``attention_ex``'s rule.

@@ -18,8 +18,8 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     declared = _declared()
-    assert declared == ["fa_bwd", "fa_bwd_ex", "fa_fwd", "fa_fwd_ex", "fa_fwd_varlen", "fa_last_error", "fa_merge",
-                        "fa_status_str", "fa_version"]
+    assert declared == ["fa_bwd", "fa_bwd_ex", "fa_bwd_varlen", "fa_fwd", "fa_fwd_ex", "fa_fwd_varlen", "fa_last_error",
+                        "fa_merge", "fa_status_str", "fa_version"]
     out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], stdout=subprocess.PIPE,
                          text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if l.split() and l.split()[1] == "T"}
@@ -43,7 +43,7 @@ def test_header_constants_match_binding():
 
 
 def test_status_strings_and_version():
-    assert fa.version() == 500
+    assert fa.version() == 600
     for st in range(12):
         assert fa.status_str(st)
     assert fa.status_str(0) == "ok"
@@ -266,3 +266,32 @@ def test_fa_bwd_ex_good_arguments_reach_the_device_check():
     assert _call_bx(dtype=0) in (fa.FA_ERR_NOT_DEVICE_MEMORY, fa.FA_ERR_HIP)
     assert _call_b(dtype=0, dk=DQ + 2 * 64 * 64 * 4) in (fa.FA_ERR_NOT_DEVICE_MEMORY, fa.FA_ERR_HIP)
     assert _call_bx(kv_start=100, kv_len=0) in (fa.FA_ERR_NOT_DEVICE_MEMORY, fa.FA_ERR_HIP)
+
+
+# ---- fa_bwd_varlen: pure argument checks ----
+CQ, CK = 0x10000000000 + 11 * (SZ * 4), 0x10000000000 + 12 * (SZ * 4)
+GOOD_BV = dict(q=Q, k=K, v=V, o=O, lse=L, do=DO, dq=DQ, dk=DK, dv=DV, delta=DL, cq=CQ, ck=CK, B=3, H=2, tq=300,
+               tk=400, mq=150, mk=200, D=128, causal=1, scale=0.1, dtype=2, stream=0)
+
+
+def _call_bv(**kw):
+    a = dict(GOOD_BV)
+    a.update(kw)
+    return fa.fa_bwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"], a["delta"],
+                            a["cq"], a["ck"], a["B"], a["H"], a["tq"], a["tk"], a["mq"], a["mk"], a["D"], a["causal"],
+                            a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ck=0), fa.FA_ERR_NULL), (dict(delta=0), fa.FA_ERR_NULL), (dict(dtype=7), fa.FA_ERR_BAD_DTYPE),
+    (dict(mk=0), fa.FA_ERR_BAD_DIM), (dict(tq=0), fa.FA_ERR_BAD_DIM), (dict(D=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=0), fa.FA_ERR_UNSUPPORTED), (dict(mq=301), fa.FA_ERR_BAD_RANGE), (dict(mk=401), fa.FA_ERR_BAD_RANGE),
+    (dict(scale=float("nan")), fa.FA_ERR_BAD_SCALE), (dict(cq=CQ + 2), fa.FA_ERR_MISALIGNED),
+    (dict(dv=DQ + 16), fa.FA_ERR_ALIAS), (dict(delta=CK), fa.FA_ERR_ALIAS), (dict(dk=V + 16), fa.FA_ERR_ALIAS),
+])
+def test_fa_bwd_varlen_argument_checks(kw, status):
+    assert _call_bv(**kw) == status
+
+
+def test_fa_bwd_varlen_good_arguments_reach_the_device_check():
+    assert _call_bv() in (fa.FA_ERR_NOT_DEVICE_MEMORY, fa.FA_ERR_HIP)

@@ -33,6 +33,11 @@ There is no CPU or framework fallback: if ``libfa.so`` is missing the first call
                      kv_start=0, kv_len=None, dk=None, dv=None, delta=None) -> (dq, dk, dv)
         the generalised backward (dk, dv rows outside the key chunk keep the given tensors' values; new
         tensors start at zero).
+    fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, delta, cu_seqlens_q, cu_seqlens_k, B, H, total_q, total_k,
+                  max_seqlen_q, max_seqlen_k, D, causal, scale, dtype, stream) -> status
+    attention_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, *,
+                         causal=False, scale=None, delta=None, out=None) -> (dq, dk, dv)
+        the backward of packed variable-length batches.
 """
 from __future__ import annotations
 
@@ -40,8 +45,8 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "fa_fwd_ex", "fa_fwd_varlen", "fa_merge", "fa_bwd", "fa_bwd_ex", "attention", "attention_ex",
-           "attention_varlen", "merge", "attention_bwd", "attention_bwd_ex", "FaError", "library_path",
+__all__ = ["fa_fwd", "fa_fwd_ex", "fa_fwd_varlen", "fa_merge", "fa_bwd", "fa_bwd_ex", "fa_bwd_varlen", "attention",
+           "attention_ex", "attention_varlen", "merge", "attention_bwd", "attention_bwd_ex", "attention_bwd_varlen", "FaError", "library_path",
            "load", "status_str", "version",
            "LAYOUT_BHSD", "LAYOUT_BSND", "DTYPE_FP32", "DTYPE_FP16", "DTYPE_BF16"]
 
@@ -100,6 +105,9 @@ def load():
         lib.fa_bwd.restype = ctypes.c_int
         lib.fa_bwd.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_int,
                                ctypes.c_float, ctypes.c_int, ctypes.c_void_p])
+        lib.fa_bwd_varlen.restype = ctypes.c_int
+        lib.fa_bwd_varlen.argtypes = ([ctypes.c_void_p] * 12 + [ctypes.c_int64] * 7 + [ctypes.c_int, ctypes.c_float,
+                                      ctypes.c_int, ctypes.c_void_p])
         lib.fa_bwd_ex.restype = ctypes.c_int
         lib.fa_bwd_ex.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int64] * 5 + [ctypes.c_int, ctypes.c_int] +
                                   [ctypes.c_int64] * 4 + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p])
@@ -130,6 +138,15 @@ def fa_merge(o_parts, lse_parts, n_parts, o, lse, B, H, N, D, layout, dtype, str
     """The C merge entry point: pointers are ints (0 = NULL), returns the status code."""
     return load().fa_merge(o_parts or None, lse_parts or None, n_parts, o or None, lse or None, B, H, N, D,
                            layout, dtype, stream or None)
+
+
+def fa_bwd_varlen(q, k, v, o, lse, dout, dq, dk, dv, delta, cu_seqlens_q, cu_seqlens_k, B, H, total_q, total_k,
+                  max_seqlen_q, max_seqlen_k, D, causal, scale, dtype, stream) -> int:
+    """The packed variable-length backward C entry point: pointers are ints (0 = NULL), returns the status."""
+    return load().fa_bwd_varlen(q or None, k or None, v or None, o or None, lse or None, dout or None, dq or None,
+                                dk or None, dv or None, delta or None, cu_seqlens_q or None, cu_seqlens_k or None, B,
+                                H, total_q, total_k, max_seqlen_q, max_seqlen_k, D, int(causal), scale, dtype,
+                                stream or None)
 
 
 def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, total_q, total_k, max_seqlen_q, D, causal,
@@ -357,6 +374,44 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, *, 
                             cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, total_q, total_k, int(max_seqlen_q),
                             D, causal, float(scale), _dtype_code(q), stream))
     return out, lse
+
+
+def attention_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, *,
+                         causal: bool = False, scale: float | None = None, delta=None, out=None):
+    """fa_bwd_varlen for torch device tensors: q, o, dout [total_q, H, D]; k, v [total_k, H, D]; lse [H, total_q]
+    of fa_fwd_varlen; int32 offsets.  Returns (dq, dk, dv); out = (dq, dk, dv) tensors to write into (rows of
+    skipped sequences keep their values), else new ones."""
+    import torch
+    if q.dim() != 3 or k.dim() != 3 or v.shape != k.shape or q.shape[1:] != k.shape[1:]:
+        raise ValueError("q must be [total_q, H, D] and k, v [total_k, H, D]")
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must be shaped like q")
+    if any(t.dtype != q.dtype for t in (k, v, o, dout)):
+        raise TypeError("q, k, v, o, dout must share a dtype")
+    for t in (q, k, v, o, dout):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v, o, dout must be contiguous")
+    for t in (cu_seqlens_q, cu_seqlens_k):
+        if t.dim() != 1 or t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError("cu_seqlens must be contiguous 1-D int32 tensors")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must hold B + 1 offsets")
+    total_q, H, D = q.shape
+    total_k = k.shape[0]
+    B = cu_seqlens_q.numel() - 1
+    if lse.shape != (H, total_q) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of shape [H, total_q]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if delta is None:
+        delta = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    stream = torch.cuda.current_stream(q.device).cuda_stream if q.is_cuda else 0
+    _raise_on(fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), cu_seqlens_q.data_ptr(),
+                            cu_seqlens_k.data_ptr(), B, H, total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), D,
+                            causal, float(scale), _dtype_code(q), stream))
+    return dq, dk, dv
 
 
 def attention_bwd_ex(q, k, v, o, lse, dout, *, layout: str = "BHSD", causal: bool = False, scale: float | None = None,

@@ -70,7 +70,7 @@ FA_API const char* fa_status_str(int status) {
 
 FA_API const char* fa_last_error(void) { return g_last_error; }
 
-FA_API int fa_version(void) { return 500; }  // 0.5.0
+FA_API int fa_version(void) { return 600; }  // 0.6.0
 
 FA_API int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                      int64_t Nq, int64_t Nk, int64_t D, int layout, int causal, int64_t window, int64_t q_offset,
@@ -378,6 +378,101 @@ FA_API int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
   p.scale = scale;
   const int kd = dtype == FA_DTYPE_FP32 ? fa::kDtypeFp32 : dtype == FA_DTYPE_FP16 ? fa::kDtypeFp16 : fa::kDtypeBf16;
   e = fa::launch_bwd(p, kd, (int)D, causal != 0, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    set_error("kernel launch", e);
+    return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+FA_API int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, float* delta, const int32_t* cu_seqlens_q,
+                         const int32_t* cu_seqlens_k, int64_t B, int64_t H, int64_t total_q, int64_t total_k,
+                         int64_t max_seqlen_q, int64_t max_seqlen_k, int64_t D, int causal, float scale, int dtype,
+                         void* stream) {
+  // ---- pure argument checks (no HIP calls) ----
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta || !cu_seqlens_q || !cu_seqlens_k)
+    return FA_ERR_NULL;
+  if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_BAD_DTYPE;
+  if (B < 1 || H < 1 || total_q < 1 || total_k < 1 || max_seqlen_q < 1 || max_seqlen_k < 1 || D < 1)
+    return FA_ERR_BAD_DIM;
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_DTYPE_FP32) return FA_ERR_UNSUPPORTED;
+  int64_t rows_q, rows_k, elems_q, elems_k, bytes_q, bytes_k, row_bytes, bh, cu_bytes;
+  if (total_q > kMaxRows || total_k > kMaxRows || B > kMaxRows || !mul_ok(total_q, H, &rows_q) ||
+      !mul_ok(total_k, H, &rows_k) || !mul_ok(rows_q, D, &elems_q) || !mul_ok(rows_k, D, &elems_k) ||
+      !mul_ok(elems_q, 2, &bytes_q) || !mul_ok(elems_k, 2, &bytes_k) || !mul_ok(rows_q, 4, &row_bytes) ||
+      !mul_ok(B, H, &bh) || bh > INT32_MAX || !mul_ok(B + 1, 4, &cu_bytes))
+    return FA_ERR_UNSUPPORTED;
+  if (max_seqlen_q > total_q || max_seqlen_k > total_k) return FA_ERR_BAD_RANGE;
+  const int64_t rpw = fa::bwd_rows_per_workgroup();
+  if ((bh + 7) / 8 * 8 * ((max_seqlen_q + rpw - 1) / rpw) > INT32_MAX ||
+      (bh + 7) / 8 * 8 * ((max_seqlen_k + rpw - 1) / rpw) > INT32_MAX)
+    return FA_ERR_UNSUPPORTED;
+  // every sequence's rows lie inside [0, total): one head's rows fit a buffer descriptor
+  if ((total_q - 1) * H * D * 2 + D * 2 > INT32_MAX || (total_k - 1) * H * D * 2 + D * 2 > INT32_MAX)
+    return FA_ERR_UNSUPPORTED;
+  if (!isfinite(scale) || !isfinite(fabsf(scale) * 1.4426950408889634f)) return FA_ERR_BAD_SCALE;
+  if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse | (uintptr_t)dout |
+        (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)delta) & 15) ||
+      (((uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k) & 3))
+    return FA_ERR_MISALIGNED;
+  const void* ins[8] = {q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k};
+  const int64_t in_bytes[8] = {bytes_q, bytes_k, bytes_k, bytes_q, row_bytes, bytes_q, cu_bytes, cu_bytes};
+  const void* outs[4] = {dq, dk, dv, delta};
+  const int64_t out_bytes[4] = {bytes_q, bytes_k, bytes_k, row_bytes};
+  for (int a = 0; a < 4; ++a) {
+    for (int i = 0; i < 8; ++i)
+      if (overlaps(outs[a], out_bytes[a], ins[i], in_bytes[i])) return FA_ERR_ALIAS;
+    for (int c = a + 1; c < 4; ++c)
+      if (overlaps(outs[a], out_bytes[a], outs[c], out_bytes[c])) return FA_ERR_ALIAS;
+  }
+
+  // ---- device residency ----
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) {
+    set_error("hipGetDevice", e);
+    return FA_ERR_HIP;
+  }
+  for (const void* ptr : ins) {
+    const int st = check_device(ptr, device);
+    if (st != FA_OK) return st;
+  }
+  for (const void* ptr : outs) {
+    const int st = check_device(ptr, device);
+    if (st != FA_OK) return st;
+  }
+
+  // ---- launch ----
+  fa::BwdParams p;
+  memset(&p, 0, sizeof p);
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.delta = delta;
+  p.B = (int)B;
+  p.H = (int)H;
+  p.Nq = (int)max_seqlen_q;
+  p.Nk = (int)max_seqlen_k;
+  p.window = -1;
+  p.stride_h_q = D;
+  p.stride_h_k = D;
+  p.stride_s = H * D;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.total_q = total_q;
+  p.total_k = total_k;
+  p.c = scale * 1.4426950408889634f;
+  p.scale = scale;
+  e = fa::launch_bwd_varlen(p, dtype == FA_DTYPE_FP16 ? fa::kDtypeFp16 : fa::kDtypeBf16, (int)D, causal != 0,
+                            (hipStream_t)stream);
   if (e != hipSuccess) {
     set_error("kernel launch", e);
     return FA_ERR_HIP;

@@ -102,10 +102,50 @@ __device__ __forceinline__ void lane_offsets(int li, int g, int (&rb)[BwdTile<D>
   }
 }
 
+// Where one workgroup's (b, h) rows lie: the query and key counts, the key chunk, the query offset and
+// window, the element offsets of the rows in Q/O/dO/dQ and K/V/dK/dV, and the index of the first row's lse
+// and D.  For packed variable-length batches these come from sequence b's offsets (the two ends aligned
+// under causal); offsets outside [0, total] or decreasing leave the sequence untouched (skip).
+struct BwdGeom {
+  int Nq, Nk, kv0, kv1;
+  int64_t qoff, window, qhead, khead, row0;
+  bool skip;
+};
+
+template <bool VARLEN, bool CAUSAL>
+__device__ __forceinline__ BwdGeom bwd_geometry(const BwdParams& p, int b, int h, int bh) {
+  BwdGeom gm;
+  if constexpr (VARLEN) {
+    const int qs = p.cu_q[b], qe = p.cu_q[b + 1], ks = p.cu_k[b], ke = p.cu_k[b + 1];
+    gm.skip = qs < 0 || qe < qs || qe > p.total_q || ks < 0 || ke < ks || ke > p.total_k;
+    gm.Nq = qe - qs;
+    gm.Nk = ke - ks;
+    gm.kv0 = 0;
+    gm.kv1 = gm.Nk;
+    gm.qoff = CAUSAL ? (int64_t)gm.Nk - gm.Nq : 0;
+    gm.window = -1;
+    gm.qhead = (int64_t)qs * p.stride_s + h * p.stride_h_q;
+    gm.khead = (int64_t)ks * p.stride_s + h * p.stride_h_k;
+    gm.row0 = (int64_t)h * p.total_q + qs;
+  } else {
+    gm.skip = false;
+    gm.Nq = p.Nq;
+    gm.Nk = p.Nk;
+    gm.kv0 = p.kv_start;
+    gm.kv1 = p.kv_start + p.kv_len;
+    gm.qoff = p.q_offset;
+    gm.window = p.window;
+    gm.qhead = b * p.stride_b_q + h * p.stride_h_q;
+    gm.khead = b * p.stride_b_k + h * p.stride_h_k;
+    gm.row0 = (int64_t)bh * p.Nq;
+  }
+  return gm;
+}
+
 // ------------------------------------------------------------------------------------------------
 // dQ (and D) : one workgroup per (b, h, 128-query tile)
 // ------------------------------------------------------------------------------------------------
-template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW>
+template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW, bool VARLEN>
 __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
   typedef BwdTile<D> T;
   typedef Elem<IS_BF16> E;
@@ -123,14 +163,20 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, li = lane & 15;
   int bh, qt;
-  unit_of(blockIdx.x, p.n_units_q, p.n_tiles_q, CAUSAL, bh, qt);
+  if constexpr (VARLEN) {
+    unit_of_spread(blockIdx.x, p.n_tiles_q, CAUSAL, bh, qt);
+    if (bh >= p.B * p.H) return;  // padding head of the grid
+  } else {
+    unit_of(blockIdx.x, p.n_units_q, p.n_tiles_q, CAUSAL, bh, qt);
+  }
   const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
-  const int Nq = p.Nq, Nk = p.Nk;
-  const int64_t qoff = p.q_offset, window = p.window;
-  const int kv0 = p.kv_start, kv1 = p.kv_start + p.kv_len;  // the key chunk [kv0, kv1)
+  const BwdGeom gm = bwd_geometry<VARLEN, CAUSAL>(p, b, h, bh);
+  if (VARLEN && (gm.skip || qt * BM >= gm.Nq)) return;  // a bad sequence, or a tile past its end
+  const int Nq = gm.Nq, Nk = gm.Nk;
+  const int64_t qoff = gm.qoff, window = gm.window;
+  const int kv0 = gm.kv0, kv1 = gm.kv1;  // the key chunk [kv0, kv1)
   const int q_wg = qt * BM, q0 = q_wg + wave * QW;
-  const int64_t qhead = b * p.stride_b_q + h * p.stride_h_q;
-  const int64_t khead = b * p.stride_b_k + h * p.stride_h_k;
+  const int64_t qhead = gm.qhead, khead = gm.khead;
   const int64_t ss = p.stride_s;
 
   // K/V tiles from k_lo: the chunk's keys that some query of this workgroup sees
@@ -145,7 +191,7 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
   const int rbase = (int)max((int64_t)-(1 << 26), min((int64_t)(1 << 26), base64));
   const int wbase = WINDOW ? (int)max((int64_t)-(1 << 26), min((int64_t)(1 << 26), base64 - window)) : 0;
   const int row_bytes = (int)(2 * ss);
-  const int span = (Nk - 1) * row_bytes + T::ROW_BYTES;  // the host keeps this below 2^31
+  const int span = max(0, (Nk - 1) * row_bytes + T::ROW_BYTES);  // the host keeps this below 2^31
   const __amdgpu_buffer_rsrc_t kbuf =
       __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.k + khead), 0, span, kBufferFlags);
   const __amdgpu_buffer_rsrc_t vbuf =
@@ -184,8 +230,8 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
       for (int x = 0; x < 8; ++x) acc = __builtin_fmaf(to_f32<IS_BF16>(df[qg][c], x), to_f32<IS_BF16>(of, x), acc);
     }
     dlt[qg] = wave_sum_xor16_32(acc);
-    lse2[qg] = p.lse[(int64_t)bh * Nq + qrow] * kLog2e;
-    if (g == 0 && qi < Nq) p.delta[(int64_t)bh * Nq + qi] = dlt[qg];
+    lse2[qg] = p.lse[gm.row0 + qrow] * kLog2e;
+    if (g == 0 && qi < Nq) p.delta[gm.row0 + qi] = dlt[qg];
   }
 
   const float cexp = p.c;  // scale * log2(e), signed
@@ -309,7 +355,7 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
 // ------------------------------------------------------------------------------------------------
 // dK, dV : one workgroup per (b, h, 128-key tile)
 // ------------------------------------------------------------------------------------------------
-template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW, int NW, int KW, int MINB>
+template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW, bool VARLEN, int NW, int KW, int MINB>
 __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
   typedef BwdTile<D> T;
   typedef Elem<IS_BF16> E;
@@ -333,14 +379,20 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, li = lane & 15;
   int bh, kt;
-  unit_of(blockIdx.x, p.n_units_k, p.n_tiles_k, false, bh, kt);  // causal: the chunk's first key tile first
+  if constexpr (VARLEN) {
+    unit_of_spread(blockIdx.x, p.n_tiles_k, false, bh, kt);
+    if (bh >= p.B * p.H) return;  // padding head of the grid
+  } else {
+    unit_of(blockIdx.x, p.n_units_k, p.n_tiles_k, false, bh, kt);  // causal: the chunk's first key tile first
+  }
   const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
-  const int Nq = p.Nq;
-  const int64_t qoff = p.q_offset, window = p.window;
-  const int kv1 = p.kv_start + p.kv_len;  // keys of the chunk: [p.kv_start, kv1)
-  const int k_wg = p.kv_start + kt * BK, kw0 = k_wg + wave * KW;
-  const int64_t qhead = b * p.stride_b_q + h * p.stride_h_q;
-  const int64_t khead = b * p.stride_b_k + h * p.stride_h_k;
+  const BwdGeom gm = bwd_geometry<VARLEN, CAUSAL>(p, b, h, bh);
+  if (VARLEN && (gm.skip || kt * BK >= gm.Nk)) return;  // a bad sequence, or a tile past its end
+  const int Nq = gm.Nq;
+  const int64_t qoff = gm.qoff, window = gm.window;
+  const int kv1 = gm.kv1;  // keys of the chunk: [gm.kv0, kv1)
+  const int k_wg = gm.kv0 + kt * BK, kw0 = k_wg + wave * KW;
+  const int64_t qhead = gm.qhead, khead = gm.khead;
   const int64_t ss = p.stride_s;
 
   // K and V of the wave's keys as B operands of S = Q K^T and dP = dO V^T: lane holds key kw0 + 16*kg + li,
@@ -377,7 +429,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
   const int rbase = (int)rbc64;
   const int wv = WINDOW ? (int)max((int64_t)-(1 << 27), min((int64_t)(1 << 27), window - (rb64 - rbc64))) : 0;
   const int row_bytes = (int)(2 * ss);
-  const int span = (Nq - 1) * row_bytes + T::ROW_BYTES;
+  const int span = max(0, (Nq - 1) * row_bytes + T::ROW_BYTES);
   const __amdgpu_buffer_rsrc_t qbuf =
       __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)p.q + qhead), 0, span, kBufferFlags);
   const __amdgpu_buffer_rsrc_t obuf =
@@ -395,8 +447,8 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
   if (n_qt > 0) issue_tile(0, qs0, os0);
 
   const float cexp = p.c;
-  const float* lse_h = p.lse + (int64_t)bh * Nq;
-  const float* dlt_h = p.delta + (int64_t)bh * Nq;
+  const float* lse_h = p.lse + gm.row0;
+  const float* dlt_h = p.delta + gm.row0;
   // row values of tile jt for this lane's row (wave 0 only)
   auto load_rows = [&](int jt, float& l2v, float& dv) __attribute__((always_inline)) {
     const int qi = i_begin + jt * BQ + lane;
@@ -567,10 +619,27 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
   p.n_units_q = p.B * p.H * p.n_tiles_q;
   p.n_tiles_k = (p.kv_len + 127) / 128;
   p.n_units_k = p.B * p.H * p.n_tiles_k;
-  hipLaunchKernelGGL((fa_bwd_dq<D, IS_BF16, CAUSAL, WINDOW>), dim3(p.n_units_q), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((fa_bwd_dq<D, IS_BF16, CAUSAL, WINDOW, false>), dim3(p.n_units_q), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_units_k == 0) return e;
-  hipLaunchKernelGGL((fa_bwd_dkdv<D, IS_BF16, CAUSAL, WINDOW, kDkdvWaves, kDkdvKeys, kDkdvMinBlocks>),
+  hipLaunchKernelGGL((fa_bwd_dkdv<D, IS_BF16, CAUSAL, WINDOW, false, kDkdvWaves, kDkdvKeys, kDkdvMinBlocks>),
+                     dim3(p.n_units_k), dim3(64 * kDkdvWaves), 0, stream, p);
+  return hipGetLastError();
+}
+
+// packed sequences: the grid covers the longest query (key) count for every head, heads spread over the
+// XCDs and padded to a multiple of 8
+template <int D, bool IS_BF16, bool CAUSAL>
+hipError_t launch_bwd_varlen_t(BwdParams p, hipStream_t stream) {
+  const int heads = (p.B * p.H + 7) / 8 * 8;
+  p.n_tiles_q = (p.Nq + 127) / 128;
+  p.n_units_q = heads * p.n_tiles_q;
+  p.n_tiles_k = (p.Nk + 127) / 128;
+  p.n_units_k = heads * p.n_tiles_k;
+  hipLaunchKernelGGL((fa_bwd_dq<D, IS_BF16, CAUSAL, false, true>), dim3(p.n_units_q), dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((fa_bwd_dkdv<D, IS_BF16, CAUSAL, false, true, kDkdvWaves, kDkdvKeys, kDkdvMinBlocks>),
                      dim3(p.n_units_k), dim3(64 * kDkdvWaves), 0, stream, p);
   return hipGetLastError();
 }
@@ -588,6 +657,16 @@ hipError_t launch_bwd(const BwdParams& p, int dtype, int d, bool causal, hipStre
   const bool bf = dtype == kDtypeBf16;
   if (d == 128) return bf ? launch_bwd_c<128, true>(p, causal, stream) : launch_bwd_c<128, false>(p, causal, stream);
   return bf ? launch_bwd_c<64, true>(p, causal, stream) : launch_bwd_c<64, false>(p, causal, stream);
+}
+
+hipError_t launch_bwd_varlen(const BwdParams& p, int dtype, int d, bool causal, hipStream_t stream) {
+  const bool bf = dtype == kDtypeBf16;
+  if (d == 128) {
+    if (bf) return causal ? launch_bwd_varlen_t<128, true, true>(p, stream) : launch_bwd_varlen_t<128, true, false>(p, stream);
+    return causal ? launch_bwd_varlen_t<128, false, true>(p, stream) : launch_bwd_varlen_t<128, false, false>(p, stream);
+  }
+  if (bf) return causal ? launch_bwd_varlen_t<64, true, true>(p, stream) : launch_bwd_varlen_t<64, true, false>(p, stream);
+  return causal ? launch_bwd_varlen_t<64, false, true>(p, stream) : launch_bwd_varlen_t<64, false, false>(p, stream);
 }
 
 int bwd_rows_per_workgroup() { return 128; }

@@ -33,11 +33,20 @@ struct BwdParams {
   int n_tiles_k, n_units_k;  // filled by the launcher
   float c;            // scale * log2(e), signed
   float scale;
+  // Packed variable-length batches only (null otherwise): sequence b owns query rows cu_q[b] ..
+  // cu_q[b+1]-1 of the [total_q][H][D] tensors and key rows cu_k[b] .. cu_k[b+1]-1 of [total_k][H][D];
+  // Nq and Nk then hold the longest query and key counts (grid sizing) and lse, delta are [H][total_q].
+  const int* cu_q;
+  const int* cu_k;
+  int64_t total_q, total_k;
 };
 
 // Enqueue the two backward kernels (dQ and D, then dK and dV) for `dtype` on `stream`; a window is used
 // only with causal.
 hipError_t launch_bwd(const BwdParams& p, int dtype, int d, bool causal, hipStream_t stream);
+
+// Enqueue the backward of packed variable-length batches (16-bit dtypes; BwdParams::cu_q / cu_k set).
+hipError_t launch_bwd_varlen(const BwdParams& p, int dtype, int d, bool causal, hipStream_t stream);
 
 // The fp32 kernels behind launch_bwd.
 hipError_t launch_bwd32(const BwdParams& p, int d, bool causal, hipStream_t stream);

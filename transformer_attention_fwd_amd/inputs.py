@@ -23,8 +23,9 @@ backward pass comes from its own stream, ``default_rng([42, c, 7])``, as one mor
 of the same shape, rounded and stored the same way.
 
 Packed variable-length batches (``make_varlen``): Q [total_q, H, D] then K, V [total_k, H, D] from
-``default_rng([42, seed, 11])``, rounded the same way; ``varlen_lengths`` draws the sequence lengths
-uniformly from an inclusive range with ``default_rng([4243, seed])``.
+``default_rng([42, seed, 11])``, rounded the same way; their upstream gradient dO [total_q, H, D]
+(``make_grad_varlen``) from ``default_rng([42, seed, 12])``; ``varlen_lengths`` draws the sequence
+lengths uniformly from an inclusive range with ``default_rng([4243, seed])``.
 """
 from __future__ import annotations
 
@@ -160,6 +161,13 @@ def make_varlen(lens_q, lens_k, H: int, D: int, *, dtype: str, seed):
     k = rng.standard_normal((tk, H, D), dtype=np.float32)
     v = rng.standard_normal((tk, H, D), dtype=np.float32)
     return tuple(np.ascontiguousarray(cast_bits(t, dtype)) for t in (q, k, v))
+
+
+def make_grad_varlen(lens_q, H: int, D: int, *, dtype: str, seed):
+    """Stored packed upstream gradient dO [sum(lens_q), H, D] for generator ``[42, seed, 12]``."""
+    rng = np.random.default_rng([42] + ([seed] if np.isscalar(seed) else list(seed)) + [12])
+    tq = int(np.sum(lens_q))
+    return np.ascontiguousarray(cast_bits(rng.standard_normal((tq, H, D), dtype=np.float32), dtype))
 
 
 def make_workload(w: Workload, dtype: str | None = None):
