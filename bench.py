@@ -29,7 +29,9 @@ Options: --gpus N (only 1 is supported), --steps K, --warmup W, --no-cpu-baselin
            (recomputed S, dP, dV, dK, dQ) over the visible pairs, 10*D per pair = 2.5 x the forward's,
          or c3_bwd_window1024: the same through fa_bwd_ex with a sliding window of 1024 earlier keys
            (O and lse from fa_fwd_ex with that window),
-         or c3_bwd_fp32: fa_bwd on the C3 draws kept in fp32 (roofline against the fp32 MFMA peak).
+         or c3_bwd_fp32: fa_bwd on the C3 draws kept in fp32 (roofline against the fp32 MFMA peak),
+         or varlen_bwd: one step = one fa_bwd_varlen on the varlen workload's packed sequences with a
+           seeded upstream gradient (O and lse from one fa_fwd_varlen before timing).
 """
 from __future__ import annotations
 
@@ -108,6 +110,8 @@ def main():
                          dtype="fp32" if args.workload == "c3_bwd_fp32" else "bf16")
     if args.workload == "varlen":
         return bench_varlen(args)
+    if args.workload == "varlen_bwd":
+        return bench_varlen_bwd(args)
     if args.workload in VARIANTS:
         var = VARIANTS[args.workload]
         w = inputs.WORKLOADS["c3"]
@@ -395,6 +399,125 @@ def bench_varlen(args):
         "config": {"workload": "packed causal attention forward bf16, 8 sequences of lengths %s, H=%d D=%d"
                                % (list(map(int, lens)), H, D), "B": B, "H": H, "D": D, "total_tokens": total,
                    "max_seqlen": max_q, "causal": True, "scale": scale, "flop_per_step": flops},
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": roofline,
+        "cpu_baseline": cpu_baseline,
+        "parity_sample": parity,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def bench_varlen_bwd(args):
+    """One step = fa_bwd_varlen over the varlen workload's packed causal sequences; see the module notes."""
+    import numpy as np
+    import torch
+
+    import transformer_attention_fwd_amd as fa
+    from transformer_attention_fwd_amd import inputs
+
+    B, H, D = 8, 32, 128
+    lens = inputs.varlen_lengths(B, 512, 7680, seed=3)
+    cu = inputs.cu_seqlens(lens)
+    total = int(cu[-1])
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    log("bench: varlen lengths %s (total %d), backward" % (list(lens), total))
+    qh, kh, vh = inputs.make_varlen(lens, lens, H, D, dtype="bf16", seed=3)
+    doh = inputs.make_grad_varlen(lens, H, D, dtype="bf16", seed=3)
+    to_dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda")
+    q, k, v, do = to_dev(qh), to_dev(kh), to_dev(vh), to_dev(doh)
+    cu_d = torch.from_numpy(cu).to("cuda")
+    max_n = int(lens.max())
+    o, lse = fa.attention_varlen(q, k, v, cu_d, cu_d, max_n, causal=True, scale=scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty((H, total), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        st = fa.fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                              dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), cu_d.data_ptr(),
+                              cu_d.data_ptr(), B, H, total, total, max_n, max_n, D, True, scale, fa.DTYPE_BF16,
+                              stream.cuda_stream)
+        if st != fa.FA_OK:
+            raise RuntimeError("fa_bwd_varlen failed: %s %s" % (fa.status_str(st), fa.last_error()))
+
+    log("bench: warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    call_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
+    ms_per_step = ev[0][0].elapsed_time(ev[-1][1]) / args.steps
+    pairs = float(H * sum(int(n) * (int(n) + 1) // 2 for n in lens))
+    flops = 10.0 * D * pairs
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    mean_ms = float(np.mean(call_ms))
+    achieved = flops / (mean_ms * 1e-3) / 1e12
+    log("bench: %d steps, %.4f ms/step (wall %.4f), median %.4f ms, %.1f TFLOP/s"
+        % (args.steps, ms_per_step, (t1 - t0) * 1e3 / args.steps, float(np.median(call_ms)), value))
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "kernel": "fa_bwd_dq<128,bf16,causal,varlen> + fa_bwd_dkdv<128,bf16,causal,varlen> (one fa_bwd_varlen "
+                          "call)", "mean_launch_ms": round(mean_ms, 5), "launches_per_step": 2}
+    cpu_baseline = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        cores = min(16, os.cpu_count() or 1)
+        rng = np.random.default_rng([4242, 3, 13])
+        order = [divmod(int(x), H) for x in rng.permutation(B * H)]
+        t_cpu, sample_flops, picked = 0.0, 0.0, []
+        errs = {"dQ": 0.0, "dK": 0.0, "dV": 0.0}
+        mags = {"dQ": 0.0, "dK": 0.0, "dV": 0.0}
+        got_all = [t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv)]
+        for b, h in order:  # seeded (sequence, head) pairs in full, until about 10 s of oracle time
+            if t_cpu >= 10.0 and picked:
+                break
+            sl = slice(int(cu[b]), int(cu[b + 1]))
+            t_a = time.perf_counter()
+            ref = oracle.attention_bwd_ex(qh[sl][None], kh[sl][None], vh[sl][None], doh[sl][None], dtype="bf16",
+                                          layout="BSND", causal=True, scale=scale, heads=[(0, h)], nthreads=cores)
+            t_cpu += time.perf_counter() - t_a
+            picked.append([b, h])
+            nb = int(lens[b])
+            sample_flops += 10.0 * D * nb * (nb + 1) / 2
+            for name, g, r in zip(("dQ", "dK", "dV"), got_all, ref):
+                errs[name] = max(errs[name], float(np.abs(g[sl, h] - r[0]).max()))
+                mags[name] = max(mags[name], float(np.abs(r[0]).max()))
+        cpu_tflops = sample_flops / t_cpu / 1e12
+        cpu_baseline = {"value": round(cpu_tflops, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                        "sample": "%d whole (sequence, head) pairs of the same workload (dQ, dK, dV; %.3e FLOP, "
+                                  "%.1f s); full-step time at this rate %.0f s"
+                                  % (len(picked), sample_flops, t_cpu, flops / (cpu_tflops * 1e12))}
+        parity = {"pairs": picked}
+        for name in ("dQ", "dK", "dV"):
+            parity["max_abs_err_" + name] = errs[name]
+            parity["max_abs_ref_" + name] = mags[name]
+        log("bench: oracle %d pairs in %.2f s; parity %s" % (len(picked), t_cpu, parity))
+    line = {
+        "metric": "attention bwd TFLOP/s (dQ, dK, dV), packed causal sequences of mixed length, H=32 D=128",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "packed causal attention backward bf16, 8 sequences of lengths %s, H=%d D=%d"
+                               % (list(map(int, lens)), H, D), "B": B, "H": H, "D": D, "total_tokens": total,
+                   "max_seqlen": max_n, "causal": True, "scale": scale, "flop_per_step": flops},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": roofline,
         "cpu_baseline": cpu_baseline,
