@@ -255,8 +255,14 @@ def main():
         idx = torch.from_numpy(rows).to("cuda")
         o_s = o[idx[:, 0], idx[:, 1], idx[:, 2]].float().cpu().numpy().astype(np.float64)
         l_s = lse[idx[:, 0], idx[:, 1], idx[:, 2]].cpu().numpy().astype(np.float64)
-        parity = {"rows": int(len(rows)), "max_abs_dO": float(np.abs(o_s - o_ref).max()),
-                  "max_abs_dlse": float(np.abs(l_s - lse_ref).max())}
+        err = np.abs(o_s - o_ref)
+        # the bf16 bound: |dO| <= max(1e-2, one bf16 ulp of the exact value) per element (an output rounded
+        # to bf16 can sit half an ulp away before any other error)
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(o_ref), 2.0 ** -126))) - 7)
+        parity = {"rows": int(len(rows)), "max_abs_dO": float(err.max()),
+                  "max_abs_dlse": float(np.abs(l_s - lse_ref).max()),
+                  "elements_over_1e-2": int(np.sum(err > 1e-2)),
+                  "elements_over_max_1e-2_ulp": int(np.sum(err > np.maximum(1e-2, ulp)))}
         log("bench: oracle %d rows in %.2f s on %d threads; parity max|dO| %.3e max|dlse| %.3e"
             % (len(rows), t_cpu, cores, parity["max_abs_dO"], parity["max_abs_dlse"]))
 

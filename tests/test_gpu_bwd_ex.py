@@ -116,6 +116,12 @@ def test_sliding_window(window, D):
     compare_chunks(1, 3, 333, 333, D, window=window, seed=3, what="bwd_ex window")
 
 
+@pytest.mark.parametrize("window", [1, 100])
+def test_sliding_window_fp16(window):
+    compare_chunks(1, 2, 333, 333, 128, dtype="fp16", window=window, q_offset=0, chunks=[(0, 129), (129, 333)],
+                   seed=14, what="bwd_ex window fp16")
+
+
 def test_window_with_offset_and_short_keys():
     # positions 100 .. 249 against 250 keys, window 77
     compare_chunks(2, 2, 150, 250, 128, window=77, q_offset=100, seed=4, what="bwd_ex window offset")
