@@ -189,3 +189,9 @@ def test_host_pointer_rejected():
     with pytest.raises(fa.FaError) as e:
         fa.attention_bwd(x, x.clone(), x.clone(), x.clone(), lse, host)
     assert e.value.status == fa.FA_ERR_NOT_DEVICE_MEMORY
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_many_heads_short_rows(causal):
+    # B*H = 2048 (b, h) units of 17 rows: the workgroup -> unit mapping with a large, ragged grid
+    full_compare(64, 32, 17, 64, "bf16", "BSND", causal, 0.125, [17, 64, causal], "bwd many heads")

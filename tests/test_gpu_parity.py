@@ -273,3 +273,10 @@ def test_on_a_side_stream():
     o_ref, lse_ref = oracle.attention(q, k, v, dtype="bf16", layout="BHSD", causal=True, scale=0.125)
     check(o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref,
           "bf16", "side stream")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_many_heads_short_rows(dtype, causal):
+    # B*H = 2048 (b, h) units of 17 rows: the workgroup -> unit mapping with a large, ragged grid
+    full_compare(64, 32, 17, 64, dtype, "BSND", causal, 0.125, 43, "many heads %s causal=%d" % (dtype, causal))

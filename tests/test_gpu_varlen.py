@@ -101,3 +101,13 @@ def test_rows_beyond_max_seqlen_untouched():
     keep = np.r_[0:128, 300:400]
     check(o.float().cpu().numpy().astype(np.float64)[keep], lse.cpu().numpy().astype(np.float64)[:, keep],
           o_ref[keep], lse_ref[:, keep], "bf16", "varlen max_seqlen cut")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_a_thousand_short_sequences(causal):
+    # many tiny sequences (lengths 0..20): the grid's head spreading and padding with 1000 x 2 units
+    lens = inputs.varlen_lengths(1000, 0, 20, seed=24)
+    (q, k, v, cq, ck, scale), o, lse = run(lens, lens, 2, 64, "bf16", causal, 24)
+    o_ref, lse_ref = oracle.attention_varlen(q, k, v, cq, ck, dtype="bf16", causal=causal, scale=scale, nthreads=NTHREADS)
+    check(o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, "bf16",
+          "varlen 1000 sequences causal=%d" % causal)

@@ -102,3 +102,11 @@ def test_bad_offsets_skip_only_their_sequence():
     ref = oracle.attention_bwd_varlen(q[:50], k[:50], v[:50], do[:50], [0, 50], [0, 50], dtype="bf16", causal=True,
                                       scale=float(np.float32(1 / np.sqrt(D))), nthreads=NTHREADS)
     _check(tuple(t[:50] for t in out), ref, "varlen bwd bad offsets, sequence 0")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_a_thousand_short_sequences(causal):
+    # many tiny sequences: the grid's head spreading and padding with 1000 x 2 (sequence, head) units
+    lens = inputs.varlen_lengths(1000, 0, 20, seed=34)
+    got, ref = run(lens, lens, 2, 64, "bf16", causal, 34)
+    _check(got, ref, "varlen bwd 1000 sequences causal=%d" % causal)
