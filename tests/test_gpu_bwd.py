@@ -182,6 +182,37 @@ def test_c3_full_size_sampled_heads():
     check(got, ref, "bwd c3 heads %s" % heads)
 
 
+def test_c5_full_size_rows_and_properties():
+    # the 65536-token causal shape: every output finite, the two sum identities over every head, and the dQ
+    # of sampled rows against the oracle -- a row's dQ depends only on its own query, its dO row and its
+    # visible keys, so the generalised backward of that one row (at its position, over keys 0 .. i) is exact
+    w = inputs.WORKLOADS["c5"]
+    q, k, v = inputs.make_workload(w)
+    do = inputs.make_grad(w.B, w.H, w.N, w.D, layout=w.layout, dtype="bf16", seed=w.seed)
+    _say("bwd c5: inputs ready")
+    (dq, dk, dv), _ = run(q, k, v, do, "bf16", w.layout, True, w.scale)
+    for t in (dq, dk, dv):
+        assert bool(torch.isfinite(t).all())
+    dof = to_dev(do, "bf16").float()
+    sk = dk.float().sum(2).abs() / dk.float().abs().sum(2)
+    sv = (dv.float().sum(2) - dof.sum(2)).abs() / (dv.float().abs().sum(2) + dof.abs().sum(2))
+    _say("bwd c5: max relative |sum dK|=%.3e, |sum dV - sum dO|=%.3e" % (sk.max().item(), sv.max().item()))
+    assert sk.max().item() <= 2 ** -6 and sv.max().item() <= 2 ** -6
+    rows = inputs.sample_rows(w.B, w.H, w.N, 48, seed=[5, 7], heads_subset=2, rows_per_head=6)
+    got, ref = [], []
+    for b, h, i in rows:
+        b, h, i = int(b), int(h), int(i)
+        r = oracle.attention_bwd_ex(q[b:b + 1, h:h + 1, i:i + 1], k[b:b + 1, h:h + 1, :i + 1], v[b:b + 1, h:h + 1, :i + 1],
+                                    do[b:b + 1, h:h + 1, i:i + 1], dtype="bf16", layout=w.layout, causal=True,
+                                    scale=w.scale, q_offset=i, nthreads=NTHREADS)
+        ref.append(r[0][0, 0, 0])
+        got.append(f64(dq[b, h, i]))
+    got, ref = np.stack(got), np.stack(ref)
+    err, scale = np.abs(got - ref).max(), np.abs(ref).max()
+    _say("bwd c5: %d sampled dQ rows: max|err|=%.3e max|ref|=%.3e" % (len(rows), err, scale))
+    assert err <= TOL * scale + ATOL
+
+
 def test_host_pointer_rejected():
     x = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16, device="cuda")
     lse = torch.zeros(1, 1, 64, device="cuda")
