@@ -109,6 +109,30 @@ def test_wrapper_rejects_shape_mismatch_before_calling():
         fa.attention(q.double(), q.double(), q.double())
 
 
+def test_backward_wrappers_reject_bad_caller_buffers():
+    # a caller's delta or gradient buffer of the wrong shape, dtype or strides would be written past its
+    # end by the kernels: the wrappers raise before any library call
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.float16)
+    lse = torch.zeros(1, 2, 8)
+    with pytest.raises(ValueError):
+        fa.attention_bwd(q, q, q, q, lse, q, delta=torch.zeros(1, 2, 7))
+    with pytest.raises(ValueError):
+        fa.attention_bwd_ex(q, q, q, q, lse, q, delta=torch.zeros(1, 2, 8, dtype=torch.float64))
+    with pytest.raises(ValueError):
+        fa.attention_bwd_ex(q, q, q, q, lse, q, dk=torch.zeros(1, 2, 4, 64, dtype=torch.float16))
+    p = torch.zeros(12, 2, 64, dtype=torch.float16)
+    lse_p = torch.zeros(2, 12)
+    cu = torch.tensor([0, 5, 12], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        fa.attention_bwd_varlen(p, p, p, p, lse_p, p, cu, cu, 7, 7, delta=torch.zeros(12, 2))
+    with pytest.raises(ValueError):
+        fa.attention_bwd_varlen(p, p, p, p, lse_p, p, cu, cu, 7, 7, out=(p, p, torch.zeros(11, 2, 64,
+                                                                                         dtype=torch.float16)))
+    with pytest.raises(ValueError):
+        fa.attention_bwd_varlen(p, p, p, p, lse_p, p, cu, cu, 7, 7, out=(p, p, p.transpose(0, 1)))
+
+
 def test_every_kernel_stub_is_defined():
     # A kernel whose host-side stub failed to instantiate leaves an undefined __device_stub__ symbol:
     # the library would then fail to load at run time.

@@ -405,7 +405,12 @@ def attention_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_
         scale = 1.0 / math.sqrt(D)
     if delta is None:
         delta = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    if delta.shape != (H, total_q) or delta.dtype != torch.float32 or not delta.is_contiguous():
+        raise ValueError("delta must be a contiguous float32 tensor of shape [H, total_q]")
     dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    for t, like in ((dq, q), (dk, k), (dv, v)):
+        if t.shape != like.shape or t.dtype != like.dtype or not t.is_contiguous():
+            raise ValueError("out must hold contiguous tensors shaped like q, k, v")
     stream = torch.cuda.current_stream(q.device).cuda_stream if q.is_cuda else 0
     _raise_on(fa_bwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
                             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), cu_seqlens_q.data_ptr(),
@@ -441,6 +446,8 @@ def attention_bwd_ex(q, k, v, o, lse, dout, *, layout: str = "BHSD", causal: boo
         scale = 1.0 / math.sqrt(D)
     if delta is None:
         delta = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if delta.shape != (B, H, Nq) or delta.dtype != torch.float32 or not delta.is_contiguous():
+        raise ValueError("delta must be a contiguous float32 tensor of shape [B, H, Nq]")
     dq = torch.empty_like(q)
     dk = torch.zeros_like(k) if dk is None else dk
     dv = torch.zeros_like(v) if dv is None else dv
