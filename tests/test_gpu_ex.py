@@ -96,6 +96,31 @@ def test_sliding_window(dtype, window, D):
     _check_ex(o, l, o_ref, l_ref, dtype, "window %d D=%d %s %s" % (window, D, dtype, layout))
 
 
+# Windows at several sizes: ragged last query tiles (1000 rows), windows that are and are not a
+# multiple of the 64-key tile, both layouts and D, a query chunk at q_offset 512 against 1024 keys,
+# and the benchmark's window of 1024 over 4096 tokens (two heads).
+@pytest.mark.parametrize("case", [
+    dict(B=1, H=3, nq=1000, nk=1000, q_offset=0, window=256, D=128, dtype="bf16", layout="BHSD"),
+    dict(B=2, H=2, nq=1000, nk=1000, q_offset=0, window=256, D=64, dtype="fp16", layout="BSND"),
+    dict(B=1, H=3, nq=1000, nk=1000, q_offset=0, window=300, D=128, dtype="bf16", layout="BHSD"),
+    dict(B=1, H=2, nq=4096, nk=4096, q_offset=0, window=1024, D=128, dtype="bf16", layout="BHSD"),
+    dict(B=1, H=4, nq=512, nk=1024, q_offset=512, window=256, D=128, dtype="bf16", layout="BSND"),
+    dict(B=1, H=4, nq=512, nk=1024, q_offset=512, window=300, D=128, dtype="fp16", layout="BHSD"),
+])
+def test_window_sizes(case):
+    c = case
+    _say("window sizes: %s" % c)
+    q, k, v = _make_qk(c["B"], c["H"], c["nq"], c["nk"], c["D"], c["layout"], c["dtype"], seed=c["window"] + c["nq"])
+    qd, kd, vd = (to_dev(x, c["dtype"]) for x in (q, k, v))
+    scale = float(np.float32(1 / math.sqrt(c["D"])))
+    o, l = fa.attention_ex(qd, kd, vd, layout=c["layout"], causal=True, scale=scale, window=c["window"],
+                           q_offset=c["q_offset"])
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_ex(q, k, v, dtype=c["dtype"], layout=c["layout"], causal=True, scale=scale,
+                                       window=c["window"], q_offset=c["q_offset"], nthreads=NTHREADS)
+    _check_ex(o, l, o_ref, l_ref, c["dtype"], "window sizes %s" % c)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("case", [
     dict(nq=90, nk=700, q_offset=400, kv_start=128, kv_len=300, window=150),
