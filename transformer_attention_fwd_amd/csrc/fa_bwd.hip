@@ -502,6 +502,24 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
         // span fewer than 64 keys and rows, so values past +-512 hide the same rows
         const int dk0 = CAUSAL ? max(-512, min(512, -c)) : 0;
         const int dkw = WINDOW ? max(-512, min(512, wv - c)) : 0;
+        // LDS fragments are read ahead of their products: the Q and dO rows of (qq, c) pair f + RA while
+        // pair f's products run; the transposed dO and Q of d-tiles 0..TA-1 before the last query group's
+        // exponentials, then those of d-tile dt + TA while dt's products run.  A scheduling barrier after
+        // each group of reads keeps the compiler from moving them back down to their uses.
+        constexpr int NR = QGS * T::DC, RA = 3, TA = 3;
+        const int hrow = QS * hh * T::ROW_BYTES;
+        vec8 rq[RA], ro[RA], tq[TA], to[TA];
+        auto read_rows = [&](int f, vec8& a, vec8& b) __attribute__((always_inline)) {
+          const int off = hrow + 16 * (f / T::DC) * T::ROW_BYTES;
+          a = row_frag<vec8>(qs, rb[f % T::DC], off);
+          b = row_frag<vec8>(os, rb[f % T::DC], off);
+        };
+        auto read_tr = [&](int dt, vec8& a, vec8& b) __attribute__((always_inline)) {
+          a = tr_frag<T::ROW_BYTES, vec8>(os, tb[dt], hrow);
+          b = tr_frag<T::ROW_BYTES, vec8>(qs, tb[dt], hrow);
+        };
+#pragma unroll
+        for (int f = 0; f < RA; ++f) read_rows(f, rq[f], ro[f]);
         uint32_t pp[KG][4], dsp[KG][4];
 #pragma unroll
         for (int qq = 0; qq < QGS; ++qq) {
@@ -513,8 +531,10 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
           }
 #pragma unroll
           for (int c = 0; c < T::DC; ++c) {
-            const vec8 qa = row_frag<vec8>(qs, rb[c], (QS * hh + 16 * qq) * T::ROW_BYTES);
-            const vec8 oa = row_frag<vec8>(os, rb[c], (QS * hh + 16 * qq) * T::ROW_BYTES);
+            const int f = qq * T::DC + c;
+            const vec8 qa = rq[f % RA], oa = ro[f % RA];
+            if (f + RA < NR) read_rows(f + RA, rq[f % RA], ro[f % RA]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kg = 0; kg < KG; ++kg) {
               s[kg] = E::mfma(qa, kf[kg][c], s[kg]);
@@ -524,6 +544,12 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
           // lane holds queries qh0 + 16*qq + 4*g + r for key kw0 + 16*kg + li
           const f32x4_t l2 = *(const f32x4_t*)(rv + QS * hh + 16 * qq + 4 * g);
           const f32x4_t dl = *(const f32x4_t*)(rv + BQ + QS * hh + 16 * qq + 4 * g);
+          if (qq == QGS - 1) {  // after the row values, which the exponentials wait for
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int dt = 0; dt < TA; ++dt) read_tr(dt, to[dt], tq[dt]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
           float a[KG][4];
 #pragma unroll
           for (int kg = 0; kg < KG; ++kg)
@@ -560,8 +586,9 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
         // dV^T += dO^T P ;  dK^T += Q^T dS  (k index over this step's 32 queries)
 #pragma unroll
         for (int dt = 0; dt < T::DT; ++dt) {
-          const vec8 ot = tr_frag<T::ROW_BYTES, vec8>(os, tb[dt], QS * hh * T::ROW_BYTES);
-          const vec8 qtf = tr_frag<T::ROW_BYTES, vec8>(qs, tb[dt], QS * hh * T::ROW_BYTES);
+          const vec8 ot = to[dt % TA], qtf = tq[dt % TA];
+          if (dt + TA < T::DT) read_tr(dt + TA, to[dt % TA], tq[dt % TA]);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int kg = 0; kg < KG; ++kg) {
             dva[kg][dt] = E::mfma(ot, as_vec8<vec8>(pp[kg]), dva[kg][dt]);
