@@ -311,6 +311,8 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
 #pragma unroll
           for (int c = 0; c < T::DC; ++c) kf_next[c] = k_frag(kt + 1, c);
         }
+        // keeps the scheduler from moving the reads above back down next to their MFMAs
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int qg = 0; qg < T::QG; ++qg) s[qg][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -428,6 +430,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
       for (int f = 0; f < NF; ++f) {
         const vec8 vf = vring[f % VA];
         if (f + VA < NF) vring[f % VA] = v_frag(f + VA);
+        __builtin_amdgcn_sched_barrier(0);  // the same for the V^T reads
         const int kc = f / T::DT, dt = f % T::DT;
 #pragma unroll
         for (int qg = 0; qg < T::QG; ++qg) {
