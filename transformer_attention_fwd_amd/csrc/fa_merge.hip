@@ -103,15 +103,29 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const void* __restrict__ 
   float out_lse = -__builtin_inff();
   if (m != -__builtin_inff()) {
     float tot = 0.f;
-    for (int s = 0; s < n_parts; ++s) {
-      const float ls = lse_parts[s * rows + r];
-      if (ls == -__builtin_inff()) continue;  // a part without visible keys adds nothing
-      const float w = __builtin_amdgcn_exp2f((ls - m) * kLog2e);
-      tot += w;
-      float x[8];
-      Pack8<DT>::load(o_parts, s * part_elems + e, x);
+    // parts in groups of U whose loads are in flight together, summed in part order; a part without
+    // visible keys (or whose weight underflows to 0) is not loaded and adds exactly nothing
+    constexpr int U = 4;
+    for (int s0 = 0; s0 < n_parts; s0 += U) {
+      float w[U], x[U][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(w, x[i], acc[i]);
+      for (int u = 0; u < U; ++u) {
+        const int s = s0 + u;
+        const float ls = s < n_parts ? lse_parts[s * rows + r] : -__builtin_inff();
+        w[u] = ls == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((ls - m) * kLog2e);
+        if (w[u] != 0.f) {
+          Pack8<DT>::load(o_parts, s * part_elems + e, x[u]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x[u][i] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        tot += w[u];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(w[u], x[u][i], acc[i]);
+      }
     }
     const float inv = 1.0f / tot;
 #pragma unroll
