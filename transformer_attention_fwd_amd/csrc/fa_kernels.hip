@@ -197,18 +197,27 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
   const int span = (Nkv - 1) * row_bytes + T::ROW_BYTES;  // the host keeps this below 2^31
   const __amdgpu_buffer_rsrc_t kbuf = __builtin_amdgcn_make_buffer_rsrc((void*)kg_ptr, 0, span, kBufferFlags);
   const __amdgpu_buffer_rsrc_t vbuf = __builtin_amdgcn_make_buffer_rsrc((void*)vg_ptr, 0, span, kBufferFlags);
-  int voff_k[T::LOADS], voff_v[T::LOADS];
-#pragma unroll
-  for (int i = 0; i < T::LOADS; ++i) {
-    const int slot = (i * T::NW + wave) * 64 + lane;  // 16-byte slot within the LDS tile
+  // Load i of a lane fills 16-byte slot (i*NW + wave)*64 + lane of the tile, NW*64/CHUNKS rows below
+  // load 0's; both swizzles depend on the row only through bits that step leaves alone, so one lane
+  // offset per tensor serves every load and the step goes into the uniform offset.
+  int voff_k, voff_v;
+  {
+    const int slot = wave * 64 + lane;
     const int row = slot / T::CHUNKS, pc = slot % T::CHUNKS;
-    voff_k[i] = row * row_bytes + ((pc ^ T::swz_k(row)) << 4);
-    voff_v[i] = row * row_bytes + ((pc ^ T::swz_v(row)) << 4);
+    voff_k = row * row_bytes + ((pc ^ T::swz_k(row)) << 4);
+    voff_v = row * row_bytes + ((pc ^ T::swz_v(row)) << 4);
   }
+  const int load_step = (T::NW * 64 / T::CHUNKS) * row_bytes;
   // tile j of the workgroup's sequence of tiles: the first unit's tiles, then the light unit's
   auto key_of = [&](int j) __attribute__((always_inline)) { return k_begin + (j < n_kt_a ? j : j - n_kt_a) * T::BN; };
   auto issue_tile = [&](int j, uint8_t* kdst, uint8_t* vdst) {
-    issue_kv_tile<T::LOADS, T::NW>(kbuf, vbuf, voff_k, voff_v, key_of(j) * row_bytes, wave, kdst, vdst);
+    const int soff = key_of(j) * row_bytes;
+#pragma unroll
+    for (int i = 0; i < T::LOADS; ++i) {
+      const int lds_off = (i * T::NW + wave) * 1024;  // wave-uniform base; lane lands at +16*lane
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kbuf, (lds_void_t*)(kdst + lds_off), 16, voff_k, soff + i * load_step, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vbuf, (lds_void_t*)(vdst + lds_off), 16, voff_v, soff + i * load_step, 0, 0);
+    }
   };
 
   issue_tile(0, ks0, vs0);
