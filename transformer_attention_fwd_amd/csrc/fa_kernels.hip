@@ -16,7 +16,8 @@
 //     section "分块策略：不是越大越好", constraint 2.
 //
 // gfx950 design (16-bit inputs):
-//   * 4 waves x 32 queries = 128 queries per workgroup; K/V tiles of 64 keys.
+//   * 4 waves x 32 queries = 128 queries per workgroup (8 waves, 256 queries, for the paired whole
+//     causal problem); K/V tiles of 64 keys.
 //   * MFMA v_mfma_f32_16x16x32_{bf16,f16}.  The kernel computes S^T = K Q^T and O^T = V^T P^T, so a
 //     lane's accumulator registers all belong to one query (lane % 16): the softmax rescale is a
 //     per-lane scalar, row reductions are in-lane plus two cross-lane steps, and the exponentiated
@@ -68,9 +69,9 @@ __device__ __forceinline__ float quad_max(float x) {
 // ------------------------------------------------------------------------------------------------
 // 16-bit inputs (bf16 / fp16)
 // ------------------------------------------------------------------------------------------------
-template <int D>
+template <int D, int NW_ = 4>
 struct Tile16 {
-  static constexpr int NW = 4;              // waves per workgroup
+  static constexpr int NW = NW_;            // waves per workgroup
   static constexpr int QW = 32;             // queries per wave
   static constexpr int BM = NW * QW;        // queries per workgroup
   static constexpr int BN = 64;             // keys per K/V tile
@@ -123,9 +124,9 @@ __device__ __forceinline__ SeqGeom seq_geometry(const Params& p, int b, int h, i
   return sg;
 }
 
-template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW, bool VARLEN, bool PAIR>
-__global__ __launch_bounds__(256, 2) void fa_fwd_16(Params p) {
-  typedef Tile16<D> T;
+template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW, bool VARLEN, bool PAIR, int NWV>
+__global__ __launch_bounds__(64 * NWV, 8 / NWV) void fa_fwd_16(Params p) {
+  typedef Tile16<D, NWV> T;
   typedef Elem<IS_BF16> E;
   typedef typename E::vec8 vec8;
   // Two stages for K and two for V, as four separate LDS objects: with the stage fixed at compile
@@ -673,14 +674,15 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_32(Params p) {
 // ------------------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------------------
-template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW, bool VARLEN = false, bool PAIR = false>
+template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW, bool VARLEN = false, bool PAIR = false, int NWV = 4>
 static hipError_t launch16(Params p, hipStream_t stream) {
-  typedef Tile16<D> T;
+  typedef Tile16<D, NWV> T;
   p.n_qtiles = (p.Nq + T::BM - 1) / T::BM;
   if (PAIR) p.n_qtiles = (p.n_qtiles + 1) / 2;  // pairs of tiles per head
   // packed sequences: heads spread over the XCDs, the grid padded to a multiple of 8 heads
   p.n_units = p.n_qtiles * (VARLEN ? (p.B * p.H + 7) / 8 * 8 : p.B * p.H);
-  hipLaunchKernelGGL((fa_fwd_16<D, IS_BF16, CAUSAL, WINDOW, VARLEN, PAIR>), dim3(p.n_units), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((fa_fwd_16<D, IS_BF16, CAUSAL, WINDOW, VARLEN, PAIR, NWV>), dim3(p.n_units), dim3(64 * NWV), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
@@ -697,11 +699,15 @@ template <int D, bool IS_BF16>
 static hipError_t launch16_d(const Params& p, bool causal, hipStream_t stream) {
   if (!causal) return launch16<D, IS_BF16, false, false>(p, stream);
   if (p.window >= 0) return launch16<D, IS_BF16, true, true>(p, stream);
-  // the whole causal problem (every query tile sees key 0): pairs of heavy and light tiles
-  // (an even number of query tiles, each visiting an even number of 64-key tiles)
-  const int n_full = (p.Nq + Tile16<D>::BM - 1) / Tile16<D>::BM, rem = p.Nq % Tile16<D>::BM;
-  if (p.delta == 0 && p.Nq == p.Nkv && p.kv_start == 0 && n_full % 2 == 0 && (rem == 0 || rem > Tile16<D>::BN))
-    return launch16<D, IS_BF16, true, false, false, true>(p, stream);
+  // The whole causal problem (every query tile sees key 0): pairs of heavy and light tiles.  The pair
+  // loop needs an even number of query tiles, each visiting an even number of 64-key tiles: the full
+  // tiles do (BM is a multiple of 128), the last one does when the key count rounds up to an even
+  // number of key tiles.  Pairs of 256-query tiles (8 waves) first, then of 128-query tiles.
+  const bool whole = p.delta == 0 && p.Nq == p.Nkv && p.kv_start == 0;
+  const bool even_keys = ((p.Nq + Tile16<D>::BN - 1) / Tile16<D>::BN) % 2 == 0;
+  const auto pairs = [&](int bm) { return whole && even_keys && ((p.Nq + bm - 1) / bm) % 2 == 0; };
+  if (pairs(Tile16<D, 8>::BM)) return launch16<D, IS_BF16, true, false, false, true, 8>(p, stream);
+  if (pairs(Tile16<D, 4>::BM)) return launch16<D, IS_BF16, true, false, false, true, 4>(p, stream);
   return launch16<D, IS_BF16, true, false>(p, stream);
 }
 
