@@ -71,6 +71,20 @@ def kernel_sha() -> str:
     return h.hexdigest()[:16]
 
 
+def fwd_kernel_label(nq, nk, q_offset, window, chunks):
+    """Which forward kernel a causal call runs, by the library's own rule: a whole causal problem pairs
+    256-query tiles (8 waves) when ceil(N/256) and ceil(N/64) are even, else 128-query tiles (4 waves)
+    when ceil(N/128) and ceil(N/64) are even; every other call runs one 128-query tile per workgroup."""
+    if window >= 0:
+        return "fa_fwd_16<128,bf16,causal,window> (4 waves)"
+    if chunks == 1 and q_offset == 0 and nq == nk and (nq + 63) // 64 % 2 == 0:
+        if (nq + 255) // 256 % 2 == 0:
+            return "fa_fwd_16<128,bf16,causal> (paired 256-query tiles, 8 waves)"
+        if (nq + 127) // 128 % 2 == 0:
+            return "fa_fwd_16<128,bf16,causal> (paired 128-query tiles, 4 waves)"
+    return "fa_fwd_16<128,bf16,causal> (one 128-query tile per workgroup, 4 waves)"
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -210,7 +224,7 @@ def main():
             traffic = t["hbm_bytes_per_launch"]
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "fa_fwd_16<128,bf16,causal%s>" % (",window" if window >= 0 else ""),
+                "kernel": fwd_kernel_label(Nq, Nk, q_offset, window, chunks),
                 "mean_launch_ms": round(mean_attn_ms / chunks, 5), "launches_per_step": chunks,
                 "kernel_sha": kernel_sha()}
     extra = {}
