@@ -375,21 +375,22 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void fa_fwd_16(Params p) {
         }
         part[qg] = acc;
       };
-      bool slow = first_tile;  // the wave's first active tile sets the reference maximum
+      const bool first = first_tile;  // the wave's first active tile sets the reference maximum
       first_tile = false;
-      if (!slow) {
-        bool over = false;
+      // each 16-query group moves its reference only when one of its lanes needs it
+      bool slow[T::QG];
 #pragma unroll
-        for (int qg = 0; qg < T::QG; ++qg) {
+      for (int qg = 0; qg < T::QG; ++qg) {
+        slow[qg] = first;
+        if (!first) {
           expo(qg);
-          over |= part[qg] > part_limit<IS_BF16>();
+          slow[qg] = __builtin_amdgcn_ballot_w64(part[qg] > part_limit<IS_BF16>()) != 0;
         }
-        slow = __builtin_amdgcn_ballot_w64(over) != 0;
       }
-      if (slow) {
-        keep_branch();
 #pragma unroll
-        for (int qg = 0; qg < T::QG; ++qg) {
+      for (int qg = 0; qg < T::QG; ++qg) {
+        if (slow[qg]) {
+          keep_branch();
           float mx = kNegInf;
 #pragma unroll
           for (int kt = 0; kt < T::KT; ++kt)
