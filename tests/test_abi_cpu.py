@@ -109,6 +109,26 @@ def test_wrapper_rejects_shape_mismatch_before_calling():
         fa.attention(q.double(), q.double(), q.double())
 
 
+
+def test_merge_wrapper_rejects_bad_caller_outputs():
+    # fa_merge writes one part's worth of O and B*H*N lse floats: an undersized, wrong-dtype or strided
+    # out or lse would be written past its end, so the wrapper raises before any library call
+    torch = pytest.importorskip("torch")
+    parts = torch.zeros(3, 1, 2, 8, 64, dtype=torch.bfloat16)
+    lparts = torch.zeros(3, 1, 2, 8)
+    with pytest.raises(ValueError):
+        fa.merge(parts, lparts, out=torch.zeros(1, 2, 7, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        fa.merge(parts.float(), lparts, out=torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        fa.merge(parts, lparts, out=torch.zeros(1, 2, 64, 8, dtype=torch.bfloat16).transpose(2, 3))
+    with pytest.raises(ValueError):
+        fa.merge(parts, lparts, lse=torch.zeros(1, 2, 4))
+    with pytest.raises(ValueError):
+        fa.merge(parts, lparts, lse=torch.zeros(1, 2, 8, dtype=torch.float16))
+    with pytest.raises(ValueError):
+        fa.merge(parts, lparts, lse=torch.zeros(1, 8, 2).transpose(1, 2))
+
 def test_backward_wrappers_reject_bad_caller_buffers():
     # a caller's delta or gradient buffer of the wrong shape, dtype or strides would be written past its
     # end by the kernels: the wrappers raise before any library call

@@ -96,6 +96,29 @@ def test_sliding_window(dtype, window, D):
     _check_ex(o, l, o_ref, l_ref, dtype, "window %d D=%d %s %s" % (window, D, dtype, layout))
 
 
+
+@pytest.mark.parametrize("dtype,target", [("fp16", 25.0), ("bf16", 110.0)])
+@pytest.mark.parametrize("window", [50, 300])
+def test_window_negative_logits(dtype, target, window):
+    """Windows where a wave's first tile holds none of some rows' keys, with every logit far below 0
+    (Q anti-aligned with K: scale * q.k near -target).  The row's reference maximum must follow its visible
+    keys: with a placeholder of 0 for the empty start, exp2(logit) underflows (fp16 below 2^-24, fp32
+    below 2^-149) and O = 0 (fp16) or lse = -inf (bf16) came out instead of the softmax."""
+    B, H, N, D = 1, 2, 600, 128
+    scale = float(np.float32(1 / math.sqrt(D)))
+    a = math.sqrt(target / (scale * D))
+    zq, zk, v32 = inputs.draw_f32(B, H, N, D, seed=(450, window))
+    q = inputs.to_layout(inputs.cast_bits((-a + 0.25 * zq).astype(np.float32), dtype), "BHSD")
+    k = inputs.to_layout(inputs.cast_bits((a + 0.25 * zk).astype(np.float32), dtype), "BHSD")
+    v = inputs.to_layout(inputs.cast_bits(v32, dtype), "BHSD")
+    qd, kd, vd = (to_dev(x, dtype) for x in (q, k, v))
+    o, l = fa.attention_ex(qd, kd, vd, layout="BHSD", causal=True, scale=scale, window=window)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_ex(q, k, v, dtype=dtype, layout="BHSD", causal=True, scale=scale, window=window,
+                                       nthreads=NTHREADS)
+    assert float(np.max(l_ref)) < -0.5 * target, "the logits are not as negative as intended"
+    _check_ex(o, l, o_ref, l_ref, dtype, "window %d, logits near -%g, %s" % (window, target, dtype))
+
 # Windows at several sizes: ragged last query tiles (1000 rows), windows that are and are not a
 # multiple of the 64-key tile, both layouts and D, a query chunk at q_offset 512 against 1024 keys,
 # and the benchmark's window of 1024 over 4096 tokens (two heads).

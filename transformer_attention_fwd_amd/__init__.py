@@ -304,6 +304,11 @@ def merge(o_parts, lse_parts, *, layout: str = "BHSD", out=None, lse=None):
         out = torch.empty_like(o_parts[0])
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=o_parts.device)
+    # the kernel writes B*H*N*D elements of o_parts' dtype into out and B*H*N floats into lse
+    if out.shape != o_parts.shape[1:] or out.dtype != o_parts.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like one part of o_parts")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor of shape [B, H, N]")
     stream = torch.cuda.current_stream(o_parts.device).cuda_stream if o_parts.is_cuda else 0
     _raise_on(fa_merge(o_parts.data_ptr(), lse_parts.data_ptr(), S, out.data_ptr(), lse.data_ptr(), B, H, N, D,
                        _LAYOUTS[layout], _dtype_code(o_parts), stream))

@@ -1,4 +1,9 @@
-"""Build libfa.so (HIP kernels + C-ABI entry point) for gfx950, in place next to this file."""
+"""Build libfa.so (HIP kernels + C-ABI entry point) for gfx950, in place next to this file.
+
+Also builds libfa_tilecount.so, a test-only variant of the same sources compiled with FA_TILE_COUNT: its
+forward kernels record the K/V tiles every workgroup visits (tests/test_gpu_tile_visits.py).  The product
+path loads libfa.so only.
+"""
 from __future__ import annotations
 
 import os
@@ -7,6 +12,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa.so")
+LIB_TILECOUNT = os.path.join(HERE, "libfa_tilecount.so")
 SOURCES = [os.path.join(CSRC, f) for f in ("fa_kernels.hip", "fa_merge.hip", "fa_bwd.hip", "fa_bwd32.hip", "fa_api.cpp")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -18,20 +24,33 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into libfa.so (always recompiles).  Returns the library path."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS
+def _command(out: str, extra: list[str]) -> list[str]:
+    cmd = [HIPCC] + FLAGS + extra
     for src in SOURCES:
         cmd += ["-x", "hip", src]
-    cmd += ["-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    out = "\n".join(l for l in res.stdout.splitlines() if "packed-fp32-ops" not in l)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + out)
-    os.replace(tmp, LIB)
+    return cmd + ["-o", out]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into libfa.so and the test-only libfa_tilecount.so (always recompiles; the two
+    compilations run side by side).  Returns the path of libfa.so."""
+    jobs = []
+    for lib, extra in ((LIB, []), (LIB_TILECOUNT, ["-DFA_TILE_COUNT"])):
+        tmp = lib + ".tmp%d" % os.getpid()
+        cmd = _command(tmp, extra)
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        jobs.append((lib, tmp, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+    failed = []
+    for lib, tmp, proc in jobs:
+        out, _ = proc.communicate()
+        out = "\n".join(l for l in out.splitlines() if "packed-fp32-ops" not in l)
+        if proc.returncode != 0:
+            failed.append("hipcc failed for %s:\n%s" % (os.path.basename(lib), out))
+        else:
+            os.replace(tmp, lib)
+    if failed:
+        raise RuntimeError("\n".join(failed))
     return LIB
 
 

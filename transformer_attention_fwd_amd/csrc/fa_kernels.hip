@@ -57,6 +57,9 @@ constexpr float kRescaleThreshold = 8.0f;
 // exceed it, and the reference maximum moves.  P is rounded to the input type for the P.V product, so the
 // limit keeps P representable there: 2^14 for fp16 (largest finite 65504); 2^64 for bf16, whose exponent
 // range is fp32's (O, u and l accumulate in fp32: 2^16 keys x 2^64 x |v| stays far from overflow).
+// Reference maximum (log2 units) of a row that has seen no visible key: exp2 of any visible logit minus it
+// is +inf, which the limit check catches.
+constexpr float kNoKeyRef = -1.0e30f;
 template <bool IS_BF16>
 __device__ constexpr float part_limit() { return IS_BF16 ? 18446744073709551616.0f : 16384.0f; }
 __device__ __forceinline__ float quad_max(float x) {
@@ -64,6 +67,42 @@ __device__ __forceinline__ float quad_max(float x) {
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+#ifdef FA_TILE_COUNT
+// Test-only build (libfa_tilecount.so): every 16-bit forward workgroup records the K/V tiles it visits, so a
+// test can hold them against the closed form of the visibility rule.  Record of block x (kTileRecInts ints):
+// [0] b*H + h (the head slot), [1] queries per unit, [2] keys per tile, [3] queries per wave, [4] first query
+// of the first unit, [5] tiles it streams, [6] first query of a pair's light unit or -1, [7] its tiles,
+// [8 + w] tiles wave w computes on (both units), [16] waves, [17] 0 for fa_fwd_16, 1 for fa_fwd_16pp.
+__device__ int* g_tile_rec = nullptr;
+__device__ long long g_tile_rec_cap = 0;
+#endif
+constexpr int kTileRecInts = 24;
+__device__ __forceinline__ void record_tiles(int kernel, int bh, int bm, int bn, int qw, int nw, int qa, int na, int qb,
+                                             int nb, int wave, int lane, int n_act) {
+#ifdef FA_TILE_COUNT
+  int* rec = g_tile_rec;
+  if (lane == 0 && rec != nullptr && (long long)blockIdx.x < g_tile_rec_cap) {
+    int* r = rec + (size_t)blockIdx.x * kTileRecInts;
+    if (wave == 0) {
+      r[0] = bh;
+      r[1] = bm;
+      r[2] = bn;
+      r[3] = qw;
+      r[4] = qa;
+      r[5] = na;
+      r[6] = qb;
+      r[7] = nb;
+      r[16] = nw;
+      r[17] = kernel;
+    }
+    r[8 + wave] = n_act;
+  }
+#else
+  (void)kernel, (void)bh, (void)bm, (void)bn, (void)qw, (void)nw, (void)qa, (void)na, (void)qb, (void)nb, (void)wave,
+      (void)lane, (void)n_act;
+#endif
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -171,12 +210,16 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void fa_fwd_16(Params p) {
   // ---- the chunk keys this workgroup visits: from the lowest key inside the window of its first query
   // (0 without a window) to the last key visible to its last query; tiles of BN keys from k_begin ----
   const int k_begin = WINDOW ? (int)min((int64_t)Nkv, max((int64_t)0, q_wg + delta - window)) : 0;
-  const int k_last = CAUSAL ? (int)max((int64_t)-1, min((int64_t)Nkv - 1, q_wg + T::BM - 1 + delta)) : Nkv - 1;
+  // (the last key visible to the workgroup's last real query: a ragged last tile streams no further)
+  const int k_last = CAUSAL ? (int)max((int64_t)-1, min((int64_t)Nkv - 1, min(q_wg + T::BM, Nq) - 1 + delta)) : Nkv - 1;
   const int n_kt_a = k_last >= k_begin ? (k_last - k_begin) / T::BN + 1 : 0;
   // the light tile of a pair (PAIR: no window, every tile sees key 0)
   const int n_kt_b = qt_b >= 0 ? (int)min((int64_t)Nkv - 1, qt_b * T::BM + T::BM - 1 + delta) / T::BN + 1 : 0;
   const int n_kt = n_kt_a + n_kt_b;
+  const int q_wg_a = q_wg;
+  int n_act = 0;  // tiles this wave computes on (recorded by the test-only build)
   if (n_kt == 0) {  // no query of this workgroup sees any key of the chunk: O = 0, lse = -inf
+    record_tiles(0, bh, T::BM, T::BN, T::QW, T::NW, q_wg, 0, -1, 0, wave, lane, 0);
     uint16_t* og = (uint16_t*)p.o + sg.q_base;
 #pragma unroll
     for (int qg = 0; qg < T::QG; ++qg) {
@@ -302,10 +345,12 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void fa_fwd_16(Params p) {
     // the last tile of the heavy unit of a pair: the light unit's Q is loaded once S^T no longer needs
     // the heavy unit's (the state moves over to the light unit after this step)
     constexpr bool switch_unit = decltype(sw_c)::value;
-    // the wave's 32 queries see some key of this tile (causal: its first key is not after the last
+    // the wave's real queries see some key of this tile (causal: its first key is not after the last
     // query's position; window: its last key is not before the first query's window)
-    const bool active = (!CAUSAL || key0 <= q0 + T::QW - 1 + delta) && (!WINDOW || key0 + T::BN - 1 >= q0 + delta - window);
+    const bool active = q0 < Nq && (!CAUSAL || key0 <= min(q0 + T::QW, Nq) - 1 + delta) &&
+                        (!WINDOW || min(key0 + T::BN, Nkv) - 1 >= q0 + delta - window);
     if (active) {
+      ++n_act;
       // ---- S^T = K Q^T : s[qg][kt] holds keys key0 + 16*kt + 4*g + r for query q0 + 16*qg + li ----
       // the K fragments of 16-key tile kt+1 are read while tile kt's MFMAs run
       f32x4_t s[T::QG][T::KT];
@@ -397,10 +442,11 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void fa_fwd_16(Params p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[qg][kt][r]);
           mx = quad_max(mx);
-          // a row that has seen no visible key yet takes 0 as its reference (its sums stay 0 and any
-          // reference is valid until a probability would exceed the limit, which the check above catches)
+          // a row that has seen no visible key yet takes a huge negative reference: its sums stay 0, and its
+          // first visible key gives P = inf, which fails the limit check and moves the reference to the
+          // row's real maximum (a finite placeholder such as 0 could leave every later P underflowing)
           float m_new = fmaxf(m_ref[qg], mx * cexp);
-          if (m_new == kNegInf) m_new = 0.0f;
+          if (m_new == kNegInf) m_new = kNoKeyRef;
           const float alpha = __builtin_amdgcn_exp2f(m_ref[qg] - m_new);
           l_part[qg] *= alpha;
           uacc[qg] *= alpha;
@@ -500,6 +546,463 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void fa_fwd_16(Params p) {
     }
   }
   finish();
+  record_tiles(0, bh, T::BM, T::BN, T::QW, T::NW, q_wg_a, n_kt_a, PAIR ? qt_b * T::BM : -1, n_kt_b, wave, lane, n_act);
+}
+
+// ------------------------------------------------------------------------------------------------
+// 16-bit inputs, ping-pong schedule: 8 waves, whole problems without a window
+// ------------------------------------------------------------------------------------------------
+// Waves w and w + 4 share a SIMD.  Per K/V tile j every wave runs two phases, each closed by a
+// workgroup barrier:
+//   matrix phase M(j): O^T += V^T P^T of tile j-1 (its V fragments already sit in registers) while the
+//                      K fragments of tile j are read from LDS, then S^T = K Q^T of tile j;
+//   vector phase V(j): the transposing reads of tile j's V fragments into registers, then the mask and
+//                      the online softmax of S(j) into P(j).
+// Waves 4-7 run one phase behind waves 0-3, so on every SIMD one wave issues MFMAs while the other
+// computes exponentials (the formula page, section "ops-transformer 中的实现", has the matrix and
+// vector units of the Ascend core work side by side; here the two waves of a SIMD take those roles in
+// turn).  The matrix wave runs at the higher issue priority.  K/V tiles stream through a 4-stage LDS
+// ring: tile j+2 is issued once every wave is done with tile j-2, three phases before its first use; the
+// extra stage lets a vector phase end with its V reads still in flight (they are consumed in the next
+// matrix phase, one barrier before their stage is refilled).
+template <int D, bool IS_BF16, bool CAUSAL, bool PAIR>
+__global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
+  typedef Tile16<D, 8> T;
+  typedef Elem<IS_BF16> E;
+  typedef typename E::vec8 vec8;
+  // four stages for K and four for V, eight LDS objects (a stage fixed at compile time lets the compiler
+  // see that reads of one stage do not wait for the DMA filling another)
+  __shared__ __attribute__((aligned(1024))) uint8_t ks0[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks1[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks2[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t ks3[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs0[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs1[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs2[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vs3[T::TILE_BYTES];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave >> 2;  // 0: waves 0-3, 1: waves 4-7 (one phase behind)
+  const int g = lane >> 4;
+  const int li = lane & 15;
+
+  int bh, qt, qt_b = 0;
+  if constexpr (PAIR) {
+    int r;
+    unit_of(blockIdx.x, p.n_units, p.n_qtiles, false, bh, r);
+    const int n_full = (p.Nq + T::BM - 1) / T::BM;
+    qt = n_full - 1 - r;
+    qt_b = r;  // the launcher pairs only an even number of tiles
+  } else {
+    unit_of(blockIdx.x, p.n_units, p.n_qtiles, CAUSAL, bh, qt);
+  }
+  const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
+  const SeqGeom sg = seq_geometry<CAUSAL, false>(p, b, h, bh);
+  const int Nq = sg.Nq, Nkv = sg.Nkv;
+  const int64_t delta = sg.delta;
+  const int q0a = qt * T::BM + wave * T::QW;    // first query of this wave in the (first) unit
+  const int q0b = qt_b * T::BM + wave * T::QW;  // ... in the light unit of a pair
+
+  const uint16_t* __restrict__ qg_ptr = (const uint16_t*)p.q + sg.q_base;
+  const uint8_t* __restrict__ kg_ptr = (const uint8_t*)p.k + 2 * sg.kv_base;
+  const uint8_t* __restrict__ vg_ptr = (const uint8_t*)p.v + 2 * sg.kv_base;
+  uint16_t* og_ptr = (uint16_t*)p.o + sg.q_base;
+
+  // tiles of 64 keys from key 0 up to the last key visible to the unit's last query
+  const int q_wg = qt * T::BM;
+  // (the last key visible to the workgroup's last real query: a ragged last tile streams no further)
+  const int k_last = CAUSAL ? (int)max((int64_t)-1, min((int64_t)Nkv - 1, min(q_wg + T::BM, Nq) - 1 + delta)) : Nkv - 1;
+  const int n_kt_a = k_last >= 0 ? k_last / T::BN + 1 : 0;
+  const int n_kt_b = PAIR ? (int)min((int64_t)Nkv - 1, qt_b * T::BM + T::BM - 1 + delta) / T::BN + 1 : 0;
+  const int n_kt = n_kt_a + n_kt_b;
+  if (n_kt == 0) {  // no key at all (an empty chunk): O = 0, lse = -inf
+#pragma unroll
+    for (int qg = 0; qg < T::QG; ++qg) {
+      const int qi = q0a + 16 * qg + li;
+      if (qi < Nq) {
+#pragma unroll
+        for (int dt = 0; dt < T::DT; ++dt) *(u32x2_t*)(og_ptr + qi * p.stride_s + 16 * dt + 4 * g) = u32x2_t{0u, 0u};
+        if (g == 0) p.lse[sg.lse_base + qi] = kNegInf;
+      }
+    }
+    return;
+  }
+
+  // K/V tile DMA, as in fa_fwd_16: buffer loads straight into LDS, the swizzle applied on the global side
+  const int row_bytes = (int)(2 * p.stride_s);
+  const int span = (Nkv - 1) * row_bytes + T::ROW_BYTES;
+  const __amdgpu_buffer_rsrc_t kbuf = __builtin_amdgcn_make_buffer_rsrc((void*)kg_ptr, 0, span, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vbuf = __builtin_amdgcn_make_buffer_rsrc((void*)vg_ptr, 0, span, kBufferFlags);
+  int voff_k, voff_v;
+  {
+    const int slot = wave * 64 + lane;
+    const int row = slot / T::CHUNKS, pc = slot % T::CHUNKS;
+    voff_k = row * row_bytes + ((pc ^ T::swz_k(row)) << 4);
+    voff_v = row * row_bytes + ((pc ^ T::swz_v(row)) << 4);
+  }
+  const int load_step = (T::NW * 64 / T::CHUNKS) * row_bytes;
+  auto key_of = [&](int j) __attribute__((always_inline)) { return (j < n_kt_a ? j : j - n_kt_a) * T::BN; };
+  auto q0_of = [&](int j) __attribute__((always_inline)) { return (PAIR && j >= n_kt_a) ? q0b : q0a; };
+  auto kstage = [&](auto st) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int s = decltype(st)::value % 4;
+    if constexpr (s == 0) return ks0;
+    else if constexpr (s == 1) return ks1;
+    else if constexpr (s == 2) return ks2;
+    else return ks3;
+  };
+  auto vstage = [&](auto st) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int s = decltype(st)::value % 4;
+    if constexpr (s == 0) return vs0;
+    else if constexpr (s == 1) return vs1;
+    else if constexpr (s == 2) return vs2;
+    else return vs3;
+  };
+  auto issue_tile = [&](int j, uint8_t* kdst, uint8_t* vdst) __attribute__((always_inline)) {
+    const int soff = key_of(j) * row_bytes;
+#pragma unroll
+    for (int i = 0; i < T::LOADS; ++i) {
+      const int lds_off = (i * T::NW + wave) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kbuf, (lds_void_t*)(kdst + lds_off), 16, voff_k, soff + i * load_step, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vbuf, (lds_void_t*)(vdst + lds_off), 16, voff_v, soff + i * load_step, 0, 0);
+    }
+  };
+  constexpr int TILE_LOADS = 2 * T::LOADS;  // DMA instructions per wave and tile
+  constexpr int Q_LOADS = T::QG * T::DC;    // global load instructions of one Q fragment set
+
+  vec8 qf[T::QG][T::DC];
+  auto load_q = [&](int qbase) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qg = 0; qg < T::QG; ++qg) {
+      const int qrow = min(qbase + 16 * qg + li, Nq - 1);
+#pragma unroll
+      for (int c = 0; c < T::DC; ++c) {
+        u32x4_t raw = *(const u32x4_t*)(qg_ptr + qrow * p.stride_s + 32 * c + 8 * g);
+        raw ^= p.qsign;
+        qf[qg][c] = __builtin_bit_cast(vec8, raw);
+      }
+    }
+  };
+
+  const float cexp = p.c;
+  float m_ref[T::QG], l_part[T::QG];
+  f32x4_t oacc[T::QG][T::DT], uacc[T::QG];
+  auto reset = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int qg = 0; qg < T::QG; ++qg) {
+      m_ref[qg] = kNegInf;
+      l_part[qg] = 0.f;
+      uacc[qg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt) oacc[qg][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  reset();
+
+  int kb[T::DC], vb[T::DT];
+#pragma unroll
+  for (int c = 0; c < T::DC; ++c) kb[c] = li * T::ROW_BYTES + (((4 * c + g) ^ T::swz_k(li)) << 4);
+#pragma unroll
+  for (int dt = 0; dt < T::DT; ++dt) {
+    const int vrow = 4 * g + (li >> 2);
+    const int col = 16 * dt + 4 * (li & 3);
+    vb[dt] = vrow * T::ROW_BYTES + (((col >> 3) ^ T::swz_v(vrow)) << 4) + (col & 7) * 2;
+  }
+
+  auto finish = [&](int q0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qg = 0; qg < T::QG; ++qg) {
+      const float l = wave_sum_xor16_32(l_part[qg]);
+      const float inv = uacc[qg][0] > 0.0f ? 1.0f / uacc[qg][0] : 0.0f;
+      const int qi = q0 + 16 * qg + li;
+      if (qi < Nq) {
+#pragma unroll
+        for (int dt = 0; dt < T::DT; ++dt) {
+          const f32x4_t o = oacc[qg][dt] * inv;
+          u32x2_t w = {E::pack2(o[0], o[1]), E::pack2(o[2], o[3])};
+          *(u32x2_t*)(og_ptr + qi * p.stride_s + 16 * dt + 4 * g) = w;
+        }
+        if (g == 0) p.lse[sg.lse_base + qi] = (m_ref[qg] + __builtin_log2f(l)) * kLn2;
+      }
+    }
+  };
+
+  constexpr int NF = T::KC * T::DT;  // V^T fragments per tile (= K fragments per tile, KT * DC)
+  static_assert(NF == T::KT * T::DC, "one K fragment read per V fragment product");
+  // Every wave runs every tile of the workgroup's stream: on a tile wholly above its queries the mask
+  // leaves P = 0, so the products add nothing, and the barrier waits for the busiest SIMD either way.
+  constexpr int H = NF / 2;
+  vec8 vfr[H];                   // first half of the previous tile's V^T fragments (read in its vector phase)
+  uint32_t pf[T::QG][T::KC][4];  // P of the previous tile, B-operand layout
+  f32x4_t s[T::QG][T::KT];       // S^T of the current tile
+
+  // V^T fragment f of a tile (transposing reads): lanes 4e..4e+3 of each 16-lane group address row e
+  // and lane li receives column li of those rows
+  auto v_frag = [&](const uint8_t* vs, int f) __attribute__((always_inline)) {
+    const int kc = f / T::DT, dt = f % T::DT;
+    const uint8_t* a0 = vs + vb[dt] + 32 * kc * T::ROW_BYTES;
+    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)a0);
+    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(a0 + 16 * T::ROW_BYTES));
+    u32x4_t w = {__builtin_bit_cast(u32x2_t, lo)[0], __builtin_bit_cast(u32x2_t, lo)[1],
+                 __builtin_bit_cast(u32x2_t, hi)[0], __builtin_bit_cast(u32x2_t, hi)[1]};
+    return __builtin_bit_cast(vec8, w);
+  };
+  // K fragment g = c * KT + kt of a tile (row reads), in the order the S^T products use them
+  auto k_frag = [&](const uint8_t* ks, int g) __attribute__((always_inline)) {
+    return *(const vec8*)(ks + kb[g / T::KT] + 16 * (g % T::KT) * T::ROW_BYTES);
+  };
+  auto pv_mfma = [&](int f, const vec8& vf) __attribute__((always_inline)) {
+    const int kc = f / T::DT, dt = f % T::DT;
+#pragma unroll
+    for (int qg = 0; qg < T::QG; ++qg) {
+      u32x4_t w = {pf[qg][kc][0], pf[qg][kc][1], pf[qg][kc][2], pf[qg][kc][3]};
+      oacc[qg][dt] = E::mfma(vf, __builtin_bit_cast(vec8, w), oacc[qg][dt]);
+    }
+  };
+  // u += the all-ones product of P's key chunk kc (the rounded P summed per query)
+  auto u_mfma = [&](int kc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qg = 0; qg < T::QG; ++qg) {
+      u32x4_t w = {pf[qg][kc][0], pf[qg][kc][1], pf[qg][kc][2], pf[qg][kc][3]};
+      uacc[qg] = E::mfma(E::ones(), __builtin_bit_cast(vec8, w), uacc[qg]);
+    }
+  };
+  // O^T += V^T P^T of the previous tile (and u): the first half of its fragments is in registers, the
+  // second half is read from LDS behind the first half's products.  Products into one accumulator are at
+  // least 8 MFMAs apart (a dependent MFMA issued sooner waits for its predecessor's result).
+  auto pv_first = [&](const uint8_t* vs_prev, vec8 (&v2)[H]) __attribute__((always_inline)) {
+    u_mfma(0);
+#pragma unroll
+    for (int f = 0; f < H; ++f) {
+      pv_mfma(f, vfr[f]);
+      v2[f] = v_frag(vs_prev, H + f);
+      if (f == H / 2 && T::KC > 1) u_mfma(1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // Every wave issues tile j+2's DMA at the start of its matrix phase M(j) (past the stream's end it
+  // fetches the last tile again into the free stage) and waits at the end of M(j) until its share of tile
+  // j+1 has landed: at most tile j+2's loads (and the Q loads issued after them) stay in flight.  The issue
+  // and the wait sit at the same program point for both groups, a constant count.  Stage safety: tile j+2
+  // refills the stage of tile j-2, whose last readers (group 1's matrix phase M(j-1), which drains its LDS
+  // reads) finish before the barrier that precedes any wave's M(j); tile j+1 is needed from the barrier
+  // after group 1's M(j) on.
+  auto issue_next = [&](int j, auto st) __attribute__((always_inline)) {
+    constexpr int S = decltype(st)::value;
+    issue_tile(min(j + 2, n_kt - 1), kstage(std::integral_constant<int, S + 2>()),
+               vstage(std::integral_constant<int, S + 2>()));
+  };
+
+  // matrix phase M(j): P.V of tile j-1 (stage st-1), then S of tile j (stage st).  PV: there is a tile
+  // j-1 (not on the kernel's first tile, where stage st-1 holds no data yet).  QLOAD: the heavy unit's
+  // last tile, after whose S^T the light unit's Q is loaded
+  auto mphase = [&](int j, auto st, auto pv_c, auto qload_c) __attribute__((always_inline)) {
+    constexpr int S = decltype(st)::value;
+    constexpr bool PV = decltype(pv_c)::value;
+    constexpr bool QLOAD = decltype(qload_c)::value;
+    issue_next(j, st);
+    __builtin_amdgcn_s_setprio(1);
+    const uint8_t* ks = kstage(st);
+    vec8 ka[H], kc2[H];
+    if constexpr (PV) {
+      vec8 v2[H];
+      pv_first(vstage(std::integral_constant<int, S + 3>()), v2);
+#pragma unroll
+      for (int f = 0; f < H; ++f) {
+        pv_mfma(H + f, v2[f]);
+        ka[f] = k_frag(ks, f);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int f = 0; f < H; ++f) ka[f] = k_frag(ks, f);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // S^T = K Q^T, d-chunk outer (products into one accumulator KT * QG MFMAs apart); the first half of
+    // the d-chunks runs while the second half's fragments are read
+#pragma unroll
+    for (int kt = 0; kt < T::KT; ++kt)
+#pragma unroll
+      for (int qg = 0; qg < T::QG; ++qg) s[qg][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < T::DC; ++c)
+#pragma unroll
+      for (int kt = 0; kt < T::KT; ++kt) {
+        const int g = c * T::KT + kt;
+        const vec8 kf = g < H ? ka[g] : kc2[g - H];
+#pragma unroll
+        for (int qg = 0; qg < T::QG; ++qg) s[qg][kt] = E::mfma(kf, qf[qg][c], s[qg][kt]);
+        if (g < H) kc2[g] = k_frag(ks, H + g);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    if (QLOAD) load_q(q0b);
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(QLOAD ? TILE_LOADS + Q_LOADS : TILE_LOADS));
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+  };
+
+  // vector phase V(j); FIRST: the unit's first tile, which sets the reference maximum (every wave sees
+  // key 0 of a whole causal or non-causal problem)
+  auto vphase = [&](int j, auto st, auto first_c, auto qload_c) __attribute__((always_inline)) {
+    constexpr bool FIRST = decltype(first_c)::value;
+    constexpr bool QLOAD = decltype(qload_c)::value;
+    const int key0 = key_of(j);
+    const int q0 = q0_of(j);
+    const bool need_mask = (CAUSAL && key0 + T::BN - 1 > q0 + delta) || (key0 + T::BN > Nkv);
+    if (need_mask) {
+      keep_branch();
+      const int dq0 = CAUSAL ? (int)max((int64_t)-512, min((int64_t)512, q0 + delta - key0)) : 0;
+      const int kend = min(512, Nkv - key0);
+#pragma unroll
+      for (int qg = 0; qg < T::QG; ++qg) {
+        const int hi = (CAUSAL ? min(kend - 1, dq0 + 16 * qg + li) : kend - 1) - 4 * g;
+#pragma unroll
+        for (int kt = 0; kt < T::KT; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (16 * kt + r > hi) s[qg][kt][r] = kNegInf;
+      }
+    }
+    float part[T::QG];
+    auto expo = [&](int qg) __attribute__((always_inline)) {
+      const float neg_m = -m_ref[qg];
+      float acc = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < T::KT; ++kt) {
+        float pv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qg][kt][r], cexp, neg_m));
+        acc += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+        const int kc = kt >> 1, half = kt & 1;
+        pf[qg][kc][2 * half + 0] = E::pack2(pv[0], pv[1]);
+        pf[qg][kc][2 * half + 1] = E::pack2(pv[2], pv[3]);
+      }
+      part[qg] = acc;
+    };
+    bool slow[T::QG];
+#pragma unroll
+    for (int qg = 0; qg < T::QG; ++qg) {
+      if constexpr (FIRST) {
+        slow[qg] = true;
+      } else {
+        expo(qg);
+        slow[qg] = __builtin_amdgcn_ballot_w64(part[qg] > part_limit<IS_BF16>()) != 0;
+      }
+    }
+#pragma unroll
+    for (int qg = 0; qg < T::QG; ++qg) {
+      if (slow[qg]) {
+        keep_branch();
+        float mx = kNegInf;
+#pragma unroll
+        for (int kt = 0; kt < T::KT; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[qg][kt][r]);
+        mx = quad_max(mx);
+        float m_new = fmaxf(m_ref[qg], mx * cexp);
+        if (m_new == kNegInf) m_new = kNoKeyRef;  // no visible key yet (as in fa_fwd_16)
+        const float alpha = __builtin_amdgcn_exp2f(m_ref[qg] - m_new);
+        l_part[qg] *= alpha;
+        uacc[qg] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < T::DT; ++dt) oacc[qg][dt] *= alpha;
+        m_ref[qg] = m_new;
+        expo(qg);
+      }
+    }
+#pragma unroll
+    for (int qg = 0; qg < T::QG; ++qg) l_part[qg] += part[qg];
+    __builtin_amdgcn_sched_barrier(0);
+    // the first half of this tile's V^T fragments, for the next matrix phase
+    const uint8_t* vs = vstage(st);
+#pragma unroll
+    for (int f = 0; f < H; ++f) vfr[f] = v_frag(vs, f);
+    // no LDS wait: the V reads may still be in flight (the next matrix phase consumes them, a barrier
+    // before the DMA refills this stage)
+    __builtin_amdgcn_sched_barrier(0);
+    compiler_fence();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+  };
+
+  issue_tile(0, ks0, vs0);
+  issue_tile(1, ks1, vs1);
+  load_q(q0a);
+  // tile 0 has landed once at most tile 1's loads and Q's are in flight
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(TILE_LOADS + Q_LOADS));
+  lds_barrier();
+  if (grp == 1) lds_barrier();  // waves 4-7 start one phase later
+
+  const std::integral_constant<int, 0> st0;
+  const std::integral_constant<int, 1> st1;
+  const std::integral_constant<int, 2> st2;
+  const std::integral_constant<int, 3> st3;
+  const std::true_type first_c, pv_c;
+  const std::false_type later_c, noq_c;
+  // one unit, or the heavy and then the light unit of a pair.  Every unit's tile count is a multiple of 4
+  // (the launcher runs this kernel only for causal pairs of 256-query tiles of a sequence whose length is
+  // a multiple of 256, and for non-causal calls whose key count is a multiple of 256), so every unit
+  // starts in stage 0 and its tiles run in whole groups of four.  A heavy unit has at least 8 tiles.
+  auto run_unit = [&](auto unit_c) __attribute__((always_inline)) {
+    constexpr int U = decltype(unit_c)::value;
+    const int j0 = U == 0 ? 0 : n_kt_a;
+    const int j_end = U == 0 ? n_kt_a : n_kt;
+    // P.V of the previous unit's last tile (none before the first unit), S of this unit's first tile
+    mphase(j0, st0, std::integral_constant<bool, U == 1>(), noq_c);
+    if constexpr (U == 1) {  // the heavy unit's output is complete: store it and start the light unit
+      finish(q0a);
+      reset();
+    }
+    vphase(j0, st0, first_c, noq_c);
+    mphase(j0 + 1, st1, pv_c, noq_c);
+    vphase(j0 + 1, st1, later_c, noq_c);
+    mphase(j0 + 2, st2, pv_c, noq_c);
+    vphase(j0 + 2, st2, later_c, noq_c);
+    mphase(j0 + 3, st3, pv_c, noq_c);
+    vphase(j0 + 3, st3, later_c, noq_c);
+    if (j_end - j0 > 4) {
+#pragma unroll 1
+      for (int j = j0 + 4; j < j_end - 4; j += 4) {
+        mphase(j, st0, pv_c, noq_c);
+        vphase(j, st0, later_c, noq_c);
+        mphase(j + 1, st1, pv_c, noq_c);
+        vphase(j + 1, st1, later_c, noq_c);
+        mphase(j + 2, st2, pv_c, noq_c);
+        vphase(j + 2, st2, later_c, noq_c);
+        mphase(j + 3, st3, pv_c, noq_c);
+        vphase(j + 3, st3, later_c, noq_c);
+      }
+      // the unit's last four tiles; after the heavy unit's last S^T, the light unit's Q is loaded
+      const int j = j_end - 4;
+      constexpr bool QL = PAIR && U == 0;
+      const std::integral_constant<bool, QL> ql_c;
+      mphase(j, st0, pv_c, noq_c);
+      vphase(j, st0, later_c, noq_c);
+      mphase(j + 1, st1, pv_c, noq_c);
+      vphase(j + 1, st1, later_c, noq_c);
+      mphase(j + 2, st2, pv_c, noq_c);
+      vphase(j + 2, st2, later_c, noq_c);
+      mphase(j + 3, st3, pv_c, ql_c);
+      vphase(j + 3, st3, later_c, ql_c);
+    }
+  };
+  run_unit(std::integral_constant<int, 0>());
+  if constexpr (PAIR) run_unit(std::integral_constant<int, 1>());
+  // the last tile's P.V product (the second half of its V fragments from its stage, the last one)
+  __builtin_amdgcn_s_setprio(1);
+  {
+    vec8 v2[H];
+    pv_first(vstage(st3), v2);
+#pragma unroll
+    for (int f = 0; f < H; ++f) pv_mfma(H + f, v2[f]);
+  }
+  __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the refetches past the end land before the LDS is released
+  if (grp == 0) lds_barrier();  // the barrier group 1 spent idle at the start
+  finish(PAIR ? q0b : q0a);
+  // every wave computes on every tile of the stream
+  record_tiles(1, bh, T::BM, T::BN, T::QW, T::NW, q_wg, n_kt_a, PAIR ? qt_b * T::BM : -1, n_kt_b, wave, lane, n_kt);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -551,7 +1054,8 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_32(Params p) {
   }
   // chunk keys visited: as in the 16-bit kernel (may be none: then O = 0, lse = -inf)
   const int k_begin = WINDOW ? (int)min((int64_t)Nkv, max((int64_t)0, q_wg + delta - window)) : 0;
-  const int k_last = CAUSAL ? (int)max((int64_t)-1, min((int64_t)Nkv - 1, q_wg + T::BM - 1 + delta)) : Nkv - 1;
+  // (the last key visible to the workgroup's last real query: a ragged last tile streams no further)
+  const int k_last = CAUSAL ? (int)max((int64_t)-1, min((int64_t)Nkv - 1, min(q_wg + T::BM, Nq) - 1 + delta)) : Nkv - 1;
   const int n_kt = k_last >= k_begin ? (k_last - k_begin) / T::BN + 1 : 0;
   const float cexp = p.c;
   float m_ref[T::QG], l_part[T::QG];
@@ -577,7 +1081,8 @@ __global__ __launch_bounds__(256, 1) void fa_fwd_32(Params p) {
       *(float4*)(vs + row * T::LD + 4 * c4) = vv;
     }
     __syncthreads();
-    const bool active = (!CAUSAL || key0 <= q0 + T::QW - 1 + delta) && (!WINDOW || key0 + T::BN - 1 >= q0 + delta - window);
+    const bool active = q0 < Nq && (!CAUSAL || key0 <= min(q0 + T::QW, Nq) - 1 + delta) &&
+                        (!WINDOW || min(key0 + T::BN, Nkv) - 1 >= q0 + delta - window);
     if (active) {
       f32x4_t s[T::QG][T::KT];
 #pragma unroll
@@ -687,6 +1192,16 @@ static hipError_t launch16(Params p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int D, bool IS_BF16, bool CAUSAL, bool PAIR>
+static hipError_t launch16pp(Params p, hipStream_t stream) {
+  typedef Tile16<D, 8> T;
+  p.n_qtiles = (p.Nq + T::BM - 1) / T::BM;
+  if (PAIR) p.n_qtiles = (p.n_qtiles + 1) / 2;
+  p.n_units = p.n_qtiles * p.B * p.H;
+  hipLaunchKernelGGL((fa_fwd_16pp<D, IS_BF16, CAUSAL, PAIR>), dim3(p.n_units), dim3(512), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int D, bool CAUSAL, bool WINDOW>
 static hipError_t launch32(Params p, hipStream_t stream) {
   typedef Tile32<D> T;
@@ -698,7 +1213,18 @@ static hipError_t launch32(Params p, hipStream_t stream) {
 
 template <int D, bool IS_BF16>
 static hipError_t launch16_d(const Params& p, bool causal, hipStream_t stream) {
-  if (!causal) return launch16<D, IS_BF16, false, false>(p, stream);
+  // The ping-pong kernel runs non-causal calls whose query and key counts are multiples of 256 (its tiles
+  // go in groups of four 64-key tiles, and every wave of a 256-query workgroup then has rows).  Causal problems keep fa_fwd_16: the ping-pong kernel also handles whole
+  // causal problems as pairs (fa_fwd_16pp<..., true, true>) but measured slower there.
+#ifndef FA_NO_PINGPONG
+  constexpr bool kPingPong = true;
+#else
+  constexpr bool kPingPong = false;
+#endif
+  if (!causal) {
+    if (kPingPong && p.Nq % 256 == 0 && p.Nkv > 0 && p.Nkv % 256 == 0) return launch16pp<D, IS_BF16, false, false>(p, stream);
+    return launch16<D, IS_BF16, false, false>(p, stream);
+  }
   if (p.window >= 0) return launch16<D, IS_BF16, true, true>(p, stream);
   // The whole causal problem (every query tile sees key 0): pairs of heavy and light tiles.  The pair
   // loop needs an even number of query tiles, each visiting an even number of 64-key tiles: the full
@@ -739,3 +1265,13 @@ hipError_t launch_varlen(const Params& p, int dtype, int d, bool causal, hipStre
 int queries_per_workgroup(int dtype) { return dtype == kDtypeFp32 ? Tile32<64>::BM : Tile16<64>::BM; }
 
 }  // namespace fa
+
+#ifdef FA_TILE_COUNT
+// Test-only entry point of libfa_tilecount.so: the device buffer (cap records of kTileRecInts ints) that the
+// forward kernels launched after this call fill; null stops the recording.
+extern "C" __attribute__((visibility("default"))) int fa_test_set_tile_record(int* buf, long long cap) {
+  if (hipMemcpyToSymbol(HIP_SYMBOL(fa::g_tile_rec), &buf, sizeof(buf)) != hipSuccess) return 1;
+  if (hipMemcpyToSymbol(HIP_SYMBOL(fa::g_tile_rec_cap), &cap, sizeof(cap)) != hipSuccess) return 1;
+  return 0;
+}
+#endif
