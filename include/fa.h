@@ -58,6 +58,10 @@ extern "C" {
 #define FA_ERR_BAD_RANGE 11        /* fa_fwd_ex / fa_bwd_ex: key chunk outside [0, Nk], a window without
                                       causal, or |q_offset| > 2^30; fa_fwd_varlen: max_seqlen_q > total_q;
                                       fa_bwd_varlen: max_seqlen_q > total_q or max_seqlen_k > total_k */
+#define FA_ERR_SCRATCH_LIMIT 12    /* fa_bwd_noalloc: B*H*N exceeds FA_NOALLOC_MAX_ROWS */
+
+/* Rows (B*H*N) fa_bwd_noalloc accepts: the size of its per-GPU scratch array of floats (16 MiB). */
+#define FA_NOALLOC_MAX_ROWS 4194304
 
 /* Limits: 1 <= N <= 2^30, B*H <= 2^31 - 1, every tensor's byte size must fit in int64, and one head's
  * span -- (N - 1) * (bytes between consecutive positions) + D * element size -- must be below 2^31
@@ -181,6 +185,19 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
            void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t N, int64_t D, int layout,
            int causal, float scale, int dtype, void* stream);
+
+/*
+ * fa_bwd_noalloc -- fa_bwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same arguments without `delta`.  The D
+ * workspace is a static device array of the library, FA_NOALLOC_MAX_ROWS floats per GPU, held until the
+ * process ends; B*H*N beyond it returns FA_ERR_SCRATCH_LIMIT (checked with the other sizes, before any
+ * HIP call).  The call allocates nothing.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams, other threads) race and must be serialised by the caller.  Results
+ * equal fa_bwd's bit for bit.  Other checks and errors as fa_bwd.
+ */
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t D, int layout, int causal,
+                   float scale, int dtype, void* stream);
 
 /*
  * fa_bwd_ex -- the backward of fa_fwd_ex's rule: query row i at position q_offset + i, key row j at j,

@@ -18,7 +18,8 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     declared = _declared()
-    assert declared == ["fa_bwd", "fa_bwd_ex", "fa_bwd_varlen", "fa_fwd", "fa_fwd_ex", "fa_fwd_varlen", "fa_last_error",
+    assert declared == ["fa_bwd", "fa_bwd_ex", "fa_bwd_noalloc", "fa_bwd_varlen", "fa_fwd", "fa_fwd_ex", "fa_fwd_varlen",
+                        "fa_last_error",
                         "fa_merge", "fa_status_str", "fa_version"]
     out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], stdout=subprocess.PIPE,
                          text=True, check=True).stdout
@@ -38,8 +39,9 @@ def test_header_constants_match_binding():
     assert consts["FA_DTYPE_BF16"] == fa.DTYPE_BF16
     for name in ("FA_OK", "FA_ERR_NULL", "FA_ERR_BAD_DIM", "FA_ERR_BAD_LAYOUT", "FA_ERR_BAD_DTYPE",
                  "FA_ERR_UNSUPPORTED", "FA_ERR_BAD_SCALE", "FA_ERR_MISALIGNED", "FA_ERR_ALIAS",
-                 "FA_ERR_NOT_DEVICE_MEMORY", "FA_ERR_HIP", "FA_ERR_BAD_RANGE"):
+                 "FA_ERR_NOT_DEVICE_MEMORY", "FA_ERR_HIP", "FA_ERR_BAD_RANGE", "FA_ERR_SCRATCH_LIMIT"):
         assert consts[name] == getattr(fa, name), name
+    assert consts["FA_NOALLOC_MAX_ROWS"] == fa.NOALLOC_MAX_ROWS
 
 
 def test_status_strings_and_version():
@@ -250,6 +252,32 @@ def test_fa_bwd_good_arguments_reach_the_device_check():
     # every pure check passes; the fake pointers then fail the residency check (or HIP is absent)
     assert _call_b() in (fa.FA_ERR_NOT_DEVICE_MEMORY, fa.FA_ERR_HIP)
 
+
+
+# ---- fa_bwd_noalloc: pure argument checks (fa_bwd's, without delta, plus the scratch limit) ----
+def _call_n(**kw):
+    a = dict(GOOD_B)
+    a.update(kw)
+    return fa.fa_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"], a["B"],
+                             a["H"], a["N"], a["D"], a["layout"], a["causal"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), fa.FA_ERR_NULL), (dict(dv=0), fa.FA_ERR_NULL), (dict(layout=2), fa.FA_ERR_BAD_LAYOUT),
+    (dict(dtype=5), fa.FA_ERR_BAD_DTYPE), (dict(N=0), fa.FA_ERR_BAD_DIM), (dict(D=96), fa.FA_ERR_UNSUPPORTED),
+    # B*H*N one row past the scratch array, and far past it, before any HIP call
+    (dict(B=1, H=1, N=4194305), fa.FA_ERR_SCRATCH_LIMIT), (dict(B=8, H=32, N=65536), fa.FA_ERR_SCRATCH_LIMIT),
+    (dict(scale=float("nan")), fa.FA_ERR_BAD_SCALE), (dict(dk=DK + 2), fa.FA_ERR_MISALIGNED),
+    (dict(dq=Q), fa.FA_ERR_ALIAS), (dict(dv=DQ + 16), fa.FA_ERR_ALIAS),
+])
+def test_fa_bwd_noalloc_argument_checks(kw, status):
+    assert _call_n(**kw) == status
+
+
+def test_fa_bwd_noalloc_good_arguments_reach_the_device_check():
+    # the largest accepted size passes the pure checks too
+    assert _call_n() in (fa.FA_ERR_NOT_DEVICE_MEMORY, fa.FA_ERR_HIP)
+    assert _call_n(B=1, H=64, N=65536) in (fa.FA_ERR_NOT_DEVICE_MEMORY, fa.FA_ERR_HIP)
 
 # ---- fa_fwd_varlen: pure argument checks ----
 CQ, CK = 0x10000000000 + 10 * (SZ * 4), 0x10000000000 + 11 * (SZ * 4)

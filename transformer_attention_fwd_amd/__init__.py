@@ -27,6 +27,9 @@ There is no CPU or framework fallback: if ``libfa.so`` is missing the first call
         the backward C entry point, same conventions.
     attention_bwd(q, k, v, o, lse, dout, *, layout="BHSD", causal=False, scale=None, delta=None) -> (dq, dk, dv)
         fa_bwd on torch tensors: allocates dq, dk, dv (and the delta workspace unless given).
+    fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, layout, causal, scale, dtype, stream) -> status
+        fa_bwd for callers that cannot allocate: the D workspace is the library's static per-GPU array
+        (B*H*N <= NOALLOC_MAX_ROWS; calls that overlap on one GPU race on it).
     fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Nq, Nk, D, layout, causal, window, q_offset,
               kv_start, kv_len, scale, dtype, stream) -> status
     attention_bwd_ex(q, k, v, o, lse, dout, *, layout="BHSD", causal=False, scale=None, window=-1, q_offset=0,
@@ -45,7 +48,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "fa_fwd_ex", "fa_fwd_varlen", "fa_merge", "fa_bwd", "fa_bwd_ex", "fa_bwd_varlen", "attention",
+__all__ = ["fa_fwd", "fa_fwd_ex", "fa_fwd_varlen", "fa_merge", "fa_bwd", "fa_bwd_ex", "fa_bwd_varlen", "fa_bwd_noalloc", "attention",
            "attention_ex", "attention_varlen", "merge", "attention_bwd", "attention_bwd_ex", "attention_bwd_varlen", "FaError", "library_path",
            "load", "status_str", "version",
            "LAYOUT_BHSD", "LAYOUT_BSND", "DTYPE_FP32", "DTYPE_FP16", "DTYPE_BF16"]
@@ -67,6 +70,8 @@ FA_ERR_ALIAS = 8
 FA_ERR_NOT_DEVICE_MEMORY = 9
 FA_ERR_HIP = 10
 FA_ERR_BAD_RANGE = 11
+FA_ERR_SCRATCH_LIMIT = 12
+NOALLOC_MAX_ROWS = 4194304  # FA_NOALLOC_MAX_ROWS
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -108,6 +113,9 @@ def load():
         lib.fa_bwd_varlen.restype = ctypes.c_int
         lib.fa_bwd_varlen.argtypes = ([ctypes.c_void_p] * 12 + [ctypes.c_int64] * 7 + [ctypes.c_int, ctypes.c_float,
                                       ctypes.c_int, ctypes.c_void_p])
+        lib.fa_bwd_noalloc.restype = ctypes.c_int
+        lib.fa_bwd_noalloc.argtypes = ([ctypes.c_void_p] * 9 + [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_float, ctypes.c_int, ctypes.c_void_p])
         lib.fa_bwd_ex.restype = ctypes.c_int
         lib.fa_bwd_ex.argtypes = ([ctypes.c_void_p] * 10 + [ctypes.c_int64] * 5 + [ctypes.c_int, ctypes.c_int] +
                                   [ctypes.c_int64] * 4 + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p])
@@ -162,6 +170,12 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, D, layout, causal,
     return load().fa_bwd(q or None, k or None, v or None, o or None, lse or None, dout or None, dq or None,
                          dk or None, dv or None, delta or None, B, H, N, D, layout, int(causal), scale, dtype,
                          stream or None)
+
+
+def fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, layout, causal, scale, dtype, stream) -> int:
+    """fa_bwd without the delta workspace (the library's static per-GPU array; allocates nothing)."""
+    return load().fa_bwd_noalloc(q or None, k or None, v or None, o or None, lse or None, dout or None, dq or None,
+                                 dk or None, dv or None, B, H, N, D, layout, int(causal), scale, dtype, stream or None)
 
 
 def fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Nq, Nk, D, layout, causal, window, q_offset, kv_start,

@@ -11,6 +11,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/fa.h"
 #include "fa_bwd_launch.h"
 
@@ -48,6 +50,34 @@ int check_device(const void* ptr, int device) {
   return FA_OK;
 }
 
+// The D workspace of fa_bwd_noalloc: one array per GPU, held until the process ends.  Every call on a GPU
+// shares it (D is written by the backward's first kernel before its second reads it, so nothing needs
+// clearing); calls that overlap on one GPU race on it.
+constexpr int64_t kNoAllocMaxRows = FA_NOALLOC_MAX_ROWS;
+__device__ __align__(256) float scratch[kNoAllocMaxRows];
+
+// Device address of `scratch` on each device, looked up once per device (with that device current) by
+// hipGetSymbolAddress: in host code the array's name is a host-side stand-in, never a device address.
+constexpr int kMaxDevices = 64;
+float* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mutex;
+
+int scratch_of_device(int device, float** out) {
+  if (device < 0 || device >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[device] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      set_error("hipGetSymbolAddress(scratch)", e);
+      return FA_ERR_HIP;
+    }
+    g_scratch_ptr[device] = (float*)ptr;
+  }
+  *out = g_scratch_ptr[device];
+  return FA_OK;
+}
+
 }  // namespace
 
 FA_API const char* fa_status_str(int status) {
@@ -64,6 +94,7 @@ FA_API const char* fa_status_str(int status) {
     case FA_ERR_NOT_DEVICE_MEMORY: return "a pointer is not device memory of the current device";
     case FA_ERR_HIP: return "HIP runtime error";
     case FA_ERR_BAD_RANGE: return "key chunk outside [0, Nk], window without causal, q_offset out of range, or max_seqlen_q > total_q";
+    case FA_ERR_SCRATCH_LIMIT: return "fa_bwd_noalloc: B*H*N exceeds the scratch array (FA_NOALLOC_MAX_ROWS rows)";
     default: return "unknown status";
   }
 }
@@ -283,12 +314,18 @@ FA_API int fa_merge(const void* o_parts, const float* lse_parts, int64_t n_parts
   return FA_OK;
 }
 
-FA_API int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-                     void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
-                     int64_t D, int layout, int causal, int64_t window, int64_t q_offset, int64_t kv_start,
-                     int64_t kv_len, float scale, int dtype, void* stream) {
+namespace {
+
+// fa_bwd_ex; with delta == nullptr the D workspace is the library's own per-device scratch array
+// (fa_bwd_noalloc), whose size limit is checked with the other sizes and which is neither an input nor a
+// caller buffer (no aliasing or residency check).
+int bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+           void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int layout,
+           int causal, int64_t window, int64_t q_offset, int64_t kv_start, int64_t kv_len, float scale, int dtype,
+           void* stream) {
+  const bool scratch = delta == nullptr;
   // ---- pure argument checks (no HIP calls) ----
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return FA_ERR_NULL;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
   if (layout != FA_LAYOUT_BHSD && layout != FA_LAYOUT_BSND) return FA_ERR_BAD_LAYOUT;
   if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_BAD_DTYPE;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || D < 1) return FA_ERR_BAD_DIM;
@@ -308,6 +345,7 @@ FA_API int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
   const int64_t stride_bytes = (layout == FA_LAYOUT_BHSD ? D : H * D) * esize;
   if ((Nq - 1) * stride_bytes + D * esize > INT32_MAX || (Nk - 1) * stride_bytes + D * esize > INT32_MAX)
     return FA_ERR_UNSUPPORTED;
+  if (scratch && rows_q > kNoAllocMaxRows) return FA_ERR_SCRATCH_LIMIT;
   if (!isfinite(scale) || !isfinite(fabsf(scale) * 1.4426950408889634f)) return FA_ERR_BAD_SCALE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse | (uintptr_t)dout |
        (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)delta) & 15)
@@ -316,10 +354,11 @@ FA_API int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
   const int64_t in_bytes[6] = {bytes_q, bytes_k, bytes_k, bytes_q, row_bytes, bytes_q};
   const void* outs[4] = {dq, dk, dv, delta};
   const int64_t out_bytes[4] = {bytes_q, bytes_k, bytes_k, row_bytes};
-  for (int a = 0; a < 4; ++a) {
+  const int n_outs = scratch ? 3 : 4;
+  for (int a = 0; a < n_outs; ++a) {
     for (int i = 0; i < 6; ++i)
       if (overlaps(outs[a], out_bytes[a], ins[i], in_bytes[i])) return FA_ERR_ALIAS;
-    for (int c = a + 1; c < 4; ++c)
+    for (int c = a + 1; c < n_outs; ++c)
       if (overlaps(outs[a], out_bytes[a], outs[c], out_bytes[c])) return FA_ERR_ALIAS;
   }
 
@@ -334,8 +373,12 @@ FA_API int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
     const int st = check_device(ptr, device);
     if (st != FA_OK) return st;
   }
-  for (const void* ptr : outs) {
-    const int st = check_device(ptr, device);
+  for (int a = 0; a < n_outs; ++a) {
+    const int st = check_device(outs[a], device);
+    if (st != FA_OK) return st;
+  }
+  if (scratch) {
+    const int st = scratch_of_device(device, &delta);
     if (st != FA_OK) return st;
   }
 
@@ -383,6 +426,24 @@ FA_API int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
     return FA_ERR_HIP;
   }
   return FA_OK;
+}
+
+}  // namespace
+
+FA_API int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                     void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                     int64_t D, int layout, int causal, int64_t window, int64_t q_offset, int64_t kv_start,
+                     int64_t kv_len, float scale, int dtype, void* stream) {
+  if (!delta) return FA_ERR_NULL;
+  return bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Nq, Nk, D, layout, causal, window, q_offset, kv_start,
+                kv_len, scale, dtype, stream);
+}
+
+FA_API int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t D,
+                          int layout, int causal, float scale, int dtype, void* stream) {
+  return bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, nullptr, B, H, N, N, D, layout, causal, -1, 0, 0, N, scale, dtype,
+                stream);
 }
 
 FA_API int fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
