@@ -11,17 +11,29 @@ Prints ONE JSON line.  Besides the contract fields it carries:
                   traffic = HBM bytes per launch from the committed rocprofv3 counter summary
                   (profiles/traffic_fa_fwd_c3.json) when it was taken on the current kernel source, else null.
   cpu_baseline  - the fp64 oracle timed on a bounded sample of the same workload's rows on the host
-                  cores, in the same unit; the sample also checks the timed GPU output (parity_sample).
+                  cores (all the CPUs the process may use: the GPU box's share of 16), in the same unit;
+                  the sample also checks the timed GPU output (parity_sample).  The whole C3 oracle would
+                  take about a minute at that rate; the sample keeps the default run within minutes.
+  gpu_clock     - amd-smi's gfx clock (one value per XCD) and hotspot temperature before, during (sampled
+                  in a thread while the timed steps run) and after; roofline.peak_at_measured_clock and
+                  frac_at_measured_clock scale the peak by the mean clock seen during the run / 2400 MHz.
+  config.flop_per_step is the metric's count (4*B*H*N^2*D, halved when causal) for whole problems, and
+                  the visible (query, key) pairs x 4*D for windows, offsets and chunks;
+                  config.flop_visible_pairs is the visible-pair count in every case (causal C3: N(N+1)/2
+                  pairs per head, 0.024 % above N^2/2).
 
 Defaults: 50 untimed warm-up steps (the GPU clock settles over the first few tens of milliseconds),
-then 100 timed steps.
+then about 3 s of timed steps (the count from the warm-up's pace; --steps overrides).
 Options: --gpus N (only 1 is supported), --steps K, --warmup W, --no-cpu-baseline,
          --calibrate-copy (after timing, run one plain device copy of 1 GiB for counter calibration),
          --workload NAME: c3 (default), or one of the variants of the same C3 tensors:
            c3_split4      the keys in 4 chunks of 1024 (fa_fwd_ex per chunk) combined by fa_merge
            c3_window1024  causal with a sliding window of 1024 earlier keys
            prefill_cache  the last 1024 queries against all 4096 keys (bottom-right causal, q_offset 3072)
-         or c4 / c5 (the plain causal forward on those configurations),
+           c3_noncausal   the same tensors without the causal mask (the ping-pong kernel; with c3 it gives
+                          the causal speed-up the catlass page tabulates in "Causal Mask的实现差异")
+         or c4 / c5 (the plain causal forward on those configurations), or c1 (fp32, non-causal, B=1 H=2
+           N=512 D=64 BSND: its rate against the 157.3 TFLOP/s fp32 MFMA peak),
          or varlen: one step = one fa_fwd_varlen over 8 packed causal sequences (H=32 D=128 bf16) whose
            lengths are drawn uniformly from [512, 7680] (mean 4096: the C3 batch as a length mix),
          or c3_bwd: one step = one fa_bwd (dQ, dK, dV) on the C3 tensors with a seeded upstream gradient
@@ -49,6 +61,7 @@ METRIC = "attention fwd TFLOP/s + % of bf16 MFMA peak, causal B=8 H=32 N=4096 D=
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0
 PEAK_FP32_TFLOPS = 157.3  # dense fp32 MFMA
+MAX_GFX_MHZ = 2400.0  # the clock the peaks are quoted at
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fa_fwd_c3.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "transformer_attention_fwd_amd", "csrc", f)
                   for f in ("fa_kernels.hip", "fa_device.h", "fa_launch.h")]
@@ -57,6 +70,7 @@ VARIANTS = {
     "c3_split4": dict(desc="causal, keys in 4 chunks + lse merge", window=-1, chunks=4, nq=None),
     "c3_window1024": dict(desc="causal, sliding window 1024", window=1024, chunks=1, nq=None),
     "prefill_cache": dict(desc="causal, last 1024 queries vs 4096 cached keys", window=-1, chunks=1, nq=1024),
+    "c3_noncausal": dict(desc="non-causal", window=-1, chunks=1, nq=None, causal=False),
 }
 
 
@@ -71,18 +85,25 @@ def kernel_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def fwd_kernel_label(nq, nk, q_offset, window, chunks):
-    """Which forward kernel a causal call runs, by the library's own rule: a whole causal problem pairs
-    256-query tiles (8 waves) when ceil(N/256) and ceil(N/64) are even, else 128-query tiles (4 waves)
-    when ceil(N/128) and ceil(N/64) are even; every other call runs one 128-query tile per workgroup."""
+def fwd_kernel_label(nq, nk, q_offset, window, chunks, causal=True, dtype="bf16", d=128):
+    """Which forward kernel a call runs, by the library's own rule: fp32 runs fa_fwd_32; a 16-bit non-causal call
+    whose query and key counts are multiples of 256 runs the ping-pong kernel; a whole causal problem pairs
+    256-query tiles (8 waves) when ceil(N/256) and ceil(N/64) are even, else 128-query tiles (4 waves) when
+    ceil(N/128) and ceil(N/64) are even; every other call runs one 128-query tile per workgroup."""
+    if dtype == "fp32":
+        return "fa_fwd_32<%d,%s>" % (d, "causal" if causal else "non-causal")
+    if not causal:
+        if nq % 256 == 0 and nk % 256 == 0:
+            return "fa_fwd_16pp<%d,bf16,non-causal> (ping-pong, 8 waves)" % d
+        return "fa_fwd_16<%d,bf16,non-causal> (one 128-query tile per workgroup, 4 waves)" % d
     if window >= 0:
-        return "fa_fwd_16<128,bf16,causal,window> (4 waves)"
+        return "fa_fwd_16<%d,bf16,causal,window> (4 waves)" % d
     if chunks == 1 and q_offset == 0 and nq == nk and (nq + 63) // 64 % 2 == 0:
         if (nq + 255) // 256 % 2 == 0:
-            return "fa_fwd_16<128,bf16,causal> (paired 256-query tiles, 8 waves)"
+            return "fa_fwd_16<%d,bf16,causal> (paired 256-query tiles, 8 waves)" % d
         if (nq + 127) // 128 % 2 == 0:
-            return "fa_fwd_16<128,bf16,causal> (paired 128-query tiles, 4 waves)"
-    return "fa_fwd_16<128,bf16,causal> (one 128-query tile per workgroup, 4 waves)"
+            return "fa_fwd_16<%d,bf16,causal> (paired 128-query tiles, 4 waves)" % d
+    return "fa_fwd_16<%d,bf16,causal> (one 128-query tile per workgroup, 4 waves)" % d
 
 
 def log(msg):
@@ -98,10 +119,102 @@ def visible_keys(nq, nk, q_offset, window):
     return np.maximum(hi - lo + 1, 0)
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def smi_sample():
+    """GPU 0's gfx clocks (MHz, one per XCD) and hotspot temperature from amd-smi, or an error string."""
+    import subprocess
+    try:
+        out = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "-t", "--json"], stdout=subprocess.PIPE,
+                             stderr=subprocess.PIPE, text=True, timeout=30)
+        d = json.loads(out.stdout)["gpu_data"][0]
+        clocks = [v["clk"]["value"] for k, v in sorted(d["clock"].items()) if k.startswith("gfx_")]
+        temp = d["temperature"].get("hotspot", {})
+        return {"t": round(time.time(), 2), "gfx_mhz": clocks, "hotspot_c": temp.get("value") if isinstance(temp, dict)
+                else None}
+    except Exception as e:  # no amd-smi, no permission, another format: say so instead of guessing
+        return {"t": round(time.time(), 2), "error": "%s: %s" % (type(e).__name__, str(e)[:120])}
+
+
+class ClockSampler:
+    """amd-smi samples before, during (a background thread, one sample after another) and after a timed loop."""
+
+    def __enter__(self):
+        import threading
+        self.before = smi_sample()
+        self.during = []
+        self._stop = threading.Event()
+
+        def loop():
+            while not self._stop.is_set():
+                self.during.append(smi_sample())
+                self._stop.wait(0.2)
+        self._thread = threading.Thread(target=loop, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join(timeout=60)
+        self.after = smi_sample()
+        return False
+
+    def mean_clock_during(self):
+        """Mean gfx clock over the samples taken while the steps ran.  amd-smi refreshes its reading about once a
+        second, so the first samples can still repeat the idle reading taken before the run: those are left out."""
+        stale = self.before.get("gfx_mhz")
+        vals = [sum(x["gfx_mhz"]) / len(x["gfx_mhz"]) for x in self.during if x.get("gfx_mhz") and x["gfx_mhz"] != stale]
+        return sum(vals) / len(vals) if vals else None
+
+    def report(self):
+        return {"before": self.before, "during": self.during, "after": self.after,
+                "mean_gfx_mhz_during": self.mean_clock_during(), "max_gfx_mhz": MAX_GFX_MHZ}
+
+
+def finish_line(line, clocks):
+    """Clock samples, the fraction of the peak at the measured clock, and the host (for every bench line)."""
+    line["gpu_clock"] = clocks.report()
+    mhz = clocks.mean_clock_during()
+    roof = line.get("roofline") or {}
+    if mhz and roof.get("peak"):
+        adj = roof["peak"] * mhz / MAX_GFX_MHZ
+        roof["peak_at_measured_clock"] = round(adj, 1)
+        roof["frac_at_measured_clock"] = round(roof["achieved"] / adj, 4)
+    line["host"] = {"cpu_model": cpu_model(), "cpus": os.cpu_count()}
+
+
+def choose_steps(args, step_ms):
+    """--steps if given, else enough steps for about 3 s of timed work (20 to 5000)."""
+    if args.steps:
+        return args.steps
+    return int(min(5000, max(20, round(3000.0 / max(step_ms, 1e-3)))))
+
+
+def warmup_ms(step, n, torch):
+    """Run n warm-up steps; return the mean ms of the last half of them (wall clock, synchronised)."""
+    for _ in range(max(1, n // 2)):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    k = max(1, n - n // 2)
+    for _ in range(k):
+        step()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / k
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=0, help="timed steps (default: about 3 s of work)")
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -129,11 +242,17 @@ def main():
     if args.workload in VARIANTS:
         var = VARIANTS[args.workload]
         w = inputs.WORKLOADS["c3"]
-    elif args.workload in ("c4", "c5"):
+    elif args.workload in ("c1", "c4", "c5"):
         var = VARIANTS["c3"]
         w = inputs.WORKLOADS[args.workload]
     else:
         raise SystemExit("unknown workload %s" % args.workload)
+    if var.get("causal") is False:
+        import dataclasses
+        w = dataclasses.replace(w, causal=False)
+    dtype = w.dtypes[0]  # bf16, or fp32 for c1
+    dcode = fa.DTYPE_FP32 if dtype == "fp32" else fa.DTYPE_BF16
+    peak = PEAK_FP32_TFLOPS if dtype == "fp32" else PEAK_BF16_TFLOPS
     log("bench: generating %s inputs %s" % (w.name, (w.B, w.H, w.N, w.D)))
     qh, kh, vh = inputs.make_workload(w)
     B, H, N, D = w.B, w.H, w.N, w.D
@@ -143,7 +262,10 @@ def main():
     if Nq != N:
         qh = np.ascontiguousarray(qh[:, :, N - Nq:, :])  # BHSD: the last Nq query rows
     window, chunks = var["window"], var["chunks"]
-    to_dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda")
+    if dtype == "fp32":
+        to_dev = lambda x: torch.from_numpy(x).to("cuda")
+    else:
+        to_dev = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda")
     q, k, v = to_dev(qh), to_dev(kh), to_dev(vh)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, Nq), dtype=torch.float32, device="cuda")
@@ -162,45 +284,50 @@ def main():
     def attention_launches():
         if chunks == 1 and window < 0 and Nq == Nk:
             check(fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, D,
-                            layout, w.causal, w.scale, fa.DTYPE_BF16, sptr), "fa_fwd")
+                            layout, w.causal, w.scale, dcode, sptr), "fa_fwd")
         elif chunks == 1:
             check(fa.fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, Nq, Nk,
-                               D, layout, w.causal, window, q_offset, 0, Nk, w.scale, fa.DTYPE_BF16, sptr), "fa_fwd_ex")
+                               D, layout, w.causal, window, q_offset, 0, Nk, w.scale, dcode, sptr), "fa_fwd_ex")
         else:
             for c in range(chunks):
                 check(fa.fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_parts[c].data_ptr(),
                                    l_parts[c].data_ptr(), B, H, Nq, Nk, D, layout, w.causal, window, q_offset,
-                                   bounds[c], bounds[c + 1] - bounds[c], w.scale, fa.DTYPE_BF16, sptr), "fa_fwd_ex")
+                                   bounds[c], bounds[c + 1] - bounds[c], w.scale, dcode, sptr), "fa_fwd_ex")
 
     def merge_launch():
         check(fa.fa_merge(o_parts.data_ptr(), l_parts.data_ptr(), chunks, o.data_ptr(), lse.data_ptr(), B, H, Nq, D,
-                          layout, fa.DTYPE_BF16, sptr), "fa_merge")
+                          layout, dcode, sptr), "fa_merge")
 
-    log("bench: warmup %d" % args.warmup)
-    for _ in range(args.warmup):
+    def whole_step():
         attention_launches()
         if chunks > 1:
             merge_launch()
-    torch.cuda.synchronize()
+
+    log("bench: warmup %d" % args.warmup)
+    args.steps = choose_steps(args, warmup_ms(whole_step, args.warmup, torch))
 
     # timed region: K steps; HIP events on the launch stream around the attention launches and the merge
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        attention_launches()
-        ev[i][1].record(stream)
-        if chunks > 1:
-            merge_launch()
-        ev[i][2].record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with ClockSampler() as clocks:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            attention_launches()
+            ev[i][1].record(stream)
+            if chunks > 1:
+                merge_launch()
+            ev[i][2].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     attn_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
     merge_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]
     total_ms = ev[0][0].elapsed_time(ev[-1][2])
     ms_per_step = total_ms / args.steps
-    flops = float(4.0 * D * B * H * visible_keys(Nq, Nk, q_offset, window).sum()) if w.causal else w.flops()
+    # whole problems: the metric's own count, 4*B*H*N^2*D halved when causal; otherwise the visible pairs
+    pairs_flops = float(4.0 * D * B * H * visible_keys(Nq, Nk, q_offset, window).sum()) if w.causal else w.flops()
+    whole = chunks == 1 and window < 0 and Nq == Nk
+    flops = w.flops() if whole else pairs_flops
     value = flops / (ms_per_step * 1e-3) / 1e12
     mean_attn_ms = float(np.mean(attn_ms))
     achieved = flops / (mean_attn_ms * 1e-3) / 1e12
@@ -222,9 +349,9 @@ def main():
         t = json.load(open(TRAFFIC_FILE))
         if t.get("kernel_sha") == kernel_sha() and t.get("workload") == w.name:
             traffic = t["hbm_bytes_per_launch"]
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": fwd_kernel_label(Nq, Nk, q_offset, window, chunks),
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic,
+                "kernel": fwd_kernel_label(Nq, Nk, q_offset, window, chunks, w.causal, dtype, D),
                 "mean_launch_ms": round(mean_attn_ms / chunks, 5), "launches_per_step": chunks,
                 "kernel_sha": kernel_sha()}
     extra = {}
@@ -243,9 +370,9 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
 
-        cores = min(16, os.cpu_count() or 1)
+        cores = len(os.sched_getaffinity(0))  # the CPUs this process may use (the GPU machine: 16)
         torch.cuda.synchronize()
-        ref = lambda rows: oracle.attention_rows_ex(qh, kh, vh, dtype="bf16", layout=w.layout, causal=w.causal,
+        ref = lambda rows: oracle.attention_rows_ex(qh, kh, vh, dtype=dtype, layout=w.layout, causal=w.causal,
                                                     scale=w.scale, rows=rows, window=window, q_offset=q_offset,
                                                     nthreads=cores)
         # bounded sample: seeded rows, sized from a short calibration (after one warm call, which pays the
@@ -264,10 +391,14 @@ def main():
         sample_flops = float(np.sum(4.0 * D * keys))
         cpu_tflops = sample_flops / t_cpu / 1e12
         cpu_baseline = {"value": round(cpu_tflops, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                        "cpu_model": cpu_model(),
                         "sample": "%d seeded query rows of the same workload (%.3e FLOP, %.1f s); full-step time "
                                   "at this rate %.0f s" % (len(rows), sample_flops, t_cpu, flops / (cpu_tflops * 1e12))}
-        idx = torch.from_numpy(rows).to("cuda")
-        o_s = o[idx[:, 0], idx[:, 1], idx[:, 2]].float().cpu().numpy().astype(np.float64)
+        idx = torch.from_numpy(rows).to("cuda")  # (b, h, i) triples; O is [B][H][N][D] or [B][N][H][D]
+        if w.layout == "BHSD":
+            o_s = o[idx[:, 0], idx[:, 1], idx[:, 2]].float().cpu().numpy().astype(np.float64)
+        else:
+            o_s = o[idx[:, 0], idx[:, 2], idx[:, 1]].float().cpu().numpy().astype(np.float64)
         l_s = lse[idx[:, 0], idx[:, 1], idx[:, 2]].cpu().numpy().astype(np.float64)
         err = np.abs(o_s - o_ref)
         # the bf16 bound: |dO| <= max(1e-2, one bf16 ulp of the exact value) per element (an output rounded
@@ -283,12 +414,17 @@ def main():
     if args.workload == "c3":
         metric = METRIC
         workload = "causal attention forward bf16 B=%d H=%d N=%d D=%d %s" % (B, H, N, D, w.layout)
+    elif args.workload in ("c1", "c4", "c5"):
+        metric = "attention fwd TFLOP/s, %s %s, B=%d H=%d N=%d D=%d" % ("causal" if w.causal else "non-causal", dtype,
+                                                                      B, H, N, D)
+        workload = "%s attention forward %s B=%d H=%d N=%d D=%d %s" % ("causal" if w.causal else "non-causal", dtype,
+                                                                      B, H, N, D, w.layout)
     else:
         metric = "attention fwd TFLOP/s, %s, B=%d H=%d Nq=%d Nk=%d D=%d" % (var["desc"], B, H, Nq, Nk, D)
         workload = "attention forward bf16 %s B=%d H=%d Nq=%d Nk=%d D=%d %s" % (var["desc"], B, H, Nq, Nk, D,
                                                                               w.layout)
     config = {"workload": workload, "B": B, "H": H, "N": N, "D": D, "layout": w.layout, "causal": w.causal,
-              "scale": w.scale, "flop_per_step": flops}
+              "scale": w.scale, "flop_per_step": flops, "flop_visible_pairs": pairs_flops}
     if args.workload != "c3":
         config.update({"Nq": Nq, "Nk": Nk, "q_offset": q_offset, "window": window, "kv_chunks": chunks})
     line = {
@@ -302,15 +438,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": dtype,
         "data": "synthetic",
         "config": config,
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "pct_of_dtype_peak": round(100.0 * value / peak, 2),
         "roofline": roofline,
         "cpu_baseline": cpu_baseline,
         "parity_sample": parity,
     }
     line.update(extra)
+    finish_line(line, clocks)
     print(json.dumps(line), flush=True)
 
 
@@ -345,18 +483,17 @@ def bench_varlen(args):
             raise RuntimeError("fa_fwd_varlen failed: %s %s" % (fa.status_str(st), fa.last_error()))
 
     log("bench: warmup %d" % args.warmup)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    args.steps = choose_steps(args, warmup_ms(step, args.warmup, torch))
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step()
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with ClockSampler() as clocks:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            step()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     call_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
     ms_per_step = ev[0][0].elapsed_time(ev[-1][1]) / args.steps
     pairs = float(H * sum(int(n) * (int(n) + 1) // 2 for n in lens))
@@ -375,7 +512,7 @@ def bench_varlen(args):
     if not args.no_cpu_baseline:
         import oracle
 
-        cores = min(16, os.cpu_count() or 1)
+        cores = len(os.sched_getaffinity(0))  # the CPUs this process may use (the GPU machine: 16)
         rng = np.random.default_rng([4242, 3, 12])
         t_cpu, n_rows, sample_flops = 0.0, 0, 0.0
         err_o, err_l = 0.0, 0.0
@@ -424,6 +561,7 @@ def bench_varlen(args):
         "cpu_baseline": cpu_baseline,
         "parity_sample": parity,
     }
+    finish_line(line, clocks)
     print(json.dumps(line), flush=True)
 
 
@@ -461,18 +599,17 @@ def bench_varlen_bwd(args):
             raise RuntimeError("fa_bwd_varlen failed: %s %s" % (fa.status_str(st), fa.last_error()))
 
     log("bench: warmup %d" % args.warmup)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    args.steps = choose_steps(args, warmup_ms(step, args.warmup, torch))
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step()
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with ClockSampler() as clocks:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            step()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     call_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
     ms_per_step = ev[0][0].elapsed_time(ev[-1][1]) / args.steps
     pairs = float(H * sum(int(n) * (int(n) + 1) // 2 for n in lens))
@@ -491,7 +628,7 @@ def bench_varlen_bwd(args):
     if not args.no_cpu_baseline:
         import oracle
 
-        cores = min(16, os.cpu_count() or 1)
+        cores = len(os.sched_getaffinity(0))  # the CPUs this process may use (the GPU machine: 16)
         rng = np.random.default_rng([4242, 3, 13])
         order = [divmod(int(x), H) for x in rng.permutation(B * H)]
         t_cpu, sample_flops, picked = 0.0, 0.0, []
@@ -543,6 +680,7 @@ def bench_varlen_bwd(args):
         "cpu_baseline": cpu_baseline,
         "parity_sample": parity,
     }
+    finish_line(line, clocks)
     print(json.dumps(line), flush=True)
 
 
@@ -585,18 +723,17 @@ def bench_bwd(args, window=-1, dtype="bf16"):
             raise RuntimeError("fa_bwd failed: %s %s" % (fa.status_str(st), fa.last_error()))
 
     log("bench: warmup %d" % args.warmup)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    args.steps = choose_steps(args, warmup_ms(step, args.warmup, torch))
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step()
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with ClockSampler() as clocks:
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            step()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     call_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)]
     ms_per_step = ev[0][0].elapsed_time(ev[-1][1]) / args.steps
     pairs = float(B * H * visible_keys(N, N, 0, window).sum())
@@ -619,7 +756,7 @@ def bench_bwd(args, window=-1, dtype="bf16"):
     if not args.no_cpu_baseline:
         import oracle
 
-        cores = min(16, os.cpu_count() or 1)
+        cores = len(os.sched_getaffinity(0))  # the CPUs this process may use (the GPU machine: 16)
         rng = np.random.default_rng([4242, 3, 9])
         order = [divmod(int(x), H) for x in rng.permutation(B * H)]
         heads, t_cpu, got, ref = [], 0.0, [], []
@@ -669,6 +806,7 @@ def bench_bwd(args, window=-1, dtype="bf16"):
         "cpu_baseline": cpu_baseline,
         "parity_sample": parity,
     }
+    finish_line(line, clocks)
     print(json.dumps(line), flush=True)
 
 
