@@ -42,6 +42,8 @@ Options: --gpus N (only 1 is supported), --steps K, --warmup W, --no-cpu-baselin
          or c3_bwd_window1024: the same through fa_bwd_ex with a sliding window of 1024 earlier keys
            (O and lse from fa_fwd_ex with that window),
          or c3_bwd_fp32: fa_bwd on the C3 draws kept in fp32 (roofline against the fp32 MFMA peak),
+         or c3_bwd_atomic: fa_bwd_atomic on the c3_bwd tensors (dQ summed with fp32 atomic adds inside the
+           dK/dV kernel instead of a second pass over the keys),
          or varlen_bwd: one step = one fa_bwd_varlen on the varlen workload's packed sequences with a
            seeded upstream gradient (O and lse from one fa_fwd_varlen before timing).
 """
@@ -232,9 +234,10 @@ def main():
     import transformer_attention_fwd_amd as fa
     from transformer_attention_fwd_amd import inputs
 
-    if args.workload in ("c3_bwd", "c3_bwd_window1024", "c3_bwd_fp32"):
+    if args.workload in ("c3_bwd", "c3_bwd_window1024", "c3_bwd_fp32", "c3_bwd_atomic"):
         return bench_bwd(args, window=1024 if args.workload == "c3_bwd_window1024" else -1,
-                         dtype="fp32" if args.workload == "c3_bwd_fp32" else "bf16")
+                         dtype="fp32" if args.workload == "c3_bwd_fp32" else "bf16",
+                         atomic=args.workload == "c3_bwd_atomic")
     if args.workload == "varlen":
         return bench_varlen(args)
     if args.workload == "varlen_bwd":
@@ -684,8 +687,9 @@ def bench_varlen_bwd(args):
     print(json.dumps(line), flush=True)
 
 
-def bench_bwd(args, window=-1, dtype="bf16"):
-    """One step = fa_bwd (window < 0) or fa_bwd_ex with that window over the C3 batch; see the module notes."""
+def bench_bwd(args, window=-1, dtype="bf16", atomic=False):
+    """One step = fa_bwd (window < 0), fa_bwd_ex with that window, or fa_bwd_atomic over the C3 batch; see the
+    module notes."""
     import numpy as np
     import torch
 
@@ -707,11 +711,16 @@ def bench_bwd(args, window=-1, dtype="bf16"):
     o, lse = fa.attention_ex(q, k, v, layout=w.layout, causal=True, scale=w.scale, window=window)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    acc = torch.empty(q.shape, dtype=torch.float32, device="cuda") if atomic else None
     stream = torch.cuda.current_stream()
     layout = fa.LAYOUT_BHSD
 
     def step():
-        if window < 0:
+        if atomic:
+            st = fa.fa_bwd_atomic(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                  do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                                  acc.data_ptr(), B, H, N, D, layout, True, w.scale, dcode, stream.cuda_stream)
+        elif window < 0:
             st = fa.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, D, layout, True,
                            w.scale, dcode, stream.cuda_stream)
@@ -747,9 +756,12 @@ def bench_bwd(args, window=-1, dtype="bf16"):
             else "fa_bwd_dq<128,bf16,causal,window> + fa_bwd_dkdv<128,bf16,causal,window> (one fa_bwd_ex call)")
     if dtype == "fp32":
         kern = "fa_bwd_dq32<128,causal> + fa_bwd_dkdv32<128,causal> (one fa_bwd call)"
+    if atomic:
+        kern = ("fa_bwd_prep<128,bf16> + fa_bwd_dkdv<128,bf16,causal,atomic dQ> + fa_bwd_dq_convert<bf16> "
+                "(one fa_bwd_atomic call)")
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": None, "kernel": kern,
-                "mean_launch_ms": round(mean_ms, 5), "launches_per_step": 2}
+                "mean_launch_ms": round(mean_ms, 5), "launches_per_step": 3 if atomic else 2}
 
     cpu_baseline = None
     parity = None
@@ -785,7 +797,8 @@ def bench_bwd(args, window=-1, dtype="bf16"):
 
     line = {
         "metric": "attention bwd TFLOP/s (dQ, dK, dV), causal B=8 H=32 N=4096 D=128"
-                  + ("" if window < 0 else ", window %d" % window) + ("" if dtype == "bf16" else ", " + dtype),
+                  + ("" if window < 0 else ", window %d" % window) + ("" if dtype == "bf16" else ", " + dtype)
+                  + (", atomic dQ" if atomic else ""),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -797,8 +810,9 @@ def bench_bwd(args, window=-1, dtype="bf16"):
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic",
-        "config": {"workload": "causal attention backward %s B=%d H=%d N=%d D=%d %s%s"
-                               % (dtype, B, H, N, D, w.layout, "" if window < 0 else " window %d" % window),
+        "config": {"workload": "causal attention backward %s B=%d H=%d N=%d D=%d %s%s%s"
+                               % (dtype, B, H, N, D, w.layout, "" if window < 0 else " window %d" % window,
+                                  " atomic dQ" if atomic else ""),
                    "B": B, "H": H, "N": N, "D": D, "layout": w.layout, "causal": True, "scale": w.scale,
                    "window": window, "flop_per_step": flops},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),

@@ -171,7 +171,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  * dout = dL/dO, writes dq = dL/dQ, dk = dL/dK, dv = dL/dV.  The N x N probabilities are recomputed from
  * lse instead of being stored (page ai6s.net/6a0d3bfb..., section "FlashAttention在昇腾NPU上怎么跑？",
  * item 3).  No atomics: the result is the same bit for bit on every run, i.e. the deterministic mode of
- * page hwcomputing.csdn.net/6a0d4681..., section "反向传播的特殊处理"; there is no atomic mode.
+ * page hwcomputing.csdn.net/6a0d4681..., section "反向传播的特殊处理" (fa_bwd_atomic is the other mode).
  *
  * q, k, v, o, dout: same shape, layout and dtype as in fa_fwd; o is the forward's output.  Read only.
  * lse   : the forward's [B][H][N] fp32 log-sum-exp (natural log).  Read only.
@@ -185,6 +185,25 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
            void* dq, void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t N, int64_t D, int layout,
            int causal, float scale, int dtype, void* stream);
+
+/*
+ * fa_bwd_atomic -- fa_bwd's gradients in the mode that accumulates with atomics (page
+ * hwcomputing.csdn.net/6a0d4681..., section "反向传播的特殊处理": a deterministic mode next to a faster
+ * one built on atomic adds).  One kernel per 128-key tile forms dK, dV and that tile's part of dQ from a
+ * single pass over the queries; the dQ parts of all key tiles are summed into `dq_accum` with fp32
+ * atomic adds, whose order varies from run to run, so dq can differ between runs in its last bits (dk,
+ * dv and delta do not).  dq is then written from dq_accum, scaled and rounded to `dtype`.
+ *
+ * Arguments, layouts and ownership as fa_bwd, plus
+ * dq_accum : caller-owned fp32 workspace shaped like q (B*H*N*D floats, same layout); overwritten (the
+ *            call clears it first).  Must not overlap any input, output or delta.
+ * dtype    : FA_DTYPE_FP16 or FA_DTYPE_BF16 (FA_DTYPE_FP32 returns FA_ERR_UNSUPPORTED).  D in {64, 128}.
+ * The call enqueues three kernels on `stream`; results are valid after the stream synchronises.  The
+ * library allocates nothing.  Errors as fa_bwd (FA_ERR_NULL for a null delta or dq_accum).
+ */
+int fa_bwd_atomic(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                  void* dq, void* dk, void* dv, float* delta, float* dq_accum, int64_t B, int64_t H, int64_t N,
+                  int64_t D, int layout, int causal, float scale, int dtype, void* stream);
 
 /*
  * fa_bwd_noalloc -- fa_bwd for callers that cannot allocate device memory (code under HIP graph capture,

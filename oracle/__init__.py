@@ -62,6 +62,14 @@ def _load():
             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
             ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ]
+        lib.fa_oracle_bwd_head_mag_ex.restype = ctypes.c_int
+        lib.fa_oracle_bwd_head_mag_ex.argtypes = [
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ]
         lib.fa_oracle_bwd_head.restype = ctypes.c_int
         lib.fa_oracle_bwd_head.argtypes = [
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
@@ -206,12 +214,14 @@ def merge(o_parts, lse_parts):
 
 
 def attention_bwd(q, k, v, dout, *, dtype: str, layout: str, causal: bool, scale: float, heads=None,
-                  nthreads: int = 1):
+                  nthreads: int = 1, mags: bool = False):
     """Gradients (dQ, dK, dV) of O = Softmax(scale Q K^T [+ causal]) V for upstream gradient ``dout``, in fp64.
 
     q, k, v, dout: stored elements as in ``attention_rows`` (same shape, dtype and layout).
     heads: None for every head -> three arrays in the input's layout; or a sequence of (b, h) pairs ->
     three arrays [len(heads), N, D] in that order.
+    mags=True: six arrays, the gradients followed by their term magnitudes (MdQ, MdK, MdV of
+    ``fa_oracle.c``, for per-element error bounds), laid out alike.
     """
     if dtype not in DTYPES:
         raise ValueError("dtype must be one of %s" % sorted(DTYPES))
@@ -221,16 +231,24 @@ def attention_bwd(q, k, v, dout, *, dtype: str, layout: str, causal: bool, scale
             raise ValueError("q, k, v, dout must share the shape and have the itemsize of %s" % dtype)
     q, k, v, dout = (np.ascontiguousarray(t) for t in (q, k, v, dout))
     sel = [(b, h) for b in range(B) for h in range(H)] if heads is None else [tuple(x) for x in heads]
-    out = [np.empty((len(sel), N, D), dtype=np.float64) for _ in range(3)]
+    nout = 6 if mags else 3
+    out = [np.empty((len(sel), N, D), dtype=np.float64) for _ in range(nout)]
     for n, (b, h) in enumerate(sel):
-        dq, dk, dv = (np.empty((N, D), dtype=np.float64) for _ in range(3))
-        rc = _load().fa_oracle_bwd_head(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
-                                        DTYPES[dtype], LAYOUTS[layout], B, H, N, D, 1 if causal else 0,
-                                        float(scale), int(b), int(h), dq.ctypes.data, dk.ctypes.data,
-                                        dv.ctypes.data, int(nthreads))
+        res = [np.empty((N, D), dtype=np.float64) for _ in range(nout)]
+        if mags:
+            rc = _load().fa_oracle_bwd_head_mag_ex(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
+                                                   DTYPES[dtype], LAYOUTS[layout], B, H, N, N, D, 1 if causal else 0,
+                                                   -1, 0, 0, N, float(scale), int(b), int(h),
+                                                   *[r.ctypes.data for r in res], int(nthreads))
+        else:
+            rc = _load().fa_oracle_bwd_head(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
+                                            DTYPES[dtype], LAYOUTS[layout], B, H, N, D, 1 if causal else 0,
+                                            float(scale), int(b), int(h), *[r.ctypes.data for r in res],
+                                            int(nthreads))
         if rc != 0:
             raise ValueError("fa_oracle_bwd_head failed with status %d" % rc)
-        out[0][n], out[1][n], out[2][n] = dq, dk, dv
+        for x, r in zip(out, res):
+            x[n] = r
     if heads is not None:
         return tuple(out)
     res = []
@@ -281,14 +299,14 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, *, dtype: str, causal:
 
 
 def attention_bwd_varlen(q, k, v, dout, cu_seqlens_q, cu_seqlens_k, *, dtype: str, causal: bool, scale: float,
-                         nthreads: int = 1):
+                         nthreads: int = 1, mags: bool = False):
     """Gradients (dQ, dK, dV) in fp64 of ``attention_varlen``'s packed batch for upstream gradient ``dout``.
 
     q, dout: [total_q, H, D]; k, v: [total_k, H, D]; offsets as in ``attention_varlen``.  Each sequence is
     independent: its gradients are ``attention_bwd_ex`` of its own rows (the BSND layout with B = 1) under
     the aligned-ends rule, query offset Nk - Nq when causal.  A sequence without queries contributes
     dK = dV = 0 for its keys; queries without keys get dQ = 0.  Returns (dQ [total_q, H, D], dK, dV
-    [total_k, H, D]).
+    [total_k, H, D]), followed with mags=True by their term magnitudes, laid out alike.
     """
     cu_q = [int(x) for x in cu_seqlens_q]
     cu_k = [int(x) for x in cu_seqlens_k]
@@ -300,30 +318,32 @@ def attention_bwd_varlen(q, k, v, dout, cu_seqlens_q, cu_seqlens_k, *, dtype: st
         raise ValueError("q, dout must be [total_q, H, D] and k, v [total_k, H, D]")
     if cu_q[-1] != q.shape[0] or cu_k[-1] != k.shape[0]:
         raise ValueError("the last offsets must equal total_q and total_k")
-    dq = np.zeros(q.shape, dtype=np.float64)
-    dk = np.zeros(k.shape, dtype=np.float64)
-    dv = np.zeros(k.shape, dtype=np.float64)
+    shapes = (q.shape, k.shape, k.shape) * (2 if mags else 1)
+    out = [np.zeros(sh, dtype=np.float64) for sh in shapes]
     for b in range(len(cu_q) - 1):
         qs, qe, ks, ke = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
         nq, nk = qe - qs, ke - ks
         if nq == 0 or nk == 0:
             continue  # no queries (dK = dV = 0) or no keys (dQ = 0), as initialised
-        gq, gk, gv = attention_bwd_ex(q[qs:qe][None], k[ks:ke][None], v[ks:ke][None], dout[qs:qe][None], dtype=dtype,
-                                      layout="BSND", causal=causal, scale=scale, q_offset=(nk - nq) if causal else 0,
-                                      nthreads=nthreads)
-        dq[qs:qe], dk[ks:ke], dv[ks:ke] = gq[0], gk[0], gv[0]
-    return dq, dk, dv
+        res = attention_bwd_ex(q[qs:qe][None], k[ks:ke][None], v[ks:ke][None], dout[qs:qe][None], dtype=dtype,
+                               layout="BSND", causal=causal, scale=scale, q_offset=(nk - nq) if causal else 0,
+                               nthreads=nthreads, mags=mags)
+        for n, r in enumerate(res):
+            rows = slice(qs, qe) if n % 3 == 0 else slice(ks, ke)
+            out[n][rows] = r[0]
+    return tuple(out)
 
 
 def attention_bwd_ex(q, k, v, dout, *, dtype: str, layout: str, causal: bool, scale: float, window: int = -1,
-                     q_offset: int = 0, kv_start: int = 0, kv_len=None, heads=None, nthreads: int = 1):
+                     q_offset: int = 0, kv_start: int = 0, kv_len=None, heads=None, nthreads: int = 1,
+                     mags: bool = False):
     """Generalised gradients in fp64, the backward of ``attention_ex``'s rule.
 
     q, dout: [B,H,Nq,D] / [B,Nq,H,D]; k, v: [B,H,Nk,D] / [B,Nk,H,D].  P and D are those of the softmax over
     every visible key of [0, Nk) (query i at q_offset + i, causal and window as in ``attention_rows_ex``);
     the key chunk [kv_start, kv_start + kv_len) restricts what is returned: dQ sums over the chunk's keys
     only, and dK, dV are 0 outside the chunk.  heads=None -> arrays in the input layout; a sequence of
-    (b, h) -> arrays [len(heads), Nq or Nk, D].
+    (b, h) -> arrays [len(heads), Nq or Nk, D].  mags=True: the three term magnitudes follow the gradients.
     """
     if dtype not in DTYPES:
         raise ValueError("dtype must be one of %s" % sorted(DTYPES))
@@ -338,21 +358,23 @@ def attention_bwd_ex(q, k, v, dout, *, dtype: str, layout: str, causal: bool, sc
         kv_len = Nk - kv_start
     q, k, v, dout = (np.ascontiguousarray(t) for t in (q, k, v, dout))
     sel = [(b, h) for b in range(B) for h in range(H)] if heads is None else [tuple(x) for x in heads]
-    dqs = np.empty((len(sel), Nq, D)); dks = np.empty((len(sel), Nk, D)); dvs = np.empty((len(sel), Nk, D))
+    rows = (Nq, Nk, Nk) * (2 if mags else 1)
+    acc = [np.empty((len(sel), n, D)) for n in rows]
     for n, (b, h) in enumerate(sel):
-        dq, dk, dv = np.empty((Nq, D)), np.empty((Nk, D)), np.empty((Nk, D))
-        rc = _load().fa_oracle_bwd_head_ex(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
-                                           DTYPES[dtype], LAYOUTS[layout], B, H, Nq, Nk, D, 1 if causal else 0,
-                                           int(window), int(q_offset), int(kv_start), int(kv_len), float(scale),
-                                           int(b), int(h), dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
-                                           int(nthreads))
+        res = [np.empty((r, D)) for r in rows]
+        ptrs = [r.ctypes.data for r in res] + ([] if mags else [None, None, None])
+        rc = _load().fa_oracle_bwd_head_mag_ex(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
+                                               DTYPES[dtype], LAYOUTS[layout], B, H, Nq, Nk, D, 1 if causal else 0,
+                                               int(window), int(q_offset), int(kv_start), int(kv_len), float(scale),
+                                               int(b), int(h), *ptrs, int(nthreads))
         if rc != 0:
             raise ValueError("fa_oracle_bwd_head_ex failed with status %d" % rc)
-        dqs[n], dks[n], dvs[n] = dq, dk, dv
+        for x, r in zip(acc, res):
+            x[n] = r
     if heads is not None:
-        return dqs, dks, dvs
+        return tuple(acc)
     out = []
-    for g, n in ((dqs, Nq), (dks, Nk), (dvs, Nk)):
+    for g, n in zip(acc, rows):
         g = g.reshape(B, H, n, D)
         if layout == "BSND":
             g = np.ascontiguousarray(g.transpose(0, 2, 1, 3))

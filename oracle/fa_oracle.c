@@ -269,6 +269,18 @@ int fa_oracle_rows(const void* q, const void* k, const void* v, int dtype, int l
  * over disjoint chunks covering [0, Nk), the partial dQ give the full dQ: the backward of attention
  * computed in key chunks whose partial results were merged through their lse (page ai6s.net/
  * 6a0d3bfb..., section "ops-transformer仓库里还有什么？", ring / block-wise attention).
+ *
+ * Term magnitudes (fa_oracle_bwd_head_mag_ex; test infrastructure for per-element error bounds, not part
+ * of the gradient): next to each gradient element, the sum of the absolute values of the terms of its
+ * defining sum above, where every dS_ij is counted with the size of what D_i is made of --
+ * D_i = sum_d dO_id O_id = sum_d sum_j dO_id P_ij v_jd has the magnitude A_i = sum_d |dO_id| sum_j P_ij |v_jd|,
+ * so a relative perturbation of the stored O moves dS_ij by at most P_ij A_i times that size:
+ *
+ *   MdQ_id = |scale| sum_j |k_jd| (|dS_ij| + P_ij A_i)
+ *   MdK_jd = |scale| sum_i |q_id| (|dS_ij| + P_ij A_i)
+ *   MdV_jd = sum_i P_ij |dO_id|
+ *
+ * over the same (i, j) pairs as the gradients.  Each is at least the absolute value of its gradient.
  * ---------------------------------------------------------------------------------------------
  */
 typedef struct {
@@ -278,6 +290,7 @@ typedef struct {
     int64_t window, q_offset, kv_start, kv_len;
     double scale;
     double *dq, *dk, *dv; /* dq: Nq x D shared (rows are disjoint); dk, dv: this worker's Nk x D */
+    double *mq, *mk, *mv; /* the term magnitudes, laid out as dq, dk, dv; all NULL when not asked for */
     int64_t first, last;
     int status;
 } orc_bwd_job;
@@ -295,15 +308,19 @@ static void* orc_bwd_worker(void* arg) {
     double* dorow = (double*)malloc(sizeof(double) * (size_t)D);
     double* p = (double*)malloc(sizeof(double) * (size_t)Nk);
     double* dp = (double*)malloc(sizeof(double) * (size_t)Nk);
-    if (!qrow || !dorow || !p || !dp) {
-        free(qrow); free(dorow); free(p); free(dp);
+    double* pv = (double*)malloc(sizeof(double) * (size_t)D); /* sum_j P_ij |v_jd| (magnitudes only) */
+    if (!qrow || !dorow || !p || !dp || !pv) {
+        free(qrow); free(dorow); free(p); free(dp); free(pv);
         J->status = -1;
         return NULL;
     }
+    const int mags = J->mq != NULL;
     const int64_t c0 = J->kv_start, c1 = J->kv_start + J->kv_len; /* the chunk */
     for (int64_t i = J->first; i < J->last; ++i) {
         double* dqi = J->dq + i * D;
         for (int64_t d = 0; d < D; ++d) dqi[d] = 0.0;
+        if (mags)
+            for (int64_t d = 0; d < D; ++d) J->mq[i * D + d] = 0.0;
         /* visible keys jbeg .. jend-1 of the full softmax */
         const int64_t qpos = i + J->q_offset;
         int64_t jbeg = 0, jend = Nk;
@@ -336,6 +353,14 @@ static void* orc_bwd_worker(void* arg) {
             dp[j] = dot;
             Di += p[j] * dp[j];
         }
+        /* magnitude of D_i's expansion: A_i = sum_d |dO_id| sum_j P_ij |v_jd| */
+        double Ai = 0.0;
+        if (mags) {
+            for (int64_t d = 0; d < D; ++d) pv[d] = 0.0;
+            for (int64_t j = jbeg; j < jend; ++j)
+                for (int64_t d = 0; d < D; ++d) pv[d] += p[j] * fabs(orc_load(J->v, J->dtype, orc_bwd_index(J, Nk, j, d)));
+            for (int64_t d = 0; d < D; ++d) Ai += fabs(dorow[d]) * pv[d];
+        }
         /* dS and the three gradients, over the visible keys of the chunk */
         const int64_t kb = jbeg > c0 ? jbeg : c0, ke = jend < c1 ? jend : c1;
         for (int64_t j = kb; j < ke; ++j) {
@@ -347,22 +372,37 @@ static void* orc_bwd_worker(void* arg) {
                 dkj[d] += J->scale * ds * qrow[d];
                 dvj[d] += p[j] * dorow[d];
             }
+            if (mags) {
+                const double w = fabs(J->scale) * (fabs(ds) + p[j] * Ai);
+                double* mqi = J->mq + i * D;
+                double* mkj = J->mk + j * D;
+                double* mvj = J->mv + j * D;
+                for (int64_t d = 0; d < D; ++d) {
+                    mqi[d] += w * fabs(orc_load(J->k, J->dtype, orc_bwd_index(J, Nk, j, d)));
+                    mkj[d] += w * fabs(qrow[d]);
+                    mvj[d] += p[j] * fabs(dorow[d]);
+                }
+            }
         }
     }
-    free(qrow); free(dorow); free(p); free(dp);
+    free(qrow); free(dorow); free(p); free(dp); free(pv);
     return NULL;
 }
 
 /*
  * Generalised gradients of head (b, h): dq (Nq x D), dk and dv (Nk x D; rows outside the chunk 0),
- * row-major fp64, under the rule described above.  q, dout: [B][H][Nq][D] or [B][Nq][H][D]; k, v:
- * [B][H][Nk][D] or [B][Nk][H][D].  Returns 0 on success, -2 on a bad argument, -1 if memory ran out.
+ * row-major fp64, under the rule described above, and, when mq, mk, mv are all given, the term
+ * magnitudes laid out the same way (all three NULL: not computed).  q, dout: [B][H][Nq][D] or
+ * [B][Nq][H][D]; k, v: [B][H][Nk][D] or [B][Nk][H][D].  Returns 0 on success, -2 on a bad argument, -1
+ * if memory ran out.
  */
-int fa_oracle_bwd_head_ex(const void* q, const void* k, const void* v, const void* dout, int dtype, int layout,
-                          int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal, int64_t window,
-                          int64_t q_offset, int64_t kv_start, int64_t kv_len, double scale, int64_t b, int64_t h,
-                          double* dq, double* dk, double* dv, int nthreads) {
+int fa_oracle_bwd_head_mag_ex(const void* q, const void* k, const void* v, const void* dout, int dtype, int layout,
+                              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal, int64_t window,
+                              int64_t q_offset, int64_t kv_start, int64_t kv_len, double scale, int64_t b, int64_t h,
+                              double* dq, double* dk, double* dv, double* mq, double* mk, double* mv, int nthreads) {
     if (!q || !k || !v || !dout || !dq || !dk || !dv) return -2;
+    const int mags = mq != NULL;
+    if ((mk != NULL) != mags || (mv != NULL) != mags) return -2;
     if (dtype < 0 || dtype > 3 || layout < 0 || layout > 1) return -2;
     if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || D < 1 || b < 0 || b >= B || h < 0 || h >= H) return -2;
     if (kv_start < 0 || kv_len < 0 || kv_start + kv_len > Nk) return -2;
@@ -373,7 +413,8 @@ int fa_oracle_bwd_head_ex(const void* q, const void* k, const void* v, const voi
     orc_bwd_job* jobs = (orc_bwd_job*)calloc((size_t)nthreads, sizeof(orc_bwd_job));
     pthread_t* tids = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
     char* running = (char*)calloc((size_t)nthreads, 1);
-    double* part = (double*)calloc((size_t)nthreads * 2 * (size_t)(Nk * D), sizeof(double));
+    const int nparts = mags ? 4 : 2; /* per worker: dk, dv (and mk, mv) */
+    double* part = (double*)calloc((size_t)nthreads * nparts * (size_t)(Nk * D), sizeof(double));
     if (!jobs || !tids || !running || !part) {
         free(jobs); free(tids); free(running); free(part);
         return -1;
@@ -387,8 +428,13 @@ int fa_oracle_bwd_head_ex(const void* q, const void* k, const void* v, const voi
         J->q_offset = q_offset; J->kv_start = kv_start; J->kv_len = kv_len;
         J->scale = scale;
         J->dq = dq;
-        J->dk = part + (size_t)(2 * t) * (size_t)(Nk * D);
-        J->dv = part + (size_t)(2 * t + 1) * (size_t)(Nk * D);
+        J->dk = part + (size_t)(nparts * t) * (size_t)(Nk * D);
+        J->dv = part + (size_t)(nparts * t + 1) * (size_t)(Nk * D);
+        if (mags) {
+            J->mq = mq;
+            J->mk = part + (size_t)(nparts * t + 2) * (size_t)(Nk * D);
+            J->mv = part + (size_t)(nparts * t + 3) * (size_t)(Nk * D);
+        }
         J->first = Nq * t / nthreads;
         J->last = Nq * (t + 1) / nthreads;
     }
@@ -412,9 +458,26 @@ int fa_oracle_bwd_head_ex(const void* q, const void* k, const void* v, const voi
         }
         dk[e] = sk;
         dv[e] = sv;
+        if (mags) {
+            double mks = 0.0, mvs = 0.0;
+            for (int t = 0; t < nthreads; ++t) {
+                mks += jobs[t].mk[e];
+                mvs += jobs[t].mv[e];
+            }
+            mk[e] = mks;
+            mv[e] = mvs;
+        }
     }
     free(jobs); free(tids); free(running); free(part);
     return status;
+}
+
+int fa_oracle_bwd_head_ex(const void* q, const void* k, const void* v, const void* dout, int dtype, int layout,
+                          int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int causal, int64_t window,
+                          int64_t q_offset, int64_t kv_start, int64_t kv_len, double scale, int64_t b, int64_t h,
+                          double* dq, double* dk, double* dv, int nthreads) {
+    return fa_oracle_bwd_head_mag_ex(q, k, v, dout, dtype, layout, B, H, Nq, Nk, D, causal, window, q_offset, kv_start,
+                                     kv_len, scale, b, h, dq, dk, dv, NULL, NULL, NULL, nthreads);
 }
 
 /*

@@ -18,7 +18,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     declared = _declared()
-    assert declared == ["fa_bwd", "fa_bwd_ex", "fa_bwd_noalloc", "fa_bwd_varlen", "fa_fwd", "fa_fwd_ex", "fa_fwd_varlen",
+    assert declared == ["fa_bwd", "fa_bwd_atomic", "fa_bwd_ex", "fa_bwd_noalloc", "fa_bwd_varlen", "fa_fwd", "fa_fwd_ex", "fa_fwd_varlen",
                         "fa_last_error",
                         "fa_merge", "fa_status_str", "fa_version"]
     out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], stdout=subprocess.PIPE,
@@ -278,6 +278,38 @@ def test_fa_bwd_noalloc_good_arguments_reach_the_device_check():
     # the largest accepted size passes the pure checks too
     assert _call_n() in (fa.FA_ERR_NOT_DEVICE_MEMORY, fa.FA_ERR_HIP)
     assert _call_n(B=1, H=64, N=65536) in (fa.FA_ERR_NOT_DEVICE_MEMORY, fa.FA_ERR_HIP)
+
+
+# ---- fa_bwd_atomic: fa_bwd's checks plus the fp32 dq_accum workspace ----
+ACC = 0x10000000000 + 12 * (SZ * 4)
+
+
+def _call_a(acc=ACC, **kw):
+    a = dict(GOOD_B)
+    a.update(kw)
+    return fa.fa_bwd_atomic(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"], a["delta"],
+                            acc, a["B"], a["H"], a["N"], a["D"], a["layout"], a["causal"], a["scale"], a["dtype"],
+                            a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(acc=0), fa.FA_ERR_NULL), (dict(delta=0), fa.FA_ERR_NULL), (dict(q=0), fa.FA_ERR_NULL),
+    (dict(layout=2), fa.FA_ERR_BAD_LAYOUT), (dict(dtype=5), fa.FA_ERR_BAD_DTYPE), (dict(N=0), fa.FA_ERR_BAD_DIM),
+    (dict(D=96), fa.FA_ERR_UNSUPPORTED), (dict(dtype=0), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), fa.FA_ERR_BAD_SCALE), (dict(acc=ACC + 4), fa.FA_ERR_MISALIGNED),
+    # the workspace holds 2 x 64 x 64 floats (32 KiB): it must clear every input, output and delta
+    (dict(acc=Q), fa.FA_ERR_ALIAS), (dict(acc=DQ - 2 * 64 * 64 * 4 + 16), fa.FA_ERR_ALIAS),
+    (dict(acc=DL + 16), fa.FA_ERR_ALIAS), (dict(acc=DV), fa.FA_ERR_ALIAS), (dict(dq=Q), fa.FA_ERR_ALIAS),
+])
+def test_fa_bwd_atomic_argument_checks(kw, status):
+    assert _call_a(**kw) == status
+
+
+def test_fa_bwd_atomic_good_arguments_reach_the_device_check():
+    assert _call_a() in (fa.FA_ERR_NOT_DEVICE_MEMORY, fa.FA_ERR_HIP)
+    # a workspace right after dq (its 16 KiB of bf16) does not overlap it
+    assert _call_a(acc=DQ + 2 * 64 * 64 * 2) in (fa.FA_ERR_NOT_DEVICE_MEMORY, fa.FA_ERR_HIP)
+
 
 # ---- fa_fwd_varlen: pure argument checks ----
 CQ, CK = 0x10000000000 + 10 * (SZ * 4), 0x10000000000 + 11 * (SZ * 4)

@@ -57,6 +57,10 @@ int main(void) {
                 fa_bwd_noalloc((void*)16, (void*)32, (void*)48, (void*)64, lse_host, (void*)80, (void*)96, (void*)112,
                                (void*)128, 1, 1, (int64_t)FA_NOALLOC_MAX_ROWS + 1, 64, FA_LAYOUT_BHSD, 1, 0.125f,
                                FA_DTYPE_BF16, NULL), FA_ERR_SCRATCH_LIMIT);
+  bad |= expect("fa_bwd_atomic fp32",
+                fa_bwd_atomic((void*)16, (void*)32, (void*)48, (void*)64, lse_host, (void*)80, (void*)96, (void*)112,
+                              (void*)128, lse_host, (float*)144, 1, 1, 4, 64, FA_LAYOUT_BHSD, 1, 0.125f, FA_DTYPE_FP32,
+                              NULL), FA_ERR_UNSUPPORTED);
   printf(bad ? "FAIL\n" : "OK version %d\n", fa_version());
   return bad;
 }

@@ -1,29 +1,10 @@
 """GPU parity of the backward pass (fa_bwd through the C ABI) against the oracle's fp64 gradients.
 
 The GPU side runs the library's forward first (its O and lse are the backward's inputs), then fa_bwd;
-the oracle computes dQ, dK, dV from Q, K, V and dO alone, by the chain rule.
-
-Tolerance, per gradient tensor g and compared set: max |g_gpu - g_ref| <= 1e-2 * max |g_ref| + 1e-5.  Each
-gradient element is an fp32 sum of products in which one factor (P for dV, dS for dQ and dK) was rounded
-to the 16-bit input format, and the element is rounded to that format once more at the end: two
-roundings of relative size <= 2^-9 (bf16; 2^-12 for fp16), i.e. about 4e-3 of the largest magnitude
-when the rounding errors of many terms do not cancel.  D_i is taken from the forward's rounded O, whose
-error (<= 1e-2) enters dS only through P_ij * dD_i and so shifts dQ_i and dK_j by at most
-|scale| * |dD_i| times an average of key (query) rows.  1e-2 of the tensor's scale -- the forward's
-16-bit bound, taken relative to the output's magnitude -- leaves a factor of about 2.5 over the sum of
-these budgets, while a dropped term, a wrong sign or a wrong mask moves elements by O(max |g|).  The
-absolute 1e-5 covers gradients that vanish exactly (one visible key: dQ = dK = 0): P is evaluated in fp32
-as exp2(scale log2(e) q.k - lse log2(e)), whose argument carries an error of about 2^-24 |scale q.k|, so
-such a P is 1 - O(1e-7) and the vanishing dS becomes O(1e-7) instead of 0.
-
-fp32 inputs: max |g_gpu - g_ref| <= 2e-4 * max |g_ref| + 1e-5.  Every factor and sum is fp32 (unit
-roundoff u = 2^-24 = 6.0e-8): a gradient element sums n <= 1024 terms here, each with a few u from its
-factors and, through P = exp2(c s - lse log2 e), an argument error of about |c s| u <= 32 u; recursive
-summation adds at most n u of the sum of magnitudes.  That is < 1.2e-4 of the sum of |terms|, which for
-these inputs stays within about 1.5x the largest |g|; a wrong term or mask still moves elements by O(max).
-The absolute 1e-5 covers gradients that vanish exactly (one visible key): there dS = P (dP - D) is the
-difference of two fp32 evaluations of sum_d dO_d v_d (dP from the products, D from the rounded O),
-about sqrt(D) u |dO| |v| ~ 1e-6, times scale |k|.
+the oracle computes dQ, dK, dV from Q, K, V and dO alone, by the chain rule, with each element's term
+magnitude beside it.  Every element must lie within the per-element bound of tests/bwd_bound.py,
+(2 u + c eps) M + 1e-6, derived there from the kernels' roundings (u the 16-bit unit roundoff, 0 for fp32
+inputs; M the element's term magnitude).
 """
 import os
 import sys
@@ -35,12 +16,10 @@ import torch
 import oracle
 import transformer_attention_fwd_amd as fa
 from transformer_attention_fwd_amd import inputs
+from tests import bwd_bound
 
 pytestmark = pytest.mark.gpu
 NTHREADS = min(16, os.cpu_count() or 1)
-TOL = 1e-2
-ATOL = 1e-5
-TOL32, ATOL32 = 2e-4, 1e-5
 
 
 def _say(msg):
@@ -64,14 +43,8 @@ def run(q, k, v, do, dtype, layout, causal, scale):
     return (dq, dk, dv), (o, lse)
 
 
-def check(got, ref, what, dtype="bf16"):
-    tol, atol = (TOL32, ATOL32) if dtype == "fp32" else (TOL, ATOL)
-    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
-        assert np.all(np.isfinite(g)), "%s %s: non-finite" % (what, name)
-        err = np.abs(g - r).max()
-        scale = np.abs(r).max()
-        _say("%s %s: max|err|=%.3e max|ref|=%.3e ratio=%.2e" % (what, name, err, scale, err / max(scale, 1e-30)))
-        assert err <= tol * scale + atol, "%s %s: max error %.3e over %.3e" % (what, name, err, tol * scale + atol)
+def check(got, ref, what, dtype, n, d, abs_term=bwd_bound.ATOL):
+    bwd_bound.check_all(got, ref, dtype, n, d, what, abs_term)
 
 
 def f64(t):
@@ -83,8 +56,9 @@ def full_compare(B, H, N, D, dtype, layout, causal, scale, seed, what, qk_mult=1
     do = inputs.make_grad(B, H, N, D, layout=layout, dtype=dtype, seed=seed)
     _say("%s: B=%d H=%d N=%d D=%d %s %s causal=%d" % (what, B, H, N, D, dtype, layout, causal))
     got, _ = run(q, k, v, do, dtype, layout, causal, scale)
-    ref = oracle.attention_bwd(q, k, v, do, dtype=dtype, layout=layout, causal=causal, scale=scale, nthreads=NTHREADS)
-    check([f64(t) for t in got], ref, what, dtype)
+    ref = oracle.attention_bwd(q, k, v, do, dtype=dtype, layout=layout, causal=causal, scale=scale, nthreads=NTHREADS,
+                               mags=True)
+    check([f64(t) for t in got], ref, what, dtype, N, D, bwd_bound.atol(dtype, N, scale, q, k, do))
     return got
 
 
@@ -127,12 +101,13 @@ def test_scale_values(scale):
 
 
 def test_single_key_rows():
-    # N = 1: P = 1, so dQ = dK = 0 (up to the fp32 evaluation of P, see the module notes) and dV = dO
-    # (P = 1 - O(1e-7) times a stored dO rounds back to it)
+    # N = 1: P = 1, so dQ = dK = 0 up to the fp32 evaluation of P (exp2 of an argument with an error of
+    # about 2^-24 |scale q.k|, so P = 1 - O(1e-7)) and dS = P (dP - D), the difference of two fp32
+    # evaluations of dO . v, O(1e-6); and dV = dO (P = 1 - O(1e-7) times a stored dO rounds back to it)
     q, k, v = inputs.make(2, 3, 1, 64, layout="BHSD", dtype="bf16", seed=14)
     do = inputs.make_grad(2, 3, 1, 64, layout="BHSD", dtype="bf16", seed=14)
     (dq, dk, dv), _ = run(q, k, v, do, "bf16", "BHSD", True, 0.125)
-    assert dq.abs().max().item() <= ATOL and dk.abs().max().item() <= ATOL
+    assert dq.abs().max().item() <= 1e-5 and dk.abs().max().item() <= 1e-5
     assert torch.equal(dv, to_dev(do, "bf16"))
 
 
@@ -177,9 +152,9 @@ def test_c3_full_size_sampled_heads():
     rng = np.random.default_rng([4242, 3, 7])
     heads = [divmod(int(x), w.H) for x in rng.choice(w.B * w.H, size=2, replace=False)]
     ref = oracle.attention_bwd(q, k, v, do, dtype="bf16", layout=w.layout, causal=True, scale=w.scale, heads=heads,
-                               nthreads=NTHREADS)
+                               nthreads=NTHREADS, mags=True)
     got = [np.stack([f64(t[b, h]) for (b, h) in heads]) for t in (dq, dk, dv)]
-    check(got, ref, "bwd c3 heads %s" % heads)
+    check(got, ref, "bwd c3 heads %s" % heads, "bf16", w.N, w.D)
 
 
 def test_c5_full_size_rows_and_properties():
@@ -199,18 +174,17 @@ def test_c5_full_size_rows_and_properties():
     _say("bwd c5: max relative |sum dK|=%.3e, |sum dV - sum dO|=%.3e" % (sk.max().item(), sv.max().item()))
     assert sk.max().item() <= 2 ** -6 and sv.max().item() <= 2 ** -6
     rows = inputs.sample_rows(w.B, w.H, w.N, 48, seed=[5, 7], heads_subset=2, rows_per_head=6)
-    got, ref = [], []
+    got, ref, mag = [], [], []
     for b, h, i in rows:
         b, h, i = int(b), int(h), int(i)
         r = oracle.attention_bwd_ex(q[b:b + 1, h:h + 1, i:i + 1], k[b:b + 1, h:h + 1, :i + 1], v[b:b + 1, h:h + 1, :i + 1],
                                     do[b:b + 1, h:h + 1, i:i + 1], dtype="bf16", layout=w.layout, causal=True,
-                                    scale=w.scale, q_offset=i, nthreads=NTHREADS)
+                                    scale=w.scale, q_offset=i, nthreads=NTHREADS, mags=True)
         ref.append(r[0][0, 0, 0])
+        mag.append(r[3][0, 0, 0])
         got.append(f64(dq[b, h, i]))
-    got, ref = np.stack(got), np.stack(ref)
-    err, scale = np.abs(got - ref).max(), np.abs(ref).max()
-    _say("bwd c5: %d sampled dQ rows: max|err|=%.3e max|ref|=%.3e" % (len(rows), err, scale))
-    assert err <= TOL * scale + ATOL
+    bwd_bound.check("%d sampled dQ rows" % len(rows), np.stack(got), np.stack(ref), np.stack(mag), "bf16", w.N, w.D,
+                    "bwd c5")
 
 
 def test_host_pointer_rejected():

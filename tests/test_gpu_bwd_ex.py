@@ -2,10 +2,10 @@
 
 The GPU side runs the library's forward over every key (fa_fwd_ex with the same query offset and
 window) for O and lse, then fa_bwd_ex, possibly once per key chunk; the oracle computes the chunk's
-dQ part and its dK, dV rows from Q, K, V and dO alone (``oracle.attention_bwd_ex``).  Tolerance as for
-fa_bwd: max |g_gpu - g_ref| <= 1e-2 * max |g_ref| + 1e-5 per gradient tensor, for the same reasons (two
-16-bit roundings per term, D taken from the rounded O; the absolute term covers gradients that vanish
-exactly); fp32 inputs: 2e-4 * max |g_ref| + 1e-5, derived in test_gpu_bwd.py.
+dQ part and its dK, dV rows from Q, K, V and dO alone (``oracle.attention_bwd_ex``), with each element's
+term magnitude.  Every element must lie within the per-element bound of tests/bwd_bound.py (the same
+roundings as fa_bwd's; the dQ parts of a chunked call are each rounded once, and their magnitudes add up
+to the whole call's, so their sum meets the bound of the whole).
 """
 import os
 import sys
@@ -17,12 +17,10 @@ import torch
 import oracle
 import transformer_attention_fwd_amd as fa
 from transformer_attention_fwd_amd import inputs
+from tests import bwd_bound
 
 pytestmark = pytest.mark.gpu
 NTHREADS = min(16, os.cpu_count() or 1)
-TOL = 1e-2
-ATOL = 1e-5
-TOL32, ATOL32 = 2e-4, 1e-5
 
 
 def _say(msg):
@@ -42,13 +40,8 @@ def f64(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def check(name, g, r, what, dtype="bf16"):
-    tol, atol = (TOL32, ATOL32) if dtype == "fp32" else (TOL, ATOL)
-    assert np.all(np.isfinite(g)), "%s %s: non-finite" % (what, name)
-    err = np.abs(g - r).max() if g.size else 0.0
-    scale = np.abs(r).max() if r.size else 0.0
-    _say("%s %s: max|err|=%.3e max|ref|=%.3e" % (what, name, err, scale))
-    assert err <= tol * scale + atol, "%s %s: max error %.3e over %.3e" % (what, name, err, tol * scale + atol)
+def check(name, g, r, m, what, dtype, n, d, abs_term=bwd_bound.ATOL):
+    bwd_bound.check(name, g, r, m, dtype, n, d, what, abs_term)
 
 
 def make_case(B, H, Nq, Nk, D, dtype, layout, seed):
@@ -70,7 +63,9 @@ def compare_chunks(B, H, Nq, Nk, D, *, dtype="bf16", layout="BHSD", causal=True,
     """Run fa_bwd_ex once per key chunk into one dk/dv; check each dQ part, the dQ sum and dK, dV."""
     scale = float(np.float32(1 / np.sqrt(D)))
     chunks = chunks or [(0, Nk)]
+    n = max(Nq, Nk)
     q, k, v, do = make_case(B, H, Nq, Nk, D, dtype, layout, seed)
+    at = bwd_bound.atol(dtype, n, scale, q, k, do)
     _say("%s: B=%d H=%d Nq=%d Nk=%d D=%d %s %s causal=%d window=%d q_offset=%d chunks=%s" %
          (what, B, H, Nq, Nk, D, dtype, layout, causal, window, q_offset, chunks))
     dev = [to_dev(x, dtype) for x in (q, k, v, do)]
@@ -84,15 +79,16 @@ def compare_chunks(B, H, Nq, Nk, D, *, dtype="bf16", layout="BHSD", causal=True,
                                          dk=dk, dv=dv)
         torch.cuda.synchronize()
         ref = oracle.attention_bwd_ex(q, k, v, do, dtype=dtype, layout=layout, causal=causal, scale=scale,
-                                      window=window, q_offset=q_offset, kv_start=s, kv_len=e - s, nthreads=NTHREADS)
-        check("dQ[%d:%d]" % (s, e), f64(dq), ref[0], what, dtype)
+                                      window=window, q_offset=q_offset, kv_start=s, kv_len=e - s, nthreads=NTHREADS,
+                                      mags=True)
+        check("dQ[%d:%d]" % (s, e), f64(dq), ref[0], ref[3], what, dtype, n, D, at)
         dq_sum += dq.double()
     full = oracle.attention_bwd_ex(q, k, v, do, dtype=dtype, layout=layout, causal=causal, scale=scale,
-                                   window=window, q_offset=q_offset, nthreads=NTHREADS)
+                                   window=window, q_offset=q_offset, nthreads=NTHREADS, mags=True)
     if len(chunks) > 1:
-        check("sum dQ", dq_sum.cpu().numpy(), full[0], what, dtype)
-    check("dK", f64(dk), full[1], what, dtype)
-    check("dV", f64(dv), full[2], what, dtype)
+        check("sum dQ", dq_sum.cpu().numpy(), full[0], full[3], what, dtype, n, D, len(chunks) * at)
+    check("dK", f64(dk), full[1], full[4], what, dtype, n, D, at)
+    check("dV", f64(dv), full[2], full[5], what, dtype, n, D, at)
     return dev, o, lse
 
 
@@ -188,10 +184,12 @@ def test_rows_outside_the_chunk_untouched_and_empty_chunk():
         assert torch.equal(t[:, :, :100], sentinel[:, :, :100]) and torch.equal(t[:, :, 228:], sentinel[:, :, 228:])
         assert bool((t[:, :, 100:228] != 1024.0).any())
     ref = oracle.attention_bwd_ex(q, k, v, do, dtype="bf16", layout="BHSD", causal=True, scale=0.088,
-                                  q_offset=Nk - Nq, kv_start=100, kv_len=128, nthreads=NTHREADS)
-    check("dQ[100:228]", f64(dq), ref[0], "bwd_ex untouched")
-    check("dK[100:228]", f64(dk[:, :, 100:228]), ref[1][:, :, 100:228], "bwd_ex untouched")
-    check("dV[100:228]", f64(dv[:, :, 100:228]), ref[2][:, :, 100:228], "bwd_ex untouched")
+                                  q_offset=Nk - Nq, kv_start=100, kv_len=128, nthreads=NTHREADS, mags=True)
+    check("dQ[100:228]", f64(dq), ref[0], ref[3], "bwd_ex untouched", "bf16", Nk, D)
+    check("dK[100:228]", f64(dk[:, :, 100:228]), ref[1][:, :, 100:228], ref[4][:, :, 100:228], "bwd_ex untouched",
+          "bf16", Nk, D)
+    check("dV[100:228]", f64(dv[:, :, 100:228]), ref[2][:, :, 100:228], ref[5][:, :, 100:228], "bwd_ex untouched",
+          "bf16", Nk, D)
     # an empty chunk: dQ's part is 0, dK and dV untouched, D still written for every row
     dk2, dv2 = sentinel.clone(), sentinel.clone()
     delta.fill_(float("nan"))
@@ -230,6 +228,6 @@ def test_prefill_behind_cache_sampled_heads():
     torch.cuda.synchronize()
     heads = [(0, 2), (0, 7)]
     ref = oracle.attention_bwd_ex(q, k, v, do, dtype="bf16", layout="BHSD", causal=True, scale=scale,
-                                  q_offset=Nk - Nq, heads=heads, nthreads=NTHREADS)
-    for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
-        check(name, np.stack([f64(g[b, h]) for (b, h) in heads]), r, "bwd_ex prefill")
+                                  q_offset=Nk - Nq, heads=heads, nthreads=NTHREADS, mags=True)
+    for i, (name, g) in enumerate(zip(("dQ", "dK", "dV"), (dq, dk, dv))):
+        check(name, np.stack([f64(g[b, h]) for (b, h) in heads]), ref[i], ref[i + 3], "bwd_ex prefill", "bf16", Nk, D)

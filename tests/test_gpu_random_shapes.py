@@ -89,4 +89,4 @@ def test_random_varlen_backward(i):
     from tests.test_gpu_varlen_bwd import _check, run
     c = _draw_varlen(1, i)
     got, ref = run(c["lq"], c["lk"], c["H"], c["D"], c["dtype"], c["causal"], 990 + i)
-    _check(got, ref, "random varlen backward %d: %s" % (i, c))
+    _check(got, ref, "random varlen backward %d: %s" % (i, c), c["dtype"])

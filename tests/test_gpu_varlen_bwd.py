@@ -1,7 +1,7 @@
 """GPU parity of the packed variable-length backward (fa_bwd_varlen through the C ABI) against the oracle's
-per-sequence composition (oracle.attention_bwd_varlen), with the backward's tolerance: per gradient tensor
-max |g_gpu - g_ref| <= 1e-2 * max |g_ref| + 1e-5 (derived in test_gpu_bwd.py).  The GPU side runs the
-library's packed forward first for O and lse."""
+per-sequence composition (oracle.attention_bwd_varlen), with the backward's per-element bound of
+tests/bwd_bound.py (each element within (2 u + c eps) M + 1e-6 of the oracle, M its term magnitude).  The
+GPU side runs the library's packed forward first for O and lse."""
 import numpy as np
 import pytest
 import torch
@@ -9,20 +9,20 @@ import torch
 import oracle
 import transformer_attention_fwd_amd as fa
 from transformer_attention_fwd_amd import inputs
+from tests import bwd_bound
 from tests.test_gpu_parity import NTHREADS, _say, to_dev
 
 pytestmark = pytest.mark.gpu
-TOL, ATOL = 1e-2, 1e-5
 
 
-def _check(got, ref, what):
-    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
-        g = g.float().cpu().numpy().astype(np.float64)
-        assert np.all(np.isfinite(g)), "%s %s: non-finite" % (what, name)
-        err = np.abs(g - r).max() if r.size else 0.0
-        scale = np.abs(r).max() if r.size else 0.0
-        _say("%s %s: max|err|=%.3e max|ref|=%.3e" % (what, name, err, scale))
-        assert err <= TOL * scale + ATOL, "%s %s: max error %.3e over %.3e" % (what, name, err, TOL * scale + ATOL)
+def _check(got, ref, what, dtype="bf16", abs_term=bwd_bound.ATOL):
+    """got: the GPU's (dQ, dK, dV); ref: the oracle's gradients and term magnitudes, or ``run``'s pair of
+    those and the absolute term.  n: the row counts (an upper bound of every sequence's)."""
+    if len(ref) == 2:
+        ref, abs_term = ref
+    d = got[0].shape[-1]
+    n = max(got[0].shape[0], got[1].shape[0])
+    bwd_bound.check_all([g.float().cpu().numpy().astype(np.float64) for g in got], ref, dtype, n, d, what, abs_term)
 
 
 def run(lq, lk, H, D, dtype, causal, seed):
@@ -38,8 +38,11 @@ def run(lq, lk, H, D, dtype, causal, seed):
     got = fa.attention_bwd_varlen(dev[0], dev[1], dev[2], o, lse, dev[3], cqd, ckd, max(max(lq), 1), max(max(lk), 1),
                                   causal=causal, scale=scale)
     torch.cuda.synchronize()
-    ref = oracle.attention_bwd_varlen(q, k, v, do, cq, ck, dtype=dtype, causal=causal, scale=scale, nthreads=NTHREADS)
-    return got, ref
+    ref = oracle.attention_bwd_varlen(q, k, v, do, cq, ck, dtype=dtype, causal=causal, scale=scale, nthreads=NTHREADS,
+                                      mags=True)
+    # the absolute term of the longest sequence's sums (fp16 only)
+    at = bwd_bound.atol(dtype, max(max(lq), max(lk), 1), scale, q, k, do)
+    return got, (ref, at)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
@@ -48,7 +51,7 @@ def run(lq, lk, H, D, dtype, causal, seed):
 def test_self_attention_length_mix(dtype, causal, D):
     lens = [1, 300, 0, 128, 129, 77, 513, 64]
     got, ref = run(lens, lens, 3, D, dtype, causal, [D, causal])
-    _check(got, ref, "varlen bwd self D=%d %s causal=%d" % (D, dtype, causal))
+    _check(got, ref, "varlen bwd self D=%d %s causal=%d" % (D, dtype, causal), dtype)
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -100,7 +103,7 @@ def test_bad_offsets_skip_only_their_sequence():
         assert bool((t[50:] == 5.0).all())
     assert bool((delta[:, 50:] == 5.0).all())
     ref = oracle.attention_bwd_varlen(q[:50], k[:50], v[:50], do[:50], [0, 50], [0, 50], dtype="bf16", causal=True,
-                                      scale=float(np.float32(1 / np.sqrt(D))), nthreads=NTHREADS)
+                                      scale=float(np.float32(1 / np.sqrt(D))), nthreads=NTHREADS, mags=True)
     _check(tuple(t[:50] for t in out), ref, "varlen bwd bad offsets, sequence 0")
 
 

@@ -249,3 +249,100 @@ def test_ex_bad_arguments():
         oracle.attention_bwd_ex(z, z, z, z, dtype="fp64", layout="BHSD", causal=False, scale=1.0, window=2)
     with pytest.raises(ValueError):
         oracle.attention_bwd_ex(z, z, z, z, dtype="fp64", layout="BHSD", causal=True, scale=1.0, kv_start=3, kv_len=2)
+
+
+# ---- term magnitudes (the per-element error bounds of the GPU backward tests are multiples of them) ----
+def _mags(q, k, v, dout, causal, scale, layout="BHSD", **ex):
+    return oracle.attention_bwd_ex(q, k, v, dout, dtype="fp64", layout=layout, causal=causal, scale=scale,
+                                   mags=True, **ex)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("layout", ["BHSD", "BSND"])
+def test_mags_bound_their_gradients(causal, layout):
+    # |sum of terms| <= sum of |terms|: each magnitude is at least its gradient's absolute value, and the
+    # gradients returned beside them are those of the plain call
+    rng = np.random.default_rng(31 + causal)
+    shape = (2, 3, 70, 16) if layout == "BHSD" else (2, 70, 3, 16)
+    q, k, v, dout = (_rand(rng, shape) for _ in range(4))
+    res = _mags(q, k, v, dout, causal, 0.4, layout)
+    plain = oracle.attention_bwd(q, k, v, dout, dtype="fp64", layout=layout, causal=causal, scale=0.4)
+    via_plain = oracle.attention_bwd(q, k, v, dout, dtype="fp64", layout=layout, causal=causal, scale=0.4, mags=True)
+    for n in range(3):
+        np.testing.assert_array_equal(res[n], plain[n])
+        np.testing.assert_array_equal(via_plain[n], plain[n])
+        np.testing.assert_array_equal(via_plain[n + 3], res[n + 3])
+        assert np.all(res[n + 3] >= np.abs(res[n]) * (1 - 1e-12))
+        assert np.all(res[n + 3] > 0)
+
+
+def test_mags_single_key_closed_form():
+    # one key: P = 1, dS = 0 and A = sum_d |dO_d| |v_d|, so MdQ = |scale| |k_d| A, MdK = |scale| |q_d| A,
+    # MdV = |dO_d|
+    rng = np.random.default_rng(33)
+    q, k, v, dout = (_rand(rng, (1, 2, 1, 8)) for _ in range(4))
+    scale = -0.3
+    _, _, _, mq, mk, mv = _mags(q, k, v, dout, True, scale)
+    a = (np.abs(dout) * np.abs(v)).sum(-1, keepdims=True)
+    np.testing.assert_allclose(mq, abs(scale) * np.abs(k) * a, rtol=1e-14)
+    np.testing.assert_allclose(mk, abs(scale) * np.abs(q) * a, rtol=1e-14)
+    np.testing.assert_array_equal(mv, np.abs(dout))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mags_dv_column_sums(causal):
+    # rows of P sum to 1, so sum_j MdV_jd = sum_i |dO_id| for every head and d
+    rng = np.random.default_rng(35)
+    q, k, v, dout = (_rand(rng, (1, 2, 50, 8)) for _ in range(4))
+    mv = _mags(q, k, v, dout, causal, 0.5)[5]
+    np.testing.assert_allclose(mv.sum(2), np.abs(dout).sum(2), rtol=1e-12)
+
+
+def test_mags_linear_in_dout():
+    # dS, D and A are linear in dO and P does not depend on it: doubling dO (exact in binary) doubles every
+    # magnitude exactly, and its sign does not matter
+    rng = np.random.default_rng(37)
+    q, k, v, dout = (_rand(rng, (1, 2, 40, 8)) for _ in range(4))
+    a = _mags(q, k, v, dout, True, 0.6)
+    b = _mags(q, k, v, 2.0 * dout, True, 0.6)
+    c = _mags(q, k, v, -dout, True, 0.6)
+    for n in range(3, 6):
+        np.testing.assert_array_equal(b[n], 2.0 * a[n])
+        np.testing.assert_array_equal(c[n], a[n])
+
+
+@pytest.mark.parametrize("cuts", [(0, 13, 40), (0, 1, 2, 40)])
+def test_mags_of_key_chunks_partition(cuts):
+    # every (i, j) term belongs to one chunk: the chunks' MdQ add up to the whole call's, and each chunk's
+    # MdK, MdV rows are the whole call's rows of its keys (0 elsewhere)
+    rng = np.random.default_rng(39)
+    q, k, v, dout = (_rand(rng, (1, 1, 40, 8)) for _ in range(4))
+    whole = _mags(q, k, v, dout, True, 0.5, window=17)
+    mq = np.zeros_like(whole[3])
+    for a, b in zip(cuts, cuts[1:]):
+        part = _mags(q, k, v, dout, True, 0.5, window=17, kv_start=a, kv_len=b - a)
+        mq += part[3]
+        np.testing.assert_allclose(part[4][:, :, a:b], whole[4][:, :, a:b], rtol=1e-13)
+        np.testing.assert_allclose(part[5][:, :, a:b], whole[5][:, :, a:b], rtol=1e-13)
+        assert not part[4][:, :, :a].any() and not part[4][:, :, b:].any()
+    np.testing.assert_allclose(mq, whole[3], rtol=1e-12)
+
+
+def test_mags_brute_force_tiny():
+    # the definitions evaluated directly with numpy on a tiny causal head
+    rng = np.random.default_rng(41)
+    n, d, scale = 5, 4, 0.8
+    q, k, v, dout = (_rand(rng, (1, 1, n, d)) for _ in range(4))
+    _, _, _, mq, mk, mv = _mags(q, k, v, dout, True, scale)
+    Q, K, V, dO = q[0, 0], k[0, 0], v[0, 0], dout[0, 0]
+    s = scale * Q @ K.T
+    s[np.triu_indices(n, 1)] = -np.inf
+    P = np.exp(s - s.max(1, keepdims=True))
+    P /= P.sum(1, keepdims=True)
+    dP = dO @ V.T
+    dS = P * (dP - (P * dP).sum(1, keepdims=True))
+    A = (np.abs(dO) * (P @ np.abs(V))).sum(1)
+    W = abs(scale) * (np.abs(dS) + P * A[:, None])
+    np.testing.assert_allclose(mq[0, 0], W @ np.abs(K), rtol=1e-12)
+    np.testing.assert_allclose(mk[0, 0], W.T @ np.abs(Q), rtol=1e-12)
+    np.testing.assert_allclose(mv[0, 0], P.T @ np.abs(dO), rtol=1e-12)

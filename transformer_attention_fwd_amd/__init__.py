@@ -27,6 +27,10 @@ There is no CPU or framework fallback: if ``libfa.so`` is missing the first call
         the backward C entry point, same conventions.
     attention_bwd(q, k, v, o, lse, dout, *, layout="BHSD", causal=False, scale=None, delta=None) -> (dq, dk, dv)
         fa_bwd on torch tensors: allocates dq, dk, dv (and the delta workspace unless given).
+    fa_bwd_atomic(q, k, v, o, lse, dout, dq, dk, dv, delta, dq_accum, B, H, N, D, layout, causal, scale, dtype,
+                  stream) -> status
+        the backward that sums dQ with fp32 atomic adds into the dq_accum workspace (B*H*N*D floats).
+    attention_bwd(..., deterministic=False) uses it (16-bit inputs).
     fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, layout, causal, scale, dtype, stream) -> status
         fa_bwd for callers that cannot allocate: the D workspace is the library's static per-GPU array
         (B*H*N <= NOALLOC_MAX_ROWS; calls that overlap on one GPU race on it).
@@ -48,7 +52,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fa_fwd", "fa_fwd_ex", "fa_fwd_varlen", "fa_merge", "fa_bwd", "fa_bwd_ex", "fa_bwd_varlen", "fa_bwd_noalloc", "attention",
+__all__ = ["fa_fwd", "fa_fwd_ex", "fa_fwd_varlen", "fa_merge", "fa_bwd", "fa_bwd_ex", "fa_bwd_varlen", "fa_bwd_noalloc", "fa_bwd_atomic", "attention",
            "attention_ex", "attention_varlen", "merge", "attention_bwd", "attention_bwd_ex", "attention_bwd_varlen", "FaError", "library_path",
            "load", "status_str", "version",
            "LAYOUT_BHSD", "LAYOUT_BSND", "DTYPE_FP32", "DTYPE_FP16", "DTYPE_BF16"]
@@ -113,6 +117,9 @@ def load():
         lib.fa_bwd_varlen.restype = ctypes.c_int
         lib.fa_bwd_varlen.argtypes = ([ctypes.c_void_p] * 12 + [ctypes.c_int64] * 7 + [ctypes.c_int, ctypes.c_float,
                                       ctypes.c_int, ctypes.c_void_p])
+        lib.fa_bwd_atomic.restype = ctypes.c_int
+        lib.fa_bwd_atomic.argtypes = ([ctypes.c_void_p] * 11 + [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_float, ctypes.c_int, ctypes.c_void_p])
         lib.fa_bwd_noalloc.restype = ctypes.c_int
         lib.fa_bwd_noalloc.argtypes = ([ctypes.c_void_p] * 9 + [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_int,
                                        ctypes.c_float, ctypes.c_int, ctypes.c_void_p])
@@ -170,6 +177,14 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, D, layout, causal,
     return load().fa_bwd(q or None, k or None, v or None, o or None, lse or None, dout or None, dq or None,
                          dk or None, dv or None, delta or None, B, H, N, D, layout, int(causal), scale, dtype,
                          stream or None)
+
+
+def fa_bwd_atomic(q, k, v, o, lse, dout, dq, dk, dv, delta, dq_accum, B, H, N, D, layout, causal, scale, dtype,
+                  stream) -> int:
+    """The atomic-mode backward C entry point: pointers are ints (0 = NULL), returns the status code."""
+    return load().fa_bwd_atomic(q or None, k or None, v or None, o or None, lse or None, dout or None, dq or None,
+                                dk or None, dv or None, delta or None, dq_accum or None, B, H, N, D, layout,
+                                int(causal), scale, dtype, stream or None)
 
 
 def fa_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, D, layout, causal, scale, dtype, stream) -> int:
@@ -330,8 +345,11 @@ def merge(o_parts, lse_parts, *, layout: str = "BHSD", out=None, lse=None):
 
 
 def attention_bwd(q, k, v, o, lse, dout, *, layout: str = "BHSD", causal: bool = False, scale: float | None = None,
-                  delta=None):
-    """dQ, dK, dV for torch device tensors (q, k, v, o, dout of one shape; lse [B, H, N] fp32 from the forward)."""
+                  delta=None, deterministic: bool = True, dq_accum=None):
+    """dQ, dK, dV for torch device tensors (q, k, v, o, dout of one shape; lse [B, H, N] fp32 from the forward).
+
+    deterministic=False runs fa_bwd_atomic (16-bit inputs): dQ summed with fp32 atomic adds into dq_accum
+    (allocated here unless given: float32, shaped like q)."""
     import torch
     if layout not in _LAYOUTS:
         raise ValueError("layout must be 'BHSD' or 'BSND'")
@@ -353,9 +371,18 @@ def attention_bwd(q, k, v, o, lse, dout, *, layout: str = "BHSD", causal: bool =
         raise ValueError("delta must be a contiguous float32 tensor of shape [B, H, N]")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     stream = torch.cuda.current_stream(q.device).cuda_stream if q.is_cuda else 0
-    _raise_on(fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, D, _LAYOUTS[layout],
-                     causal, float(scale), _dtype_code(q), stream))
+    if deterministic:
+        _raise_on(fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, D, _LAYOUTS[layout],
+                         causal, float(scale), _dtype_code(q), stream))
+        return dq, dk, dv
+    if dq_accum is None:
+        dq_accum = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if dq_accum.shape != q.shape or dq_accum.dtype != torch.float32 or not dq_accum.is_contiguous():
+        raise ValueError("dq_accum must be a contiguous float32 tensor shaped like q")
+    _raise_on(fa_bwd_atomic(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), dq_accum.data_ptr(), B, H,
+                            N, D, _LAYOUTS[layout], causal, float(scale), _dtype_code(q), stream))
     return dq, dk, dv
 
 

@@ -319,11 +319,13 @@ namespace {
 // fa_bwd_ex; with delta == nullptr the D workspace is the library's own per-device scratch array
 // (fa_bwd_noalloc), whose size limit is checked with the other sizes and which is neither an input nor a
 // caller buffer (no aliasing or residency check).
+// With dq_acc != nullptr the dQ sums go to that fp32 workspace through atomic adds (fa_bwd_atomic).
 int bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
            void* dk, void* dv, float* delta, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D, int layout,
            int causal, int64_t window, int64_t q_offset, int64_t kv_start, int64_t kv_len, float scale, int dtype,
-           void* stream) {
+           void* stream, float* dq_acc = nullptr) {
   const bool scratch = delta == nullptr;
+  const bool atomic = dq_acc != nullptr;
   // ---- pure argument checks (no HIP calls) ----
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
   if (layout != FA_LAYOUT_BHSD && layout != FA_LAYOUT_BSND) return FA_ERR_BAD_LAYOUT;
@@ -346,15 +348,27 @@ int bwd_ex(const void* q, const void* k, const void* v, const void* o, const flo
   if ((Nq - 1) * stride_bytes + D * esize > INT32_MAX || (Nk - 1) * stride_bytes + D * esize > INT32_MAX)
     return FA_ERR_UNSUPPORTED;
   if (scratch && rows_q > kNoAllocMaxRows) return FA_ERR_SCRATCH_LIMIT;
+  if (atomic && dtype == FA_DTYPE_FP32) return FA_ERR_UNSUPPORTED;
+  int64_t acc_bytes = 0;
+  if (atomic && !mul_ok(elems_q, 4, &acc_bytes)) return FA_ERR_UNSUPPORTED;
   if (!isfinite(scale) || !isfinite(fabsf(scale) * 1.4426950408889634f)) return FA_ERR_BAD_SCALE;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse | (uintptr_t)dout |
-       (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)delta) & 15)
+       (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv | (uintptr_t)delta | (uintptr_t)dq_acc) & 15)
     return FA_ERR_MISALIGNED;
   const void* ins[6] = {q, k, v, o, lse, dout};
   const int64_t in_bytes[6] = {bytes_q, bytes_k, bytes_k, bytes_q, row_bytes, bytes_q};
-  const void* outs[4] = {dq, dk, dv, delta};
-  const int64_t out_bytes[4] = {bytes_q, bytes_k, bytes_k, row_bytes};
-  const int n_outs = scratch ? 3 : 4;
+  // the caller's outputs and workspaces (the library's scratch array is none of them)
+  const void* outs[5] = {dq, dk, dv};
+  int64_t out_bytes[5] = {bytes_q, bytes_k, bytes_k};
+  int n_outs = 3;
+  if (!scratch) {
+    outs[n_outs] = delta;
+    out_bytes[n_outs++] = row_bytes;
+  }
+  if (atomic) {
+    outs[n_outs] = dq_acc;
+    out_bytes[n_outs++] = acc_bytes;
+  }
   for (int a = 0; a < n_outs; ++a) {
     for (int i = 0; i < 6; ++i)
       if (overlaps(outs[a], out_bytes[a], ins[i], in_bytes[i])) return FA_ERR_ALIAS;
@@ -395,6 +409,7 @@ int bwd_ex(const void* q, const void* k, const void* v, const void* o, const flo
   p.dk = dk;
   p.dv = dv;
   p.delta = delta;
+  p.dq_acc = dq_acc;
   p.B = (int)B;
   p.H = (int)H;
   p.Nq = (int)Nq;
@@ -420,7 +435,8 @@ int bwd_ex(const void* q, const void* k, const void* v, const void* o, const flo
   p.c = scale * 1.4426950408889634f;
   p.scale = scale;
   const int kd = dtype == FA_DTYPE_FP32 ? fa::kDtypeFp32 : dtype == FA_DTYPE_FP16 ? fa::kDtypeFp16 : fa::kDtypeBf16;
-  e = fa::launch_bwd(p, kd, (int)D, causal != 0, (hipStream_t)stream);
+  e = atomic ? fa::launch_bwd_atomic(p, kd, (int)D, causal != 0, (hipStream_t)stream)
+             : fa::launch_bwd(p, kd, (int)D, causal != 0, (hipStream_t)stream);
   if (e != hipSuccess) {
     set_error("kernel launch", e);
     return FA_ERR_HIP;
@@ -437,6 +453,15 @@ FA_API int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
   if (!delta) return FA_ERR_NULL;
   return bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, Nq, Nk, D, layout, causal, window, q_offset, kv_start,
                 kv_len, scale, dtype, stream);
+}
+
+FA_API int fa_bwd_atomic(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, float* delta, float* dq_accum, int64_t B,
+                         int64_t H, int64_t N, int64_t D, int layout, int causal, float scale, int dtype,
+                         void* stream) {
+  if (!delta || !dq_accum) return FA_ERR_NULL;
+  return bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, N, N, D, layout, causal, -1, 0, 0, N, scale, dtype,
+                stream, dq_accum);
 }
 
 FA_API int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,

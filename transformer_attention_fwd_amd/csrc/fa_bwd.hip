@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -87,19 +88,23 @@ __device__ __forceinline__ float to_f32(typename Elem<IS_BF16>::vec8 x, int e) {
   return (float)x[e];
 }
 
-// Per-lane LDS offsets: row reads of logical chunk 4c+g of row li, and transposing reads of column
-// 16*dt + 4*(li&3) of row 4g + (li>>2).
+// Per-lane LDS offset of the transposing read of d tile dt: column 16*dt + 4*(li&3) of row 4g + (li>>2).
+template <int D>
+__device__ __forceinline__ int tr_offset(int li, int g, int dt) {
+  typedef BwdTile<D> T;
+  const int row = 4 * g + (li >> 2);
+  const int col = 16 * dt + 4 * (li & 3);
+  return row * T::ROW_BYTES + (((col >> 3) ^ T::swz(row)) << 4) + (col & 7) * 2;
+}
+
+// Per-lane LDS offsets: row reads of logical chunk 4c+g of row li, and the transposing reads of every d tile.
 template <int D>
 __device__ __forceinline__ void lane_offsets(int li, int g, int (&rb)[BwdTile<D>::DC], int (&tb)[BwdTile<D>::DT]) {
   typedef BwdTile<D> T;
 #pragma unroll
   for (int c = 0; c < T::DC; ++c) rb[c] = li * T::ROW_BYTES + (((4 * c + g) ^ T::swz(li)) << 4);
 #pragma unroll
-  for (int dt = 0; dt < T::DT; ++dt) {
-    const int row = 4 * g + (li >> 2);
-    const int col = 16 * dt + 4 * (li & 3);
-    tb[dt] = row * T::ROW_BYTES + (((col >> 3) ^ T::swz(row)) << 4) + (col & 7) * 2;
-  }
+  for (int dt = 0; dt < T::DT; ++dt) tb[dt] = tr_offset<D>(li, g, dt);
 }
 
 // Where one workgroup's (b, h) rows lie: the query and key counts, the key chunk, the query offset and
@@ -355,7 +360,13 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
 // ------------------------------------------------------------------------------------------------
 // dK, dV : one workgroup per (b, h, 128-key tile)
 // ------------------------------------------------------------------------------------------------
-template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW, bool VARLEN, int NW, int KW, int MINB>
+// ATOMIC_DQ (the atomic mode, fa_bwd_atomic): the workgroup also forms dQ's part of its 128 keys from the
+// dS it computes, dQ_i += sum_j dS_ij k_j, and adds it into the fp32 accumulator p.dq_acc with global atomics
+// (the per-step sums of different workgroups arrive in any order, so the result can differ in the last
+// bits from run to run).  Per 32-query step every wave writes its dS (rounded as for dK) transposed into
+// LDS, and after a barrier each wave multiplies the whole step's dS by K (staged once in LDS) for its
+// share of dQ's 16 x 16 tiles.
+template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW, bool VARLEN, int NW, int KW, int MINB, bool ATOMIC_DQ = false>
 __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
   typedef BwdTile<D> T;
   typedef Elem<IS_BF16> E;
@@ -374,6 +385,13 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
   __shared__ __attribute__((aligned(16))) float rv0[2 * BQ];
   __shared__ __attribute__((aligned(16))) float rv1[2 * BQ];
   static_assert(BQ == 64, "one lane of one wave loads each row value");
+  // atomic mode: the workgroup's K rows (swizzled as the Q/dO tiles) and two buffers of one step's dS^T
+  // (128 keys x 32 queries, one 64-byte row per key)
+  constexpr int KS_BYTES = ATOMIC_DQ ? BK * T::ROW_BYTES : 16;
+  constexpr int DS_ROW = QS * 2, DS_BYTES = ATOMIC_DQ ? BK * DS_ROW : 16;
+  __shared__ __attribute__((aligned(1024))) uint8_t ks_l[KS_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t dst0[DS_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t dst1[DS_BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -411,6 +429,15 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
       if (key >= kv1) kr = vr = u32x4_t{0u, 0u, 0u, 0u};
       kf[kg][c] = __builtin_bit_cast(vec8, kr);
       vf[kg][c] = __builtin_bit_cast(vec8, vr);
+    }
+  }
+  if constexpr (ATOMIC_DQ) {  // published to the other waves by the first step's barrier
+#pragma unroll
+    for (int kg = 0; kg < KG; ++kg) {
+      const int row = wave * KW + 16 * kg + li;
+#pragma unroll
+      for (int c = 0; c < T::DC; ++c)
+        *(vec8*)(ks_l + row * T::ROW_BYTES + (((4 * c + g) ^ T::swz(row)) << 4)) = kf[kg][c];
     }
   }
 
@@ -477,9 +504,72 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
   int rb[T::DC], tb[T::DT];
   lane_offsets<D>(li, g, rb, tb);
 
+  // atomic mode, one 32-query step: publish this wave's dS^T rows, then form this wave's dQ tiles over the
+  // workgroup's 128 keys, dQ[q][d] = sum_k dS[q][k] K[k][d] (A = dS from dS^T by transposing reads, B =
+  // K^T from the K rows by transposing reads, both with the key order of tr_frag), and add them to dq_acc.
+  // Tiles (16 queries x 16 d): QGS * DT of them, NW waves; wave w takes query group w / (NW / QGS) and d
+  // tiles of its share.  The dS buffers alternate between steps, so one barrier per step suffices: a
+  // buffer is rewritten only after the next step's barrier, which follows every wave's reads of it.
+  float* dq_acc = p.dq_acc;
+  constexpr int WPQ = NW / QGS;     // waves per query group of a step
+  constexpr int DTW = T::DT / WPQ;  // dQ d tiles per wave (2 for D = 128, 1 for D = 64)
+  static_assert(DTW >= 1 && DTW * WPQ == T::DT, "dQ tiles split evenly over the waves");
+  // the wave's query group and first d tile; K^T read offsets computed here, not indexed from tb[] by a
+  // wave-dependent index (which would place tb[] in private memory)
+  // The offsets are made opaque to the optimizer: split into a chain of address steps, an LDS read can end
+  // up too many steps from its LDS object for the compiler to prove it apart from the Q/dO tile DMA, which
+  // then costs a wait for that DMA before the read.
+  const int dq_qg = wave / WPQ, dq_dt0 = (wave % WPQ) * DTW;
+  int ktb[DTW];
+#pragma unroll
+  for (int t = 0; t < DTW; ++t) {
+    ktb[t] = tr_offset<D>(li, g, dq_dt0 + t);
+    asm("" : "+v"(ktb[t]));
+  }
+  // dS^T lane offset: row 4g + (li >> 2) (a key), column 16 qg + 4 (li & 3) (queries)
+  int ds_off = (4 * g + (li >> 2)) * DS_ROW + (16 * dq_qg + 4 * (li & 3)) * 2;
+  asm("" : "+v"(ds_off));
+  auto atomic_dq_step = [&](uint8_t* dst, const uint32_t (&dsq)[KG][4], int qh0) __attribute__((always_inline)) {
+    if constexpr (ATOMIC_DQ) {
+#pragma unroll
+      for (int kg = 0; kg < KG; ++kg) {  // key row wave*KW + 16 kg + li: queries 4g..4g+3 and 16+4g..16+4g+3
+        uint8_t* row = dst + (wave * KW + 16 * kg + li) * DS_ROW;
+        *(u32x2_t*)(row + 8 * g) = u32x2_t{dsq[kg][0], dsq[kg][1]};
+        *(u32x2_t*)(row + 32 + 8 * g) = u32x2_t{dsq[kg][2], dsq[kg][3]};
+      }
+      lds_barrier();
+      f32x4_t acc[DTW];
+#pragma unroll
+      for (int t = 0; t < DTW; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < BK / 32; ++kc) {
+        const vec8 a = tr_frag<DS_ROW, vec8>(dst, ds_off, 32 * kc * DS_ROW);
+#pragma unroll
+        for (int t = 0; t < DTW; ++t) {
+          const vec8 bk = tr_frag<T::ROW_BYTES, vec8>(ks_l, ktb[t], 32 * kc * T::ROW_BYTES);
+          acc[t] = E::mfma(a, bk, acc[t]);
+        }
+      }
+      // lane holds dQ rows qh0 + 16 qg + 4 g + r, column 16 (dt0 + t) + li.  Every lane issues every atomic
+      // (a row past the end adds 0 to the last row), so a step always issues 4 DTW of them
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int qi = qh0 + 16 * dq_qg + 4 * g + r;
+        float* dst_row = dq_acc + qhead + min(qi, Nq - 1) * ss;
+#pragma unroll
+        for (int t = 0; t < DTW; ++t) unsafeAtomicAdd(dst_row + 16 * (dq_dt0 + t) + li, qi < Nq ? acc[t][r] : 0.f);
+      }
+    }
+  };
+  // atomic instructions a wave issues per Q/dO tile (both 32-query steps)
+  constexpr int kAtomicsPerTile = ATOMIC_DQ ? (BQ / QS) * 4 * DTW : 0;
+
   auto step = [&](int j, const uint8_t* qs, const uint8_t* os, const float* rv, uint8_t* qn, uint8_t* on, float* rvn,
                   auto last_c) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    // this wave's share of tile j has landed (the atomic mode leaves the previous tile's atomics, issued after
+    // tile j's DMA, in flight)
+    if (ATOMIC_DQ && j > 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kAtomicsPerTile));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     lds_barrier();
     // the next tile's row values are loaded before its DMA is issued (the memory counter retires in
     // order) and stored to LDS after this tile's work, for the next barrier to publish
@@ -496,6 +586,13 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
       // some query of the step sees some key of the wave (causal: the last query is not before the
       // first key; window: the first query is not past the last key's window)
       const bool active = qh0 < Nq && (!CAUSAL || c + QS - 1 >= 0) && (!WINDOW || c <= KW - 1 + wv);
+      uint32_t dsq[KG][4];  // atomic mode: this wave's dS of the step (0 when the wave skips it)
+      if constexpr (ATOMIC_DQ) {
+#pragma unroll
+        for (int kg = 0; kg < KG; ++kg)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dsq[kg][i] = 0u;
+      }
       if (active) {
         const bool need_mask = (CAUSAL && c < KW - 1) || (WINDOW && c + QS - 1 > wv);
         // the wave's first key minus the step's first row position (plus the window), clamped: lanes
@@ -595,7 +692,14 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
             dka[kg][dt] = E::mfma(qtf, as_vec8<vec8>(dsp[kg]), dka[kg][dt]);
           }
         }
+        if constexpr (ATOMIC_DQ) {
+#pragma unroll
+          for (int kg = 0; kg < KG; ++kg)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dsq[kg][i] = dsp[kg][i];
+        }
       }
+      if constexpr (ATOMIC_DQ) atomic_dq_step(hh & 1 ? dst1 : dst0, dsq, qh0);
     }
     if constexpr (!decltype(last_c)::value) {
       if (wave == 0) {
@@ -640,6 +744,70 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// atomic mode: D and the zeroed accumulator before the dK/dV kernel, dq from the accumulator after it
+// ------------------------------------------------------------------------------------------------
+// Four lanes per query row (64 rows per 256-thread block, grid-stride): D_i = sum_d dO_id O_id and the row of dq_acc set
+// to 0.  Lane g takes d = 32c + 8g .. +7 for every c and the four partial sums are combined pairwise, the
+// order in which fa_bwd_dq forms D, so both modes hold the same D bit for bit.
+template <int D, bool IS_BF16>
+__global__ __launch_bounds__(256) void fa_bwd_prep(BwdParams p) {
+  typedef typename Elem<IS_BF16>::vec8 vec8;
+  const int g = threadIdx.x & 3;
+  const int64_t rows = (int64_t)p.B * p.H * p.Nq;
+  // the 4 lanes of a row run the same iterations
+  for (int64_t row = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2); row < rows; row += (int64_t)gridDim.x * 64) {
+    const int64_t bh = row / p.Nq, i = row - bh * p.Nq;
+    const int64_t b = bh / p.H, h = bh - b * p.H;
+    const int64_t e0 = b * p.stride_b_q + h * p.stride_h_q + i * p.stride_s + 8 * g;
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      const int64_t e = e0 + 32 * c;
+      const vec8 o = *(const vec8*)((const uint16_t*)p.o + e);
+      const vec8 d = *(const vec8*)((const uint16_t*)p.dout + e);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) acc = __builtin_fmaf(to_f32<IS_BF16>(d, x), to_f32<IS_BF16>(o, x), acc);
+      *(f32x4_t*)(p.dq_acc + e) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      *(f32x4_t*)(p.dq_acc + e + 4) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    acc += __shfl_xor(acc, 1, 4);
+    acc += __shfl_xor(acc, 2, 4);
+    if (g == 0) p.delta[row] = acc;
+  }
+}
+
+// dq = scale * dq_acc, rounded to the 16-bit type; 8 elements per thread and step of a grid-stride loop
+// (dq and dq_acc are dense and share a layout).
+template <bool IS_BF16>
+__global__ __launch_bounds__(256) void fa_bwd_dq_convert(BwdParams p, int64_t n8) {
+  typedef Elem<IS_BF16> E;
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < n8; t += (int64_t)gridDim.x * 256) {
+    const f32x4_t a = *(const f32x4_t*)(p.dq_acc + 8 * t) * p.scale;
+    const f32x4_t b = *(const f32x4_t*)(p.dq_acc + 8 * t + 4) * p.scale;
+    *(u32x4_t*)((uint16_t*)p.dq + 8 * t) =
+        u32x4_t{E::pack2(a[0], a[1]), E::pack2(a[2], a[3]), E::pack2(b[0], b[1]), E::pack2(b[2], b[3])};
+  }
+}
+
+// blocks of a grid-stride launch: enough to fill the chip many times over, at most 2^20
+inline unsigned stride_grid(int64_t items, int per_block) {
+  return (unsigned)std::min<int64_t>((items + per_block - 1) / per_block, (int64_t)1 << 20);
+}
+
+template <int D, bool IS_BF16, bool CAUSAL>
+hipError_t launch_bwd_atomic_t(BwdParams p, hipStream_t stream) {
+  const int64_t rows = (int64_t)p.B * p.H * p.Nq;
+  hipLaunchKernelGGL((fa_bwd_prep<D, IS_BF16>), dim3(stride_grid(rows, 64)), dim3(256), 0, stream, p);
+  p.n_tiles_k = (p.kv_len + 127) / 128;
+  p.n_units_k = p.n_tiles_k * p.B * p.H;
+  hipLaunchKernelGGL((fa_bwd_dkdv<D, IS_BF16, CAUSAL, false, false, kDkdvWaves, kDkdvKeys, kDkdvMinBlocks, true>),
+                     dim3(p.n_units_k), dim3(64 * kDkdvWaves), 0, stream, p);
+  const int64_t n8 = rows * D / 8;
+  hipLaunchKernelGGL((fa_bwd_dq_convert<IS_BF16>), dim3(stride_grid(n8, 256)), dim3(256), 0, stream, p, n8);
+  return hipGetLastError();
+}
+
 template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW>
 hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
   p.n_tiles_q = (p.Nq + 127) / 128;
@@ -678,6 +846,16 @@ hipError_t launch_bwd_c(const BwdParams& p, bool causal, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_bwd_atomic(const BwdParams& p, int dtype, int d, bool causal, hipStream_t stream) {
+  const bool bf = dtype == kDtypeBf16;
+  if (d == 128) {
+    if (bf) return causal ? launch_bwd_atomic_t<128, true, true>(p, stream) : launch_bwd_atomic_t<128, true, false>(p, stream);
+    return causal ? launch_bwd_atomic_t<128, false, true>(p, stream) : launch_bwd_atomic_t<128, false, false>(p, stream);
+  }
+  if (bf) return causal ? launch_bwd_atomic_t<64, true, true>(p, stream) : launch_bwd_atomic_t<64, true, false>(p, stream);
+  return causal ? launch_bwd_atomic_t<64, false, true>(p, stream) : launch_bwd_atomic_t<64, false, false>(p, stream);
+}
 
 hipError_t launch_bwd(const BwdParams& p, int dtype, int d, bool causal, hipStream_t stream) {
   if (dtype == kDtypeFp32) return launch_bwd32(p, d, causal, stream);

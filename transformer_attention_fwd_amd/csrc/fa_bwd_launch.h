@@ -24,6 +24,7 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* delta;       // [B][H][Nq] workspace: D_i = sum_d dO_id O_id, written by the dQ kernel
+  float* dq_acc;      // atomic mode only: fp32 dQ accumulator laid out like dq (null otherwise)
   int64_t stride_b_q, stride_h_q, stride_b_k, stride_h_k, stride_s;
   int64_t q_offset;
   int64_t window;     // < 0: no window
@@ -47,6 +48,10 @@ hipError_t launch_bwd(const BwdParams& p, int dtype, int d, bool causal, hipStre
 
 // Enqueue the backward of packed variable-length batches (16-bit dtypes; BwdParams::cu_q / cu_k set).
 hipError_t launch_bwd_varlen(const BwdParams& p, int dtype, int d, bool causal, hipStream_t stream);
+
+// Enqueue the atomic mode (16-bit dtypes, no window, no key chunk): D and a zeroed p.dq_acc, then the dK/dV
+// kernel that also adds dQ's parts into p.dq_acc with atomics, then dq = scale * dq_acc rounded to dtype.
+hipError_t launch_bwd_atomic(const BwdParams& p, int dtype, int d, bool causal, hipStream_t stream);
 
 // The fp32 kernels behind launch_bwd.
 hipError_t launch_bwd32(const BwdParams& p, int d, bool causal, hipStream_t stream);
