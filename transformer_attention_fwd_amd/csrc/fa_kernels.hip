@@ -552,19 +552,20 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void fa_fwd_16(Params p) {
 // ------------------------------------------------------------------------------------------------
 // 16-bit inputs, ping-pong schedule: 8 waves, whole problems without a window
 // ------------------------------------------------------------------------------------------------
-// Waves w and w + 4 share a SIMD.  Per K/V tile j every wave runs two phases, each closed by a
-// workgroup barrier:
+// Waves w and w + 4 share a SIMD.  Per K/V tile j every wave runs two phases:
 //   matrix phase M(j): O^T += V^T P^T of tile j-1 (its V fragments already sit in registers) while the
 //                      K fragments of tile j are read from LDS, then S^T = K Q^T of tile j;
 //   vector phase V(j): the transposing reads of tile j's V fragments into registers, then the mask and
 //                      the online softmax of S(j) into P(j).
-// Waves 4-7 run one phase behind waves 0-3, so on every SIMD one wave issues MFMAs while the other
-// computes exponentials (the formula page, section "ops-transformer 中的实现", has the matrix and
+// One workgroup barrier per tile: waves 0-3 pass it after their vector phases, waves 4-7 after their
+// matrix phases, so between two barriers waves 0-3 run M(j) then V(j) while waves 4-7 run V(j-1) then
+// M(j).  On every SIMD one wave issues MFMAs while the other computes exponentials, and within the
+// interval the two may drift (the formula page, section "ops-transformer 中的实现", has the matrix and
 // vector units of the Ascend core work side by side; here the two waves of a SIMD take those roles in
 // turn).  The matrix wave runs at the higher issue priority.  K/V tiles stream through a 4-stage LDS
-// ring: tile j+2 is issued once every wave is done with tile j-2, three phases before its first use; the
-// extra stage lets a vector phase end with its V reads still in flight (they are consumed in the next
-// matrix phase, one barrier before their stage is refilled).
+// ring: tile j+2 is issued at the start of M(j), once every wave has passed the barrier after its last
+// use of tile j-2; the extra stage lets a vector phase end with its V reads still in flight (they are
+// consumed by the next matrix phase).
 template <int D, bool IS_BF16, bool CAUSAL, bool PAIR>
 __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
   typedef Tile16<D, 8> T;
@@ -781,12 +782,11 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
     }
   };
   // Every wave issues tile j+2's DMA at the start of its matrix phase M(j) (past the stream's end it
-  // fetches the last tile again into the free stage) and waits at the end of M(j) until its share of tile
-  // j+1 has landed: at most tile j+2's loads (and the Q loads issued after them) stay in flight.  The issue
-  // and the wait sit at the same program point for both groups, a constant count.  Stage safety: tile j+2
-  // refills the stage of tile j-2, whose last readers (group 1's matrix phase M(j-1), which drains its LDS
-  // reads) finish before the barrier that precedes any wave's M(j); tile j+1 is needed from the barrier
-  // after group 1's M(j) on.
+  // fetches the last tile again into the free stage) and, right before its barrier (after V(j) for waves
+  // 0-3, after M(j) for waves 4-7), waits until its share of tile j+1 has landed: at most tile j+2's loads
+  // (and the Q loads issued after them) stay in flight, a constant count.  Stage safety: tile j+2 refills
+  // the stage of tile j-2, whose last readers (waves 4-7's M(j-1), which drains its LDS reads) finish
+  // before the barrier that precedes any wave's M(j); tile j+1 is first read after the next barrier.
   auto issue_next = [&](int j, auto st) __attribute__((always_inline)) {
     constexpr int S = decltype(st)::value;
     issue_tile(min(j + 2, n_kt - 1), kstage(std::integral_constant<int, S + 2>()),
@@ -837,9 +837,11 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
       }
     if (QLOAD) load_q(q0b);
     __builtin_amdgcn_s_setprio(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(QLOAD ? TILE_LOADS + Q_LOADS : TILE_LOADS));
-    __builtin_amdgcn_sched_barrier(0);
-    lds_barrier();
+    if (grp == 1) {  // group 1's barrier closes its matrix phase
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(QLOAD ? TILE_LOADS + Q_LOADS : TILE_LOADS));
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+    }
   };
 
   // vector phase V(j); FIRST: the unit's first tile, which sets the reference maximum (every wave sees
@@ -921,9 +923,12 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
     // no LDS wait: the V reads may still be in flight (the next matrix phase consumes them, a barrier
     // before the DMA refills this stage)
     __builtin_amdgcn_sched_barrier(0);
-    compiler_fence();
-    __builtin_amdgcn_s_barrier();
-    compiler_fence();
+    if (grp == 0) {  // group 0's barrier closes its vector phase
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(QLOAD ? TILE_LOADS + Q_LOADS : TILE_LOADS));
+      compiler_fence();
+      __builtin_amdgcn_s_barrier();
+      compiler_fence();
+    }
   };
 
   issue_tile(0, ks0, vs0);
@@ -932,7 +937,6 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
   // tile 0 has landed once at most tile 1's loads and Q's are in flight
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(TILE_LOADS + Q_LOADS));
   lds_barrier();
-  if (grp == 1) lds_barrier();  // waves 4-7 start one phase later
 
   const std::integral_constant<int, 0> st0;
   const std::integral_constant<int, 1> st1;
@@ -999,7 +1003,6 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
   }
   __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the refetches past the end land before the LDS is released
-  if (grp == 0) lds_barrier();  // the barrier group 1 spent idle at the start
   finish(PAIR ? q0b : q0a);
   // every wave computes on every tile of the stream
   record_tiles(1, bh, T::BM, T::BN, T::QW, T::NW, q_wg, n_kt_a, PAIR ? qt_b * T::BM : -1, n_kt_b, wave, lane, n_kt);
