@@ -150,7 +150,11 @@ __device__ __forceinline__ BwdGeom bwd_geometry(const BwdParams& p, int b, int h
 // ------------------------------------------------------------------------------------------------
 // dQ (and D) : one workgroup per (b, h, 128-query tile)
 // ------------------------------------------------------------------------------------------------
-template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW, bool VARLEN>
+// PAIR (whole causal problems with an even number of 128-query tiles): workgroup r runs the heavy tile
+// n-1-r and then the light tile r of one head over one continuous K/V stream, so every workgroup has the
+// same work; the heavy tile's last step prefetches the light tile's first K/V tile and loads its Q and dO
+// once its own S^T and dP^T products are done.
+template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW, bool VARLEN, bool PAIR = false>
 __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
   typedef BwdTile<D> T;
   typedef Elem<IS_BF16> E;
@@ -167,10 +171,16 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, li = lane & 15;
-  int bh, qt;
+  static_assert(!PAIR || (CAUSAL && !WINDOW && !VARLEN), "pairs are for whole causal problems");
+  int bh, qt, qt_b = -1;
   if constexpr (VARLEN) {
     unit_of_spread(blockIdx.x, p.n_tiles_q, CAUSAL, bh, qt);
     if (bh >= p.B * p.H) return;  // padding head of the grid
+  } else if constexpr (PAIR) {
+    int r;  // pair r of a head: tiles n-1-r and r (n_tiles_q counts pairs)
+    unit_of(blockIdx.x, p.n_units_q, p.n_tiles_q, false, bh, r);
+    qt = 2 * p.n_tiles_q - 1 - r;
+    qt_b = r;
   } else {
     unit_of(blockIdx.x, p.n_units_q, p.n_tiles_q, CAUSAL, bh, qt);
   }
@@ -180,20 +190,25 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
   const int Nq = gm.Nq, Nk = gm.Nk;
   const int64_t qoff = gm.qoff, window = gm.window;
   const int kv0 = gm.kv0, kv1 = gm.kv1;  // the key chunk [kv0, kv1)
-  const int q_wg = qt * BM, q0 = q_wg + wave * QW;
+  int q_wg = qt * BM, q0 = q_wg + wave * QW;  // (the light tile's, after a pair's switch)
   const int64_t qhead = gm.qhead, khead = gm.khead;
   const int64_t ss = p.stride_s;
 
   // K/V tiles from k_lo: the chunk's keys that some query of this workgroup sees
   const int k_lo = WINDOW ? (int)max((int64_t)kv0, q_wg + qoff - window) : kv0;
   const int k_hi = CAUSAL ? (int)min((int64_t)kv1 - 1, q_wg + BM - 1 + qoff) : kv1 - 1;
-  const int n_kt = k_hi >= k_lo ? (k_hi - k_lo) / BN + 1 : 0;
+  const int n_kt_a = k_hi >= k_lo ? (k_hi - k_lo) / BN + 1 : 0;
+  // a pair's light tile streams from key 0 to its own last query
+  const int n_kt_b = PAIR ? (int)min((int64_t)kv1 - 1, (int64_t)qt_b * BM + BM - 1) / BN + 1 : 0;
+  const int n_kt = n_kt_a + n_kt_b;
+  // tile j of the stream: the first tile's, then the light tile's
+  auto tile_of = [&](int j) __attribute__((always_inline)) { return PAIR && j >= n_kt_a ? j - n_kt_a : j; };
   // positions in 32 bits: the workgroup's first query position minus k_lo (and minus the window),
   // clamped to +-2^26 once.  Rows and keys per head stay below 2^24 (the 32-bit buffer offsets), so
   // past the clamp every slot of every tile is visible (or, for the window term, none is hidden)
   // exactly as with the unclamped value.
   const int64_t base64 = q_wg + qoff - k_lo;
-  const int rbase = (int)max((int64_t)-(1 << 26), min((int64_t)(1 << 26), base64));
+  int rbase = (int)max((int64_t)-(1 << 26), min((int64_t)(1 << 26), base64));
   const int wbase = WINDOW ? (int)max((int64_t)-(1 << 26), min((int64_t)(1 << 26), base64 - window)) : 0;
   const int row_bytes = (int)(2 * ss);
   const int span = max(0, (Nk - 1) * row_bytes + T::ROW_BYTES);  // the host keeps this below 2^31
@@ -209,7 +224,7 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
     voff[i] = row * row_bytes + ((pc ^ T::swz(row)) << 4);
   }
   auto issue_tile = [&](int j, uint8_t* kdst, uint8_t* vdst) __attribute__((always_inline)) {
-    issue_kv_tile<LOADS, NW>(kbuf, vbuf, voff, voff, (k_lo + j * BN) * row_bytes, wave, kdst, vdst);
+    issue_kv_tile<LOADS, NW>(kbuf, vbuf, voff, voff, (k_lo + tile_of(j) * BN) * row_bytes, wave, kdst, vdst);
   };
   if (n_kt > 0) issue_tile(0, ks0, vs0);
 
@@ -220,24 +235,37 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
   const uint16_t* op = (const uint16_t*)p.o + qhead;
   vec8 qf[QG][T::DC], df[QG][T::DC];
   float lse2[QG], dlt[QG];
+  auto load_qdo = [&](int q0u) __attribute__((always_inline)) {
 #pragma unroll
-  for (int qg = 0; qg < QG; ++qg) {
-    const int qi = q0 + 16 * qg + li;
-    const int qrow = min(qi, Nq - 1);
-    float acc = 0.f;
+    for (int qg = 0; qg < QG; ++qg) {
+      const int qrow = min(q0u + 16 * qg + li, Nq - 1);
 #pragma unroll
-    for (int c = 0; c < T::DC; ++c) {
-      const int64_t e = qrow * ss + 32 * c + 8 * g;
-      qf[qg][c] = *(const vec8*)(qp + e);
-      df[qg][c] = *(const vec8*)(dop + e);
-      const vec8 of = *(const vec8*)(op + e);
-#pragma unroll
-      for (int x = 0; x < 8; ++x) acc = __builtin_fmaf(to_f32<IS_BF16>(df[qg][c], x), to_f32<IS_BF16>(of, x), acc);
+      for (int c = 0; c < T::DC; ++c) {
+        const int64_t e = qrow * ss + 32 * c + 8 * g;
+        qf[qg][c] = *(const vec8*)(qp + e);
+        df[qg][c] = *(const vec8*)(dop + e);
+      }
     }
-    dlt[qg] = wave_sum_xor16_32(acc);
-    lse2[qg] = p.lse[gm.row0 + qrow] * kLog2e;
-    if (g == 0 && qi < Nq) p.delta[gm.row0 + qi] = dlt[qg];
-  }
+  };
+  auto row_values = [&](int q0u) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg) {
+      const int qi = q0u + 16 * qg + li;
+      const int qrow = min(qi, Nq - 1);
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < T::DC; ++c) {
+        const vec8 of = *(const vec8*)(op + qrow * ss + 32 * c + 8 * g);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc = __builtin_fmaf(to_f32<IS_BF16>(df[qg][c], x), to_f32<IS_BF16>(of, x), acc);
+      }
+      dlt[qg] = wave_sum_xor16_32(acc);
+      lse2[qg] = p.lse[gm.row0 + qrow] * kLog2e;
+      if (g == 0 && qi < Nq) p.delta[gm.row0 + qi] = dlt[qg];
+    }
+  };
+  load_qdo(q0);
+  row_values(q0);
 
   const float cexp = p.c;  // scale * log2(e), signed
   f32x4_t dqa[QG][T::DT];
@@ -248,14 +276,18 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
   int rb[T::DC], tb[T::DT];
   lane_offsets<D>(li, g, rb, tb);
 
-  auto step = [&](int j, const uint8_t* ks, const uint8_t* vs, uint8_t* kn, uint8_t* vn, auto last_c)
+  // sw_c: the heavy tile's last step of a pair, which loads the light tile's Q and dO fragments once its
+  // own S^T and dP^T products no longer need them
+  auto step = [&](int j, const uint8_t* ks, const uint8_t* vs, uint8_t* kn, uint8_t* vn, auto last_c, auto sw_c)
       __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     lds_barrier();
     if constexpr (!decltype(last_c)::value) issue_tile(j + 1, kn, vn);
-    const int key0 = k_lo + j * BN;
-    const int dpos = rbase + wave * QW - j * BN;  // the wave's first query position minus key0
-    const int dwin = wbase + wave * QW - j * BN;  // the same minus the window
+    constexpr bool switch_unit = decltype(sw_c)::value;
+    const int jt = tile_of(j);
+    const int key0 = k_lo + jt * BN;
+    const int dpos = rbase + wave * QW - jt * BN;  // the wave's first query position minus key0
+    const int dwin = wbase + wave * QW - jt * BN;  // the same minus the window
     // the wave's 32 queries see some key of this tile; element masks where the causal edge, the window
     // edge or the chunk's end cross it
     const bool active = (!CAUSAL || dpos + QW - 1 >= 0) && (!WINDOW || dwin <= BN - 1);
@@ -313,6 +345,7 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
           dsf[qg][kc][2 * half + 1] = E::pack2(ds[2], ds[3]);
         }
       }
+      if constexpr (switch_unit) load_qdo(qt_b * BM + wave * QW);
       // dQ^T += K^T dS^T
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
@@ -322,39 +355,71 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
 #pragma unroll
           for (int qg = 0; qg < QG; ++qg) dqa[qg][dt] = E::mfma(kt_frag, as_vec8<vec8>(dsf[qg][kc]), dqa[qg][dt]);
         }
+    } else if constexpr (switch_unit) {
+      load_qdo(qt_b * BM + wave * QW);
     }
   };
-
-  const std::integral_constant<bool, false> more;
-  const std::integral_constant<bool, true> last;
-  if (n_kt > 0) {
-    int j = 0;
-    for (; j + 2 < n_kt; j += 2) {
-      step(j, ks0, vs0, ks1, vs1, more);
-      step(j + 1, ks1, vs1, ks0, vs0, more);
-    }
-    if (j + 2 == n_kt) {
-      step(j, ks0, vs0, ks1, vs1, more);
-      step(j + 1, ks1, vs1, ks0, vs0, last);
-    } else {
-      step(j, ks0, vs0, ks1, vs1, last);
-    }
-  }
 
   // dQ = scale * accumulated (dS K) over the chunk's keys (0 when it sees none); lane holds d =
   // 16*dt + 4*g + r of query q0 + 16*qg + li
   uint16_t* dqp = (uint16_t*)p.dq + qhead;
+  auto store_dq = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int qg = 0; qg < QG; ++qg) {
-    const int qi = q0 + 16 * qg + li;
-    if (qi < Nq) {
+    for (int qg = 0; qg < QG; ++qg) {
+      const int qi = q0 + 16 * qg + li;
+      if (qi < Nq) {
 #pragma unroll
-      for (int dt = 0; dt < T::DT; ++dt) {
-        const f32x4_t x = dqa[qg][dt] * p.scale;
-        *(u32x2_t*)(dqp + qi * ss + 16 * dt + 4 * g) = u32x2_t{E::pack2(x[0], x[1]), E::pack2(x[2], x[3])};
+        for (int dt = 0; dt < T::DT; ++dt) {
+          const f32x4_t x = dqa[qg][dt] * p.scale;
+          *(u32x2_t*)(dqp + qi * ss + 16 * dt + 4 * g) = u32x2_t{E::pack2(x[0], x[1]), E::pack2(x[2], x[3])};
+        }
       }
     }
+  };
+
+  const std::integral_constant<bool, false> more, stay;
+  const std::integral_constant<bool, true> last, switch_c;
+  if constexpr (PAIR) {
+    // both tiles stream an even number of key tiles (128-query tiles of 64-key tiles, a key count that is
+    // a multiple of 128), so the light tile starts in stage 0; the heavy tile's last step prefetches its
+    // first K/V tile
+    int j = 0;
+    for (; j + 2 < n_kt_a; j += 2) {
+      step(j, ks0, vs0, ks1, vs1, more, stay);
+      step(j + 1, ks1, vs1, ks0, vs0, more, stay);
+    }
+    step(j, ks0, vs0, ks1, vs1, more, stay);
+    step(j + 1, ks1, vs1, ks0, vs0, more, switch_c);
+    j += 2;
+    store_dq();
+    q_wg = qt_b * BM;
+    q0 = q_wg + wave * QW;
+    rbase = q_wg;  // the whole problem: no offset, keys from 0
+    row_values(q0);
+#pragma unroll
+    for (int qg = 0; qg < QG; ++qg)
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt) dqa[qg][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (; j + 2 < n_kt; j += 2) {
+      step(j, ks0, vs0, ks1, vs1, more, stay);
+      step(j + 1, ks1, vs1, ks0, vs0, more, stay);
+    }
+    step(j, ks0, vs0, ks1, vs1, more, stay);
+    step(j + 1, ks1, vs1, ks0, vs0, last, stay);
+  } else if (n_kt > 0) {
+    int j = 0;
+    for (; j + 2 < n_kt; j += 2) {
+      step(j, ks0, vs0, ks1, vs1, more, stay);
+      step(j + 1, ks1, vs1, ks0, vs0, more, stay);
+    }
+    if (j + 2 == n_kt) {
+      step(j, ks0, vs0, ks1, vs1, more, stay);
+      step(j + 1, ks1, vs1, ks0, vs0, last, stay);
+    } else {
+      step(j, ks0, vs0, ks1, vs1, last, stay);
+    }
   }
+  store_dq();
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -814,7 +879,22 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
   p.n_units_q = p.B * p.H * p.n_tiles_q;
   p.n_tiles_k = (p.kv_len + 127) / 128;
   p.n_units_k = p.B * p.H * p.n_tiles_k;
-  hipLaunchKernelGGL((fa_bwd_dq<D, IS_BF16, CAUSAL, WINDOW, false>), dim3(p.n_units_q), dim3(256), 0, stream, p);
+  // the whole causal problem with an even number of 128-query tiles and a key count that is a multiple of
+  // 128: the dQ kernel pairs its heavy and light tiles
+  const bool pairs = CAUSAL && !WINDOW && p.q_offset == 0 && p.kv_start == 0 && p.kv_len == p.Nk &&
+                     p.Nq == p.Nk && p.Nq % 128 == 0 && p.n_tiles_q % 2 == 0;
+  if constexpr (CAUSAL && !WINDOW) {
+    if (pairs) {
+      BwdParams pp = p;
+      pp.n_tiles_q = p.n_tiles_q / 2;
+      pp.n_units_q = p.B * p.H * pp.n_tiles_q;
+      hipLaunchKernelGGL((fa_bwd_dq<D, IS_BF16, true, false, false, true>), dim3(pp.n_units_q), dim3(256), 0, stream,
+                         pp);
+    }
+  }
+  if (!pairs) {
+    hipLaunchKernelGGL((fa_bwd_dq<D, IS_BF16, CAUSAL, WINDOW, false>), dim3(p.n_units_q), dim3(256), 0, stream, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_units_k == 0) return e;
   hipLaunchKernelGGL((fa_bwd_dkdv<D, IS_BF16, CAUSAL, WINDOW, false, kDkdvWaves, kDkdvKeys, kDkdvMinBlocks>),
