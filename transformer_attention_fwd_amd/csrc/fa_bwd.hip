@@ -431,7 +431,12 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
 // bits from run to run).  Per 32-query step every wave writes its dS (rounded as for dK) transposed into
 // LDS, and after a barrier each wave multiplies the whole step's dS by K (staged once in LDS) for its
 // share of dQ's 16 x 16 tiles.
-template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW, bool VARLEN, int NW, int KW, int MINB, bool ATOMIC_DQ = false>
+// PAIR (whole causal problems with an even number of 128-key tiles, deterministic mode): workgroup r runs
+// the heavy key tile r and then the light key tile n-1-r of one head over one continuous Q/dO stream, so
+// every workgroup has the same work; the heavy tile's last step prefetches the light tile's first Q/dO
+// tile and loads its K and V once its own S and dP products are done.
+template <int D, bool IS_BF16, bool CAUSAL, bool WINDOW, bool VARLEN, int NW, int KW, int MINB, bool ATOMIC_DQ = false,
+          bool PAIR = false>
 __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
   typedef BwdTile<D> T;
   typedef Elem<IS_BF16> E;
@@ -461,10 +466,16 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, li = lane & 15;
-  int bh, kt;
+  static_assert(!PAIR || (CAUSAL && !WINDOW && !VARLEN && !ATOMIC_DQ), "pairs are for whole causal problems");
+  int bh, kt, kt_b = -1;
   if constexpr (VARLEN) {
     unit_of_spread(blockIdx.x, p.n_tiles_k, false, bh, kt);
     if (bh >= p.B * p.H) return;  // padding head of the grid
+  } else if constexpr (PAIR) {
+    int r;  // pair r of a head: key tiles r and n-1-r (n_tiles_k counts pairs)
+    unit_of(blockIdx.x, p.n_units_k, p.n_tiles_k, false, bh, r);
+    kt = r;
+    kt_b = 2 * p.n_tiles_k - 1 - r;
   } else {
     unit_of(blockIdx.x, p.n_units_k, p.n_tiles_k, false, bh, kt);  // causal: the chunk's first key tile first
   }
@@ -474,7 +485,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
   const int Nq = gm.Nq;
   const int64_t qoff = gm.qoff, window = gm.window;
   const int kv1 = gm.kv1;  // keys of the chunk: [gm.kv0, kv1)
-  const int k_wg = gm.kv0 + kt * BK, kw0 = k_wg + wave * KW;
+  int k_wg = gm.kv0 + kt * BK, kw0 = k_wg + wave * KW;  // (the light tile's, after a pair's switch)
   const int64_t qhead = gm.qhead, khead = gm.khead;
   const int64_t ss = p.stride_s;
 
@@ -483,19 +494,22 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
   const uint16_t* kp = (const uint16_t*)p.k + khead;
   const uint16_t* vp = (const uint16_t*)p.v + khead;
   vec8 kf[KG][T::DC], vf[KG][T::DC];
+  auto load_kv = [&](int kw0u) __attribute__((always_inline)) {
 #pragma unroll
-  for (int kg = 0; kg < KG; ++kg) {
-    const int key = kw0 + 16 * kg + li;
-    const int krow = min(key, kv1 - 1);
+    for (int kg = 0; kg < KG; ++kg) {
+      const int key = kw0u + 16 * kg + li;
+      const int krow = min(key, kv1 - 1);
 #pragma unroll
-    for (int c = 0; c < T::DC; ++c) {
-      const int64_t e = krow * ss + 32 * c + 8 * g;
-      u32x4_t kr = *(const u32x4_t*)(kp + e), vr = *(const u32x4_t*)(vp + e);
-      if (key >= kv1) kr = vr = u32x4_t{0u, 0u, 0u, 0u};
-      kf[kg][c] = __builtin_bit_cast(vec8, kr);
-      vf[kg][c] = __builtin_bit_cast(vec8, vr);
+      for (int c = 0; c < T::DC; ++c) {
+        const int64_t e = krow * ss + 32 * c + 8 * g;
+        u32x4_t kr = *(const u32x4_t*)(kp + e), vr = *(const u32x4_t*)(vp + e);
+        if (key >= kv1) kr = vr = u32x4_t{0u, 0u, 0u, 0u};
+        kf[kg][c] = __builtin_bit_cast(vec8, kr);
+        vf[kg][c] = __builtin_bit_cast(vec8, vr);
+      }
     }
-  }
+  };
+  load_kv(kw0);
   if constexpr (ATOMIC_DQ) {  // published to the other waves by the first step's barrier
 #pragma unroll
     for (int kg = 0; kg < KG; ++kg) {
@@ -510,7 +524,15 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
   // the first key's position; window: up to the last key's position plus the window)
   const int i_begin = CAUSAL ? (int)min((int64_t)Nq, max((int64_t)0, k_wg - qoff)) : 0;
   const int i_last = WINDOW ? (int)min((int64_t)Nq - 1, k_wg + BK - 1 + window - qoff) : Nq - 1;
-  const int n_qt = i_last >= i_begin ? (i_last - i_begin) / BQ + 1 : 0;
+  const int n_qt_a = i_last >= i_begin ? (i_last - i_begin) / BQ + 1 : 0;
+  // a pair's light key tile: the query rows from its first key on (the whole problem: no offset)
+  const int i_begin_b = PAIR ? min(Nq, kt_b * BK) : 0;
+  const int n_qt_b = PAIR ? (Nq - 1 - i_begin_b) / BQ + 1 : 0;
+  const int n_qt = n_qt_a + n_qt_b;
+  // first query row of tile j of the stream: the first key tile's tiles, then the light tile's
+  auto row_of = [&](int j) __attribute__((always_inline)) {
+    return PAIR && j >= n_qt_a ? i_begin_b + (j - n_qt_a) * BQ : i_begin + j * BQ;
+  };
   // positions in 32 bits: row 0's position minus k_wg, clamped to +-2^26 once, and the window
   // corrected by what the clamp removed, clamped to +-2^27.  Rows per head stay below 2^24 (the
   // 32-bit buffer offsets): past +2^26 every row sees every key causally, below -2^26 no row is
@@ -518,7 +540,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
   // exact ones.
   const int64_t rb64 = qoff - k_wg;
   const int64_t rbc64 = max((int64_t)-(1 << 26), min((int64_t)(1 << 26), rb64));
-  const int rbase = (int)rbc64;
+  int rbase = (int)rbc64;
   const int wv = WINDOW ? (int)max((int64_t)-(1 << 27), min((int64_t)(1 << 27), window - (rb64 - rbc64))) : 0;
   const int row_bytes = (int)(2 * ss);
   const int span = max(0, (Nq - 1) * row_bytes + T::ROW_BYTES);
@@ -534,7 +556,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
     voff[i] = row * row_bytes + ((pc ^ T::swz(row)) << 4);
   }
   auto issue_tile = [&](int j, uint8_t* qdst, uint8_t* odst) __attribute__((always_inline)) {
-    issue_kv_tile<LOADS, NW>(qbuf, obuf, voff, voff, (i_begin + j * BQ) * row_bytes, wave, qdst, odst);
+    issue_kv_tile<LOADS, NW>(qbuf, obuf, voff, voff, row_of(j) * row_bytes, wave, qdst, odst);
   };
   if (n_qt > 0) issue_tile(0, qs0, os0);
 
@@ -543,7 +565,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
   const float* dlt_h = p.delta + gm.row0;
   // row values of tile jt for this lane's row (wave 0 only)
   auto load_rows = [&](int jt, float& l2v, float& dv) __attribute__((always_inline)) {
-    const int qi = i_begin + jt * BQ + lane;
+    const int qi = row_of(jt) + lane;
     if (qi < Nq) {
       l2v = lse_h[qi] * kLog2e;
       dv = dlt_h[qi];
@@ -629,8 +651,11 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
   // atomic instructions a wave issues per Q/dO tile (both 32-query steps)
   constexpr int kAtomicsPerTile = ATOMIC_DQ ? (BQ / QS) * 4 * DTW : 0;
 
+  // sw_c: the heavy key tile's last step of a pair, which loads the light tile's K and V once its last
+  // S and dP products no longer need them
   auto step = [&](int j, const uint8_t* qs, const uint8_t* os, const float* rv, uint8_t* qn, uint8_t* on, float* rvn,
-                  auto last_c) __attribute__((always_inline)) {
+                  auto last_c, auto sw_c) __attribute__((always_inline)) {
+    constexpr bool switch_unit = decltype(sw_c)::value;
     // this wave's share of tile j has landed (the atomic mode leaves the previous tile's atomics, issued after
     // tile j's DMA, in flight)
     if (ATOMIC_DQ && j > 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kAtomicsPerTile));
@@ -643,7 +668,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
       if (wave == 0) load_rows(j + 1, nl, nd);
       issue_tile(j + 1, qn, on);
     }
-    const int tile0 = i_begin + j * BQ;
+    const int tile0 = row_of(j);
 #pragma unroll
     for (int hh = 0; hh < BQ / QS; ++hh) {
       const int qh0 = tile0 + QS * hh;  // first query row of this step
@@ -745,6 +770,9 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
             dsp[kg][2 * qq + 1] = E::pack2(ds[2], ds[3]);
           }
         }
+        if constexpr (switch_unit) {
+          if (hh == BQ / QS - 1) load_kv(kt_b * BK + wave * KW);
+        }
         // dV^T += dO^T P ;  dK^T += Q^T dS  (k index over this step's 32 queries)
 #pragma unroll
         for (int dt = 0; dt < T::DT; ++dt) {
@@ -763,6 +791,8 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) dsq[kg][i] = dsp[kg][i];
         }
+      } else if constexpr (switch_unit) {
+        if (hh == BQ / QS - 1) load_kv(kt_b * BK + wave * KW);
       }
       if constexpr (ATOMIC_DQ) atomic_dq_step(hh & 1 ? dst1 : dst0, dsq, qh0);
     }
@@ -774,39 +804,70 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
     }
   };
 
-  const std::integral_constant<bool, false> more;
-  const std::integral_constant<bool, true> last;
-  if (n_qt > 0) {
-    int j = 0;
-    for (; j + 2 < n_qt; j += 2) {
-      step(j, qs0, os0, rv0, qs1, os1, rv1, more);
-      step(j + 1, qs1, os1, rv1, qs0, os0, rv0, more);
-    }
-    if (j + 2 == n_qt) {
-      step(j, qs0, os0, rv0, qs1, os1, rv1, more);
-      step(j + 1, qs1, os1, rv1, qs0, os0, rv0, last);
-    } else {
-      step(j, qs0, os0, rv0, qs1, os1, rv1, last);
-    }
-  }
-
   // dK = scale * accumulated (dS^T Q), dV (0 for keys no query sees): lane holds d = 16*dt + 4*g + r of
   // key kw0 + 16*kg + li; rows outside the chunk are left as they are
   uint16_t* dkp = (uint16_t*)p.dk + khead;
   uint16_t* dvp = (uint16_t*)p.dv + khead;
+  auto store_dkdv = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int kg = 0; kg < KG; ++kg) {
-    const int key = kw0 + 16 * kg + li;
-    if (key < kv1) {
+    for (int kg = 0; kg < KG; ++kg) {
+      const int key = kw0 + 16 * kg + li;
+      if (key < kv1) {
 #pragma unroll
-      for (int dt = 0; dt < T::DT; ++dt) {
-        const f32x4_t x = dka[kg][dt] * p.scale;
-        const f32x4_t y = dva[kg][dt];
-        *(u32x2_t*)(dkp + key * ss + 16 * dt + 4 * g) = u32x2_t{E::pack2(x[0], x[1]), E::pack2(x[2], x[3])};
-        *(u32x2_t*)(dvp + key * ss + 16 * dt + 4 * g) = u32x2_t{E::pack2(y[0], y[1]), E::pack2(y[2], y[3])};
+        for (int dt = 0; dt < T::DT; ++dt) {
+          const f32x4_t x = dka[kg][dt] * p.scale;
+          const f32x4_t y = dva[kg][dt];
+          *(u32x2_t*)(dkp + key * ss + 16 * dt + 4 * g) = u32x2_t{E::pack2(x[0], x[1]), E::pack2(x[2], x[3])};
+          *(u32x2_t*)(dvp + key * ss + 16 * dt + 4 * g) = u32x2_t{E::pack2(y[0], y[1]), E::pack2(y[2], y[3])};
+        }
       }
     }
+  };
+
+  const std::integral_constant<bool, false> more, stay;
+  const std::integral_constant<bool, true> last, switch_c;
+  if constexpr (PAIR) {
+    // both key tiles stream an even number of 64-row Q/dO tiles (a query count that is a multiple of
+    // 128), so the light tile starts in stage 0; the heavy tile's last step prefetches its first one
+    int j = 0;
+    for (; j + 2 < n_qt_a; j += 2) {
+      step(j, qs0, os0, rv0, qs1, os1, rv1, more, stay);
+      step(j + 1, qs1, os1, rv1, qs0, os0, rv0, more, stay);
+    }
+    step(j, qs0, os0, rv0, qs1, os1, rv1, more, stay);
+    step(j + 1, qs1, os1, rv1, qs0, os0, rv0, more, switch_c);
+    j += 2;
+    store_dkdv();
+    k_wg = kt_b * BK;
+    kw0 = k_wg + wave * KW;
+    rbase = -k_wg;  // row 0's position minus the light tile's first key (no offset)
+#pragma unroll
+    for (int kg = 0; kg < KG; ++kg)
+#pragma unroll
+      for (int dt = 0; dt < T::DT; ++dt) {
+        dka[kg][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        dva[kg][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    for (; j + 2 < n_qt; j += 2) {
+      step(j, qs0, os0, rv0, qs1, os1, rv1, more, stay);
+      step(j + 1, qs1, os1, rv1, qs0, os0, rv0, more, stay);
+    }
+    step(j, qs0, os0, rv0, qs1, os1, rv1, more, stay);
+    step(j + 1, qs1, os1, rv1, qs0, os0, rv0, last, stay);
+  } else if (n_qt > 0) {
+    int j = 0;
+    for (; j + 2 < n_qt; j += 2) {
+      step(j, qs0, os0, rv0, qs1, os1, rv1, more, stay);
+      step(j + 1, qs1, os1, rv1, qs0, os0, rv0, more, stay);
+    }
+    if (j + 2 == n_qt) {
+      step(j, qs0, os0, rv0, qs1, os1, rv1, more, stay);
+      step(j + 1, qs1, os1, rv1, qs0, os0, rv0, last, stay);
+    } else {
+      step(j, qs0, os0, rv0, qs1, os1, rv1, last, stay);
+    }
   }
+  store_dkdv();
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -897,6 +958,18 @@ hipError_t launch_bwd_t(BwdParams p, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_units_k == 0) return e;
+  // the dK/dV kernel pairs its heavy and light key tiles under the same condition (N_k = N_q)
+  if constexpr (CAUSAL && !WINDOW) {
+    if (pairs) {
+      BwdParams pp = p;
+      pp.n_tiles_k = p.n_tiles_k / 2;
+      pp.n_units_k = p.B * p.H * pp.n_tiles_k;
+      hipLaunchKernelGGL(
+          (fa_bwd_dkdv<D, IS_BF16, true, false, false, kDkdvWaves, kDkdvKeys, kDkdvMinBlocks, false, true>),
+          dim3(pp.n_units_k), dim3(64 * kDkdvWaves), 0, stream, pp);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((fa_bwd_dkdv<D, IS_BF16, CAUSAL, WINDOW, false, kDkdvWaves, kDkdvKeys, kDkdvMinBlocks>),
                      dim3(p.n_units_k), dim3(64 * kDkdvWaves), 0, stream, p);
   return hipGetLastError();
