@@ -132,8 +132,14 @@ def cpu_model():
 
 
 def smi_sample():
-    """GPU 0's gfx clocks (MHz, one per XCD) and hotspot temperature from amd-smi, or an error string."""
+    """GPU 0's gfx clocks (MHz, one per XCD) and hotspot temperature from amd-smi, or an error string.
+
+    Under rocprofv3 (ROCPROFILER_LIBRARY_CTOR set) nothing is sampled: the profiler's preloaded library
+    would start up inside the amd-smi child, which then starts its interpreter from a process that has
+    already touched the GPU."""
     import subprocess
+    if os.environ.get("ROCPROFILER_LIBRARY_CTOR"):
+        return {"t": round(time.time(), 2), "error": "not sampled under a profiler"}
     try:
         out = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "-t", "--json"], stdout=subprocess.PIPE,
                              stderr=subprocess.PIPE, text=True, timeout=30)
