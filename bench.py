@@ -90,8 +90,9 @@ def kernel_sha() -> str:
 def fwd_kernel_label(nq, nk, q_offset, window, chunks, causal=True, dtype="bf16", d=128):
     """Which forward kernel a call runs, by the library's own rule: fp32 runs fa_fwd_32; a 16-bit non-causal call
     whose query and key counts are multiples of 256 runs the ping-pong kernel; a whole causal problem pairs
-    256-query tiles (8 waves) when ceil(N/256) and ceil(N/64) are even, else 128-query tiles (4 waves) when
-    ceil(N/128) and ceil(N/64) are even; every other call runs one 128-query tile per workgroup."""
+    256-query tiles (8 waves) when ceil(N/256) and ceil(N/64) are even, on the ping-pong kernel when N is also
+    a multiple of 256, else 128-query tiles (4 waves) when ceil(N/128) and ceil(N/64) are even; every other
+    call runs one 128-query tile per workgroup."""
     if dtype == "fp32":
         return "fa_fwd_32<%d,%s>" % (d, "causal" if causal else "non-causal")
     if not causal:
@@ -102,6 +103,8 @@ def fwd_kernel_label(nq, nk, q_offset, window, chunks, causal=True, dtype="bf16"
         return "fa_fwd_16<%d,bf16,causal,window> (4 waves)" % d
     if chunks == 1 and q_offset == 0 and nq == nk and (nq + 63) // 64 % 2 == 0:
         if (nq + 255) // 256 % 2 == 0:
+            if nq % 256 == 0:
+                return "fa_fwd_16pp<%d,bf16,causal> (ping-pong, paired 256-query tiles, 8 waves)" % d
             return "fa_fwd_16<%d,bf16,causal> (paired 256-query tiles, 8 waves)" % d
         if (nq + 127) // 128 % 2 == 0:
             return "fa_fwd_16<%d,bf16,causal> (paired 128-query tiles, 4 waves)" % d

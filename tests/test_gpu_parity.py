@@ -133,13 +133,14 @@ def test_c5_bf16_causal_n65536_sampled():
 
 # ---- ragged sizes, both layouts, all dtypes ----------------------------------------------------------
 
-@pytest.mark.parametrize("N", [200, 256, 384, 385, 456, 640, 768, 1000])
+@pytest.mark.parametrize("N", [200, 256, 384, 385, 456, 512, 640, 768, 1000, 1536])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 def test_causal_tile_pairing_boundary(N, D, dtype):
     # whole causal problems run heavy and light query tiles in pairs when the tile count is even and the
     # sequence spans an even number of 64-key tiles, as 256-query tiles (8 waves) when possible, else as
-    # 128-query tiles: N = 384, 456, 1000 pair 256-query tiles; 200, 256, 768 pair 128-query tiles
+    # 128-query tiles: N = 512 and 1536 (multiples of 256) pair 256-query tiles on the ping-pong kernel;
+    # 384, 456, 1000 pair 256-query tiles on the lockstep kernel; 200, 256, 768 pair 128-query tiles
     # (an odd number of 256-query tiles); 385 (7 key tiles) and 640 (odd tile counts at both sizes) run
     # one 128-query tile per workgroup
     full_compare(2, 3, N, D, dtype, "BHSD", True, 1.0 / math.sqrt(D), 300 + N, "pairing N=%d D=%d %s" % (N, D, dtype))

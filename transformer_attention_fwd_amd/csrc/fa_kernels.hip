@@ -565,7 +565,9 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void fa_fwd_16(Params p) {
 // turn).  The matrix wave runs at the higher issue priority.  K/V tiles stream through a 4-stage LDS
 // ring: tile j+2 is issued at the start of M(j), once every wave has passed the barrier after its last
 // use of tile j-2; the extra stage lets a vector phase end with its V reads still in flight (they are
-// consumed by the next matrix phase).
+// consumed by the next matrix phase).  A whole causal problem runs as pairs: a workgroup takes the heavy
+// query tile n-1-r and then the light tile r of one head over one continuous K/V stream, so every
+// workgroup computes n+1 tiles of 256 rows by 256 keys.
 template <int D, bool IS_BF16, bool CAUSAL, bool PAIR>
 __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
   typedef Tile16<D, 8> T;
@@ -661,9 +663,15 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
   };
   auto issue_tile = [&](int j, uint8_t* kdst, uint8_t* vdst) __attribute__((always_inline)) {
     const int soff = key_of(j) * row_bytes;
+    // The LDS destination (m0) of every load is a stage's address plus this wave's offset.  Left visible,
+    // the compiler keeps all 16 sums live in SGPRs; in the causal build they then spill to VGPR lanes,
+    // and every DMA issue at the start of a matrix phase waits on v_readlane, a VALU instruction that
+    // competes with the other wave's exponentials.  One SGPR and a scalar add per load instead.
+    int wave_off = wave * 1024;
+    asm volatile("" : "+s"(wave_off));
 #pragma unroll
     for (int i = 0; i < T::LOADS; ++i) {
-      const int lds_off = (i * T::NW + wave) * 1024;
+      const int lds_off = i * T::NW * 1024 + wave_off;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(kbuf, (lds_void_t*)(kdst + lds_off), 16, voff_k, soff + i * load_step, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(vbuf, (lds_void_t*)(vdst + lds_off), 16, voff_v, soff + i * load_step, 0, 0);
     }
@@ -1217,8 +1225,9 @@ static hipError_t launch32(Params p, hipStream_t stream) {
 template <int D, bool IS_BF16>
 static hipError_t launch16_d(const Params& p, bool causal, hipStream_t stream) {
   // The ping-pong kernel runs non-causal calls whose query and key counts are multiples of 256 (its tiles
-  // go in groups of four 64-key tiles, and every wave of a 256-query workgroup then has rows).  Causal problems keep fa_fwd_16: the ping-pong kernel also handles whole
-  // causal problems as pairs (fa_fwd_16pp<..., true, true>) but measured slower there.
+  // go in groups of four 64-key tiles, and every wave of a 256-query workgroup then has rows) and whole
+  // causal problems of an even number of 256-query tiles, as heavy and light pairs.  Windows, offsets and
+  // key chunks keep fa_fwd_16 (there the ping-pong kernel measured slower: many of their tiles are masked).
 #ifndef FA_NO_PINGPONG
   constexpr bool kPingPong = true;
 #else
@@ -1236,6 +1245,9 @@ static hipError_t launch16_d(const Params& p, bool causal, hipStream_t stream) {
   const bool whole = p.delta == 0 && p.Nq == p.Nkv && p.kv_start == 0;
   const bool even_keys = ((p.Nq + Tile16<D>::BN - 1) / Tile16<D>::BN) % 2 == 0;
   const auto pairs = [&](int bm) { return whole && even_keys && ((p.Nq + bm - 1) / bm) % 2 == 0; };
+  // Pairs of 256-query tiles whose length is a multiple of 256 (every unit a whole number of groups of
+  // four 64-key tiles) run the ping-pong kernel.
+  if (kPingPong && pairs(Tile16<D, 8>::BM) && p.Nq % 256 == 0) return launch16pp<D, IS_BF16, true, true>(p, stream);
   if (pairs(Tile16<D, 8>::BM)) return launch16<D, IS_BF16, true, false, false, true, 8>(p, stream);
   if (pairs(Tile16<D, 4>::BM)) return launch16<D, IS_BF16, true, false, false, true, 4>(p, stream);
   return launch16<D, IS_BF16, true, false>(p, stream);
