@@ -78,13 +78,13 @@ __device__ __forceinline__ float quad_max(float x) {
 __device__ int* g_tile_rec = nullptr;
 __device__ long long g_tile_rec_cap = 0;
 #endif
-constexpr int kTileRecInts = 24;
-__device__ __forceinline__ void record_tiles(int kernel, int bh, int bm, int bn, int qw, int nw, int qa, int na, int qb,
-                                             int nb, int wave, int lane, int n_act) {
+[[maybe_unused]] constexpr int kTileRecInts = 24;
+__device__ __forceinline__ void record_tiles_at(int slot, int kernel, int bh, int bm, int bn, int qw, int nw, int qa,
+                                                int na, int qb, int nb, int wave, int lane, int n_act) {
 #ifdef FA_TILE_COUNT
   int* rec = g_tile_rec;
-  if (lane == 0 && rec != nullptr && (long long)blockIdx.x < g_tile_rec_cap) {
-    int* r = rec + (size_t)blockIdx.x * kTileRecInts;
+  if (lane == 0 && rec != nullptr && (long long)slot < g_tile_rec_cap) {
+    int* r = rec + (size_t)slot * kTileRecInts;
     if (wave == 0) {
       r[0] = bh;
       r[1] = bm;
@@ -103,6 +103,10 @@ __device__ __forceinline__ void record_tiles(int kernel, int bh, int bm, int bn,
   (void)kernel, (void)bh, (void)bm, (void)bn, (void)qw, (void)nw, (void)qa, (void)na, (void)qb, (void)nb, (void)wave,
       (void)lane, (void)n_act;
 #endif
+}
+__device__ __forceinline__ void record_tiles(int kernel, int bh, int bm, int bn, int qw, int nw, int qa, int na, int qb,
+                                             int nb, int wave, int lane, int n_act) {
+  record_tiles_at(blockIdx.x, kernel, bh, bm, bn, qw, nw, qa, na, qb, nb, wave, lane, n_act);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -590,22 +594,31 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
   const int g = lane >> 4;
   const int li = lane & 15;
 
-  int bh, qt, qt_b = 0;
+  // PAIR: a chain of n_pairs heavy/light pairs of one head (group c of the head's pairs, r = (c + 1) n_pairs
+  // - 1 down to c n_pairs; pair r is query tile n_full - 1 - r, then tile r).  The launcher pairs only whole
+  // causal problems of an even number of full 256-row tiles and splits the pairs evenly.  Descending, the
+  // only unit of four tiles (tile 0) ends its chain.
+  int bh, qt, c_grp = 0, n_pairs = 1;
+  const int n_full = p.Nq / T::BM;
   if constexpr (PAIR) {
-    int r;
-    unit_of(blockIdx.x, p.n_units, p.n_qtiles, false, bh, r);
-    const int n_full = (p.Nq + T::BM - 1) / T::BM;
-    qt = n_full - 1 - r;
-    qt_b = r;  // the launcher pairs only an even number of tiles
+    unit_of(blockIdx.x, p.n_units, p.n_qtiles, false, bh, c_grp);
+    n_pairs = (n_full / 2) / p.n_qtiles;
+    qt = n_full - (c_grp + 1) * n_pairs;
   } else {
     unit_of(blockIdx.x, p.n_units, p.n_qtiles, CAUSAL, bh, qt);
   }
+  // unit u of the chain: its query tile and its tile count (keys 0 .. the last key of its last row)
+  auto qt_of = [&](int u) __attribute__((always_inline)) {
+    const int r = (c_grp + 1) * n_pairs - 1 - (u >> 1);
+    return (u & 1) ? r : n_full - 1 - r;
+  };
+  auto q0_of_unit = [&](int u) __attribute__((always_inline)) { return qt_of(u) * T::BM + wave * T::QW; };
+  auto nt_of_unit = [&](int u) __attribute__((always_inline)) { return (qt_of(u) + 1) * (T::BM / T::BN); };
   const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
   const SeqGeom sg = seq_geometry<CAUSAL, false>(p, b, h, bh);
   const int Nq = sg.Nq, Nkv = sg.Nkv;
-  const int64_t delta = sg.delta;
-  const int q0a = qt * T::BM + wave * T::QW;    // first query of this wave in the (first) unit
-  const int q0b = qt_b * T::BM + wave * T::QW;  // ... in the light unit of a pair
+  const int64_t delta = PAIR ? 0 : sg.delta;  // pairs: whole causal problems (queries and keys from 0)
+  const int q0a = qt * T::BM + wave * T::QW;  // first query of this wave in the (first) unit
 
   const uint16_t* __restrict__ qg_ptr = (const uint16_t*)p.q + sg.q_base;
   const uint8_t* __restrict__ kg_ptr = (const uint8_t*)p.k + 2 * sg.kv_base;
@@ -617,9 +630,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
   // (the last key visible to the workgroup's last real query: a ragged last tile streams no further)
   const int k_last = CAUSAL ? (int)max((int64_t)-1, min((int64_t)Nkv - 1, min(q_wg + T::BM, Nq) - 1 + delta)) : Nkv - 1;
   const int n_kt_a = k_last >= 0 ? k_last / T::BN + 1 : 0;
-  const int n_kt_b = PAIR ? (int)min((int64_t)Nkv - 1, qt_b * T::BM + T::BM - 1 + delta) / T::BN + 1 : 0;
-  const int n_kt = n_kt_a + n_kt_b;
-  if (n_kt == 0) {  // no key at all (an empty chunk): O = 0, lse = -inf
+  if (n_kt_a == 0) {  // no key at all (an empty chunk): O = 0, lse = -inf
 #pragma unroll
     for (int qg = 0; qg < T::QG; ++qg) {
       const int qi = q0a + 16 * qg + li;
@@ -645,8 +656,6 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
     voff_v = row * row_bytes + ((pc ^ T::swz_v(row)) << 4);
   }
   const int load_step = (T::NW * 64 / T::CHUNKS) * row_bytes;
-  auto key_of = [&](int j) __attribute__((always_inline)) { return (j < n_kt_a ? j : j - n_kt_a) * T::BN; };
-  auto q0_of = [&](int j) __attribute__((always_inline)) { return (PAIR && j >= n_kt_a) ? q0b : q0a; };
   auto kstage = [&](auto st) __attribute__((always_inline)) -> uint8_t* {
     constexpr int s = decltype(st)::value % 4;
     if constexpr (s == 0) return ks0;
@@ -661,8 +670,8 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
     else if constexpr (s == 2) return vs2;
     else return vs3;
   };
-  auto issue_tile = [&](int j, uint8_t* kdst, uint8_t* vdst) __attribute__((always_inline)) {
-    const int soff = key_of(j) * row_bytes;
+  auto issue_tile = [&](int key, uint8_t* kdst, uint8_t* vdst) __attribute__((always_inline)) {
+    const int soff = key * row_bytes;
     // The LDS destination (m0) of every load is a stage's address plus this wave's offset.  Left visible,
     // the compiler keeps all 16 sums live in SGPRs; in the causal build they then spill to VGPR lanes,
     // and every DMA issue at the start of a matrix phase waits on v_readlane, a VALU instruction that
@@ -678,19 +687,30 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
   };
   constexpr int TILE_LOADS = 2 * T::LOADS;  // DMA instructions per wave and tile
   constexpr int Q_LOADS = T::QG * T::DC;    // global load instructions of one Q fragment set
+  // store instructions of finish() that a wait may leave in flight: the O stores (16 bytes per lane, one
+  // per two d tiles); the lse stores are not counted, which only makes the waits stricter
+  constexpr int O_STORES = T::QG * T::DT / 2;
 
+  // Q fragments; FLIP: apply the sign flip of a negative scale now (else flip_q() does it before the first
+  // use: a flip right after a load made the compiler wait there for every load in flight, the DMA too)
   vec8 qf[T::QG][T::DC];
-  auto load_q = [&](int qbase) __attribute__((always_inline)) {
+  auto load_q = [&](int qbase, auto flip_c) __attribute__((always_inline)) {
 #pragma unroll
     for (int qg = 0; qg < T::QG; ++qg) {
       const int qrow = min(qbase + 16 * qg + li, Nq - 1);
 #pragma unroll
       for (int c = 0; c < T::DC; ++c) {
         u32x4_t raw = *(const u32x4_t*)(qg_ptr + qrow * p.stride_s + 32 * c + 8 * g);
-        raw ^= p.qsign;
+        if constexpr (decltype(flip_c)::value) raw ^= p.qsign;
         qf[qg][c] = __builtin_bit_cast(vec8, raw);
       }
     }
+  };
+  auto flip_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int qg = 0; qg < T::QG; ++qg)
+#pragma unroll
+      for (int c = 0; c < T::DC; ++c) qf[qg][c] = __builtin_bit_cast(vec8, __builtin_bit_cast(u32x4_t, qf[qg][c]) ^ p.qsign);
   };
 
   const float cexp = p.c;
@@ -718,21 +738,32 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
     vb[dt] = vrow * T::ROW_BYTES + (((col >> 3) ^ T::swz_v(vrow)) << 4) + (col & 7) * 2;
   }
 
+  // O = acc / u and lse of the unit's rows.  A lane holds 4 columns of a row per 16-wide d tile, so direct
+  // stores would write 8 bytes per lane, 32 contiguous bytes per row and instruction.  Lanes g and g ^ 1
+  // (16 lanes apart, the same row) exchange the pieces of two d tiles instead: even g then holds columns 32 m + 4 g ..
+  // + 7, odd g columns 32 m + 16 + 4 (g - 1) .. + 7, and each 16-byte store writes 64 contiguous bytes of
+  // 16 rows.  At a unit switch the narrow stores cost about 3 % of the kernel.
   auto finish = [&](int q0) __attribute__((always_inline)) {
+    const bool odd = (g & 1) != 0;
 #pragma unroll
     for (int qg = 0; qg < T::QG; ++qg) {
       const float l = wave_sum_xor16_32(l_part[qg]);
       const float inv = uacc[qg][0] > 0.0f ? 1.0f / uacc[qg][0] : 0.0f;
       const int qi = q0 + 16 * qg + li;
-      if (qi < Nq) {
 #pragma unroll
-        for (int dt = 0; dt < T::DT; ++dt) {
-          const f32x4_t o = oacc[qg][dt] * inv;
-          u32x2_t w = {E::pack2(o[0], o[1]), E::pack2(o[2], o[3])};
-          *(u32x2_t*)(og_ptr + qi * p.stride_s + 16 * dt + 4 * g) = w;
-        }
-        if (g == 0) p.lse[sg.lse_base + qi] = (m_ref[qg] + __builtin_log2f(l)) * kLn2;
+      for (int m = 0; m < T::DT / 2; ++m) {
+        const f32x4_t o0 = oacc[qg][2 * m] * inv, o1 = oacc[qg][2 * m + 1] * inv;
+        const uint32_t a0 = E::pack2(o0[0], o0[1]), a1 = E::pack2(o0[2], o0[3]);  // d tile 2m, own columns
+        const uint32_t b0 = E::pack2(o1[0], o1[1]), b1 = E::pack2(o1[2], o1[3]);  // d tile 2m+1
+        // even lanes keep tile 2m and send tile 2m+1; odd lanes the reverse
+        const uint32_t s0 = odd ? a0 : b0, s1 = odd ? a1 : b1;
+        const uint32_t r0 = __shfl_xor(s0, 16), r1 = __shfl_xor(s1, 16);  // the partner's (lane ^ 16) half
+        const u32x4_t w = odd ? u32x4_t{r0, r1, b0, b1} : u32x4_t{a0, a1, r0, r1};
+        const int col = odd ? 16 * (2 * m + 1) + 4 * (g - 1) : 16 * (2 * m) + 4 * g;
+        // (pairs: every row is real, and every store must issue: the waits after a unit switch count them)
+        if (PAIR || qi < Nq) *(u32x4_t*)(og_ptr + qi * p.stride_s + col) = w;
       }
+      if (g == 0 && qi < Nq) p.lse[sg.lse_base + qi] = (m_ref[qg] + __builtin_log2f(l)) * kLn2;
     }
   };
 
@@ -795,20 +826,25 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
   // (and the Q loads issued after them) stay in flight, a constant count.  Stage safety: tile j+2 refills
   // the stage of tile j-2, whose last readers (waves 4-7's M(j-1), which drains its LDS reads) finish
   // before the barrier that precedes any wave's M(j); tile j+1 is first read after the next barrier.
-  auto issue_next = [&](int j, auto st) __attribute__((always_inline)) {
+  // (jl counts the unit's tiles; every unit starts at key 0, in stage 0)
+  auto issue_next = [&](int jl, auto st, int nt, bool more) __attribute__((always_inline)) {
     constexpr int S = decltype(st)::value;
-    issue_tile(min(j + 2, n_kt - 1), kstage(std::integral_constant<int, S + 2>()),
-               vstage(std::integral_constant<int, S + 2>()));
+    const int jn = jl + 2;
+    const int key = (jn < nt ? jn : (more ? jn - nt : nt - 1)) * T::BN;
+    issue_tile(key, kstage(std::integral_constant<int, S + 2>()), vstage(std::integral_constant<int, S + 2>()));
   };
 
   // matrix phase M(j): P.V of tile j-1 (stage st-1), then S of tile j (stage st).  PV: there is a tile
-  // j-1 (not on the kernel's first tile, where stage st-1 holds no data yet).  QLOAD: the heavy unit's
-  // last tile, after whose S^T the light unit's Q is loaded
-  auto mphase = [&](int j, auto st, auto pv_c, auto qload_c) __attribute__((always_inline)) {
+  // j-1 (not on the kernel's first tile, where stage st-1 holds no data yet).  qload: the last tile of a
+  // unit that another follows, after whose S^T the next unit's Q (first row q0_next) is loaded
+  // flip: the unit's first tile, whose Q was loaded unflipped
+  // stores: a unit's output was stored after the DMA of the tile this barrier waits for (the stores may
+  // stay in flight: vmcnt retires in issue order, so the count still covers that tile)
+  auto mphase = [&](int jl, auto st, auto pv_c, bool qload, int nt, bool more, int q0_next, bool flip = false,
+                    bool stores = false) __attribute__((always_inline)) {
     constexpr int S = decltype(st)::value;
     constexpr bool PV = decltype(pv_c)::value;
-    constexpr bool QLOAD = decltype(qload_c)::value;
-    issue_next(j, st);
+    issue_next(jl, st, nt, more);
     __builtin_amdgcn_s_setprio(1);
     const uint8_t* ks = kstage(st);
     vec8 ka[H], kc2[H];
@@ -826,6 +862,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
       for (int f = 0; f < H; ++f) ka[f] = k_frag(ks, f);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (flip) flip_q();
     // S^T = K Q^T, d-chunk outer (products into one accumulator KT * QG MFMAs apart); the first half of
     // the d-chunks runs while the second half's fragments are read
 #pragma unroll
@@ -843,10 +880,12 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
         if (g < H) kc2[g] = k_frag(ks, H + g);
         __builtin_amdgcn_sched_barrier(0);
       }
-    if (QLOAD) load_q(q0b);
+    if (qload) load_q(q0_next, std::false_type());
     __builtin_amdgcn_s_setprio(0);
     if (grp == 1) {  // group 1's barrier closes its matrix phase
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(QLOAD ? TILE_LOADS + Q_LOADS : TILE_LOADS));
+      if (qload) __builtin_amdgcn_s_waitcnt(waitcnt_vm(TILE_LOADS + Q_LOADS));
+      else if (stores) __builtin_amdgcn_s_waitcnt(waitcnt_vm(TILE_LOADS + O_STORES));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(TILE_LOADS));
       __builtin_amdgcn_sched_barrier(0);
       lds_barrier();
     }
@@ -854,24 +893,31 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
 
   // vector phase V(j); FIRST: the unit's first tile, which sets the reference maximum (every wave sees
   // key 0 of a whole causal or non-causal problem)
-  auto vphase = [&](int j, auto st, auto first_c, auto qload_c) __attribute__((always_inline)) {
+  // (first_rt: the same as FIRST, decided at run time)
+  auto vphase = [&](int jl, auto st, auto first_c, bool qload, int q0, bool first_rt = false, bool stores = false)
+                    __attribute__((always_inline)) {
     constexpr bool FIRST = decltype(first_c)::value;
-    constexpr bool QLOAD = decltype(qload_c)::value;
-    const int key0 = key_of(j);
-    const int q0 = q0_of(j);
-    const bool need_mask = (CAUSAL && key0 + T::BN - 1 > q0 + delta) || (key0 + T::BN > Nkv);
+    const int key0 = jl * T::BN;
+    // (pairs: no ragged tile, and the causal edge in 32 bits)
+    const bool need_mask = PAIR ? key0 + T::BN - 1 > q0
+                                : (CAUSAL && key0 + T::BN - 1 > q0 + delta) || (key0 + T::BN > Nkv);
     if (need_mask) {
       keep_branch();
-      const int dq0 = CAUSAL ? (int)max((int64_t)-512, min((int64_t)512, q0 + delta - key0)) : 0;
-      const int kend = min(512, Nkv - key0);
+      const int dq0 = PAIR ? max(-512, min(512, q0 - key0))
+                           : CAUSAL ? (int)max((int64_t)-512, min((int64_t)512, q0 + delta - key0)) : 0;
+      const int kend = PAIR ? 512 : min(512, Nkv - key0);
 #pragma unroll
       for (int qg = 0; qg < T::QG; ++qg) {
         const int hi = (CAUSAL ? min(kend - 1, dq0 + 16 * qg + li) : kend - 1) - 4 * g;
 #pragma unroll
-        for (int kt = 0; kt < T::KT; ++kt)
+        for (int kt = 0; kt < T::KT; ++kt) {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             if (16 * kt + r > hi) s[qg][kt][r] = kNegInf;
+          // each compare's lane mask (an SGPR pair) dies at its select: hoisted together, the 32 compares
+          // of a tile held 64 SGPRs and spilled
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     float part[T::QG];
@@ -893,7 +939,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
     bool slow[T::QG];
 #pragma unroll
     for (int qg = 0; qg < T::QG; ++qg) {
-      if constexpr (FIRST) {
+      if (FIRST || first_rt) {
         slow[qg] = true;
       } else {
         expo(qg);
@@ -932,18 +978,20 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
     // before the DMA refills this stage)
     __builtin_amdgcn_sched_barrier(0);
     if (grp == 0) {  // group 0's barrier closes its vector phase
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(QLOAD ? TILE_LOADS + Q_LOADS : TILE_LOADS));
+      if (qload) __builtin_amdgcn_s_waitcnt(waitcnt_vm(TILE_LOADS + Q_LOADS));
+      else if (stores) __builtin_amdgcn_s_waitcnt(waitcnt_vm(TILE_LOADS + O_STORES));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(TILE_LOADS));
       compiler_fence();
       __builtin_amdgcn_s_barrier();
       compiler_fence();
     }
   };
 
+  // Q before the first tiles: the wait for tile 0 covers it and leaves tile 1 in flight
+  load_q(q0a, std::false_type());
   issue_tile(0, ks0, vs0);
-  issue_tile(1, ks1, vs1);
-  load_q(q0a);
-  // tile 0 has landed once at most tile 1's loads and Q's are in flight
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(TILE_LOADS + Q_LOADS));
+  issue_tile(T::BN, ks1, vs1);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(TILE_LOADS));
   lds_barrier();
 
   const std::integral_constant<int, 0> st0;
@@ -951,56 +999,60 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
   const std::integral_constant<int, 2> st2;
   const std::integral_constant<int, 3> st3;
   const std::true_type first_c, pv_c;
-  const std::false_type later_c, noq_c;
-  // one unit, or the heavy and then the light unit of a pair.  Every unit's tile count is a multiple of 4
-  // (the launcher runs this kernel only for causal pairs of 256-query tiles of a sequence whose length is
-  // a multiple of 256, and for non-causal calls whose key count is a multiple of 256), so every unit
-  // starts in stage 0 and its tiles run in whole groups of four.  A heavy unit has at least 8 tiles.
-  auto run_unit = [&](auto unit_c) __attribute__((always_inline)) {
-    constexpr int U = decltype(unit_c)::value;
-    const int j0 = U == 0 ? 0 : n_kt_a;
-    const int j_end = U == 0 ? n_kt_a : n_kt;
-    // P.V of the previous unit's last tile (none before the first unit), S of this unit's first tile
-    mphase(j0, st0, std::integral_constant<bool, U == 1>(), noq_c);
-    if constexpr (U == 1) {  // the heavy unit's output is complete: store it and start the light unit
-      finish(q0a);
+  const std::false_type later_c;
+  // The chain's units run in groups of four tiles (every unit's tile count is a multiple of 4: the launcher
+  // runs this kernel only for causal pairs of whole 256-query tiles and for non-causal calls whose key
+  // count is a multiple of 256), so every unit starts in stage 0.  One loop over the groups: a unit's
+  // first matrix phase ends the previous unit, whose output is then stored, and its first vector phase
+  // sets the reference maximum (a loop per unit nested in a loop over units spilled registers).
+  int u = 0, nt = PAIR ? nt_of_unit(0) : n_kt_a, q0 = q0a;
+  bool more = PAIR && 2 * n_pairs > 1;
+  int q0_next = PAIR && more ? q0_of_unit(1) : q0;
+  // the first group: its first matrix phase has no P.V
+  mphase(0, st0, later_c, false, nt, more, q0_next, true);
+  vphase(0, st0, first_c, false, q0);
+  mphase(1, st1, pv_c, false, nt, more, q0_next);
+  vphase(1, st1, later_c, false, q0);
+  mphase(2, st2, pv_c, false, nt, more, q0_next);
+  vphase(2, st2, later_c, false, q0);
+  {
+    const bool ql = nt == 4 && more;
+    mphase(3, st3, pv_c, ql, nt, more, q0_next);
+    vphase(3, st3, later_c, ql, q0);
+  }
+  int jl = 4;
+#pragma unroll 1
+  while (true) {
+    bool unit_start = false;
+    int q0_prev = q0;
+    if (jl == nt) {
+      if (!more) break;
+      ++u;
+      nt = nt_of_unit(u);
+      q0 = q0_next;
+      more = u + 1 < 2 * n_pairs;
+      q0_next = more ? q0_of_unit(u + 1) : q0;
+      jl = 0;
+      unit_start = true;
+    }
+    mphase(jl, st0, pv_c, false, nt, more, q0_next, unit_start);
+    if (unit_start) {
+      finish(q0_prev);
       reset();
     }
-    vphase(j0, st0, first_c, noq_c);
-    mphase(j0 + 1, st1, pv_c, noq_c);
-    vphase(j0 + 1, st1, later_c, noq_c);
-    mphase(j0 + 2, st2, pv_c, noq_c);
-    vphase(j0 + 2, st2, later_c, noq_c);
-    mphase(j0 + 3, st3, pv_c, noq_c);
-    vphase(j0 + 3, st3, later_c, noq_c);
-    if (j_end - j0 > 4) {
-#pragma unroll 1
-      for (int j = j0 + 4; j < j_end - 4; j += 4) {
-        mphase(j, st0, pv_c, noq_c);
-        vphase(j, st0, later_c, noq_c);
-        mphase(j + 1, st1, pv_c, noq_c);
-        vphase(j + 1, st1, later_c, noq_c);
-        mphase(j + 2, st2, pv_c, noq_c);
-        vphase(j + 2, st2, later_c, noq_c);
-        mphase(j + 3, st3, pv_c, noq_c);
-        vphase(j + 3, st3, later_c, noq_c);
-      }
-      // the unit's last four tiles; after the heavy unit's last S^T, the light unit's Q is loaded
-      const int j = j_end - 4;
-      constexpr bool QL = PAIR && U == 0;
-      const std::integral_constant<bool, QL> ql_c;
-      mphase(j, st0, pv_c, noq_c);
-      vphase(j, st0, later_c, noq_c);
-      mphase(j + 1, st1, pv_c, noq_c);
-      vphase(j + 1, st1, later_c, noq_c);
-      mphase(j + 2, st2, pv_c, noq_c);
-      vphase(j + 2, st2, later_c, noq_c);
-      mphase(j + 3, st3, pv_c, ql_c);
-      vphase(j + 3, st3, later_c, ql_c);
-    }
-  };
-  run_unit(std::integral_constant<int, 0>());
-  if constexpr (PAIR) run_unit(std::integral_constant<int, 1>());
+    // the two barriers after the previous unit's stores, in each group, leave them in flight
+    vphase(jl, st0, later_c, false, q0, unit_start, unit_start);
+    mphase(jl + 1, st1, pv_c, false, nt, more, q0_next, false, unit_start);
+    vphase(jl + 1, st1, later_c, false, q0, false, unit_start);
+    mphase(jl + 2, st2, pv_c, false, nt, more, q0_next);
+    vphase(jl + 2, st2, later_c, false, q0);
+    // the unit's last group loads the next unit's Q after its last S^T
+    const bool ql = jl + 4 == nt && more;
+    mphase(jl + 3, st3, pv_c, ql, nt, more, q0_next);
+    vphase(jl + 3, st3, later_c, ql, q0);
+    jl += 4;
+  }
+  const int q0_last = q0;
   // the last tile's P.V product (the second half of its V fragments from its stage, the last one)
   __builtin_amdgcn_s_setprio(1);
   {
@@ -1011,9 +1063,17 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
   }
   __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the refetches past the end land before the LDS is released
-  finish(PAIR ? q0b : q0a);
+  finish(q0_last);
   // every wave computes on every tile of the stream
-  record_tiles(1, bh, T::BM, T::BN, T::QW, T::NW, q_wg, n_kt_a, PAIR ? qt_b * T::BM : -1, n_kt_b, wave, lane, n_kt);
+  if constexpr (PAIR) {
+    for (int i = 0; i < n_pairs; ++i) {
+      const int na = nt_of_unit(2 * i), nb = nt_of_unit(2 * i + 1);
+      record_tiles_at(blockIdx.x * n_pairs + i, 1, bh, T::BM, T::BN, T::QW, T::NW, qt_of(2 * i) * T::BM, na,
+                      qt_of(2 * i + 1) * T::BM, nb, wave, lane, na + nb);
+    }
+  } else {
+    record_tiles(1, bh, T::BM, T::BN, T::QW, T::NW, q_wg, n_kt_a, -1, 0, wave, lane, n_kt_a);
+  }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -1207,7 +1267,11 @@ template <int D, bool IS_BF16, bool CAUSAL, bool PAIR>
 static hipError_t launch16pp(Params p, hipStream_t stream) {
   typedef Tile16<D, 8> T;
   p.n_qtiles = (p.Nq + T::BM - 1) / T::BM;
-  if (PAIR) p.n_qtiles = (p.n_qtiles + 1) / 2;
+  // Pairs: one heavy/light pair per workgroup.  The kernel also takes chains of several pairs of a head
+  // (n_qtiles = chains per head), which pay the prologue, the drain and the dispatch gap once; they
+  // measured slower (C3: 2, 4, 8 pairs -0.5, -3, -11 %; C5 4 pairs -2 %): fewer workgroups of a head
+  // stream its K/V side by side through L2.
+  if (PAIR) p.n_qtiles = p.n_qtiles / 2;
   p.n_units = p.n_qtiles * p.B * p.H;
   hipLaunchKernelGGL((fa_fwd_16pp<D, IS_BF16, CAUSAL, PAIR>), dim3(p.n_units), dim3(512), 0, stream, p);
   return hipGetLastError();
