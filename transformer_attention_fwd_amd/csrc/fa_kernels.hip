@@ -319,21 +319,26 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void fa_fwd_16(Params p) {
   // epilogue of the current unit: O = acc / u, lse = (m + log2 l) ln 2; a row without any visible key
   // has u = l = 0 and gets O = 0, lse = -inf
   uint16_t* og_ptr = (uint16_t*)p.o + sg.q_base;
+  // (16-byte stores: lanes 16 apart, the same row, exchange the pieces of two d tiles, as in fa_fwd_16pp)
   auto finish = [&]() __attribute__((always_inline)) {
+    const bool odd = (g & 1) != 0;
 #pragma unroll
     for (int qg = 0; qg < T::QG; ++qg) {
       const float l = wave_sum_xor16_32(l_part[qg]);
       const float inv = uacc[qg][0] > 0.0f ? 1.0f / uacc[qg][0] : 0.0f;
       const int qi = q0 + 16 * qg + li;
-      if (qi < Nq) {
 #pragma unroll
-        for (int dt = 0; dt < T::DT; ++dt) {
-          const f32x4_t o = oacc[qg][dt] * inv;
-          u32x2_t w = {E::pack2(o[0], o[1]), E::pack2(o[2], o[3])};
-          *(u32x2_t*)(og_ptr + qi * p.stride_s + 16 * dt + 4 * g) = w;
-        }
-        if (g == 0) p.lse[sg.lse_base + qi] = (m_ref[qg] + __builtin_log2f(l)) * kLn2;
+      for (int m = 0; m < T::DT / 2; ++m) {
+        const f32x4_t o0 = oacc[qg][2 * m] * inv, o1 = oacc[qg][2 * m + 1] * inv;
+        const uint32_t a0 = E::pack2(o0[0], o0[1]), a1 = E::pack2(o0[2], o0[3]);
+        const uint32_t b0 = E::pack2(o1[0], o1[1]), b1 = E::pack2(o1[2], o1[3]);
+        const uint32_t s0 = odd ? a0 : b0, s1 = odd ? a1 : b1;
+        const uint32_t r0 = __shfl_xor(s0, 16), r1 = __shfl_xor(s1, 16);  // (the partner has the same row)
+        const u32x4_t w = odd ? u32x4_t{r0, r1, b0, b1} : u32x4_t{a0, a1, r0, r1};
+        const int col = odd ? 16 * (2 * m + 1) + 4 * (g - 1) : 16 * (2 * m) + 4 * g;
+        if (qi < Nq) *(u32x4_t*)(og_ptr + qi * p.stride_s + col) = w;
       }
+      if (g == 0 && qi < Nq) p.lse[sg.lse_base + qi] = (m_ref[qg] + __builtin_log2f(l)) * kLn2;
     }
   };
 
