@@ -278,9 +278,18 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
 
   // sw_c: the heavy tile's last step of a pair, which loads the light tile's Q and dO fragments once its
   // own S^T and dP^T products no longer need them
+  // stores_in_flight: the first step after a pair's switch, whose wait leaves the heavy tile's dQ stores
+  // (issued after this tile's DMA; the memory counter retires in order) in flight
+  constexpr int kDqStores = QG * T::DT / 2;
+  bool stores_in_flight = false;
   auto step = [&](int j, const uint8_t* ks, const uint8_t* vs, uint8_t* kn, uint8_t* vn, auto last_c, auto sw_c)
       __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    if (stores_in_flight) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDqStores));
+      stores_in_flight = false;
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
     lds_barrier();
     if constexpr (!decltype(last_c)::value) issue_tile(j + 1, kn, vn);
     constexpr bool switch_unit = decltype(sw_c)::value;
@@ -361,18 +370,25 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
   };
 
   // dQ = scale * accumulated (dS K) over the chunk's keys (0 when it sees none); lane holds d =
-  // 16*dt + 4*g + r of query q0 + 16*qg + li
+  // 16*dt + 4*g + r of query q0s + 16*qg + li.  16-byte stores: lanes 16 apart (the same row) exchange the
+  // pieces of two d tiles, so each store writes 64 contiguous bytes of 16 rows (as the forward's output)
   uint16_t* dqp = (uint16_t*)p.dq + qhead;
-  auto store_dq = [&]() __attribute__((always_inline)) {
+  auto store_dq = [&](int q0s) __attribute__((always_inline)) {
+    const bool odd = (g & 1) != 0;
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg) {
-      const int qi = q0 + 16 * qg + li;
-      if (qi < Nq) {
+      const int qi = q0s + 16 * qg + li;
 #pragma unroll
-        for (int dt = 0; dt < T::DT; ++dt) {
-          const f32x4_t x = dqa[qg][dt] * p.scale;
-          *(u32x2_t*)(dqp + qi * ss + 16 * dt + 4 * g) = u32x2_t{E::pack2(x[0], x[1]), E::pack2(x[2], x[3])};
-        }
+      for (int m = 0; m < T::DT / 2; ++m) {
+        const f32x4_t x0 = dqa[qg][2 * m] * p.scale, x1 = dqa[qg][2 * m + 1] * p.scale;
+        const uint32_t a0 = E::pack2(x0[0], x0[1]), a1 = E::pack2(x0[2], x0[3]);
+        const uint32_t b0 = E::pack2(x1[0], x1[1]), b1 = E::pack2(x1[2], x1[3]);
+        const uint32_t s0 = odd ? a0 : b0, s1 = odd ? a1 : b1;
+        const uint32_t r0 = __shfl_xor(s0, 16), r1 = __shfl_xor(s1, 16);
+        const u32x4_t w = odd ? u32x4_t{r0, r1, b0, b1} : u32x4_t{a0, a1, r0, r1};
+        const int col = odd ? 16 * (2 * m + 1) + 4 * (g - 1) : 16 * (2 * m) + 4 * g;
+        // (pairs: every row is real, and every store must issue: the next step's wait counts them)
+        if (PAIR || qi < Nq) *(u32x4_t*)(dqp + qi * ss + col) = w;
       }
     }
   };
@@ -391,15 +407,19 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
     step(j, ks0, vs0, ks1, vs1, more, stay);
     step(j + 1, ks1, vs1, ks0, vs0, more, switch_c);
     j += 2;
-    store_dq();
+    // the light tile's row values first (their loads are waited for at once), then the heavy tile's dQ,
+    // whose stores the light tile's first step leaves in flight
+    const int q0_heavy = q0;
     q_wg = qt_b * BM;
     q0 = q_wg + wave * QW;
     rbase = q_wg;  // the whole problem: no offset, keys from 0
     row_values(q0);
+    store_dq(q0_heavy);
 #pragma unroll
     for (int qg = 0; qg < QG; ++qg)
 #pragma unroll
       for (int dt = 0; dt < T::DT; ++dt) dqa[qg][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    stores_in_flight = true;  // (cleared by the light tile's first step)
     for (; j + 2 < n_kt; j += 2) {
       step(j, ks0, vs0, ks1, vs1, more, stay);
       step(j + 1, ks1, vs1, ks0, vs0, more, stay);
@@ -419,7 +439,7 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq(BwdParams p) {
       step(j, ks0, vs0, ks1, vs1, last, stay);
     }
   }
-  store_dq();
+  store_dq(q0);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -650,6 +670,9 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
   };
   // atomic instructions a wave issues per Q/dO tile (both 32-query steps)
   constexpr int kAtomicsPerTile = ATOMIC_DQ ? (BQ / QS) * 4 * DTW : 0;
+  // store instructions of store_dkdv (dK and dV, 16 bytes per lane)
+  constexpr int kDkdvStores = KG * T::DT;
+  bool stores_in_flight = false;
 
   // sw_c: the heavy key tile's last step of a pair, which loads the light tile's K and V once its last
   // S and dP products no longer need them
@@ -657,9 +680,16 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
                   auto last_c, auto sw_c) __attribute__((always_inline)) {
     constexpr bool switch_unit = decltype(sw_c)::value;
     // this wave's share of tile j has landed (the atomic mode leaves the previous tile's atomics, issued after
-    // tile j's DMA, in flight)
-    if (ATOMIC_DQ && j > 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kAtomicsPerTile));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    // tile j's DMA, in flight; the first step after a pair's switch leaves the heavy tile's dK/dV stores, issued
+    // after them, in flight too: the memory counter retires in order)
+    if (stores_in_flight) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kAtomicsPerTile + kDkdvStores));
+      stores_in_flight = false;
+    } else if (ATOMIC_DQ && j > 0) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(kAtomicsPerTile));
+    } else {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
     lds_barrier();
     // the next tile's row values are loaded before its DMA is issued (the memory counter retires in
     // order) and stored to LDS after this tile's work, for the next barrier to publish
@@ -808,18 +838,26 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
   // key kw0 + 16*kg + li; rows outside the chunk are left as they are
   uint16_t* dkp = (uint16_t*)p.dk + khead;
   uint16_t* dvp = (uint16_t*)p.dv + khead;
+  // (16-byte stores: lanes 16 apart, the same key, exchange the pieces of two d tiles, as in the forward)
   auto store_dkdv = [&]() __attribute__((always_inline)) {
+    const bool odd = (g & 1) != 0;
+    auto put = [&](uint16_t* base, int key, f32x4_t x0, f32x4_t x1, int m) __attribute__((always_inline)) {
+      const uint32_t a0 = E::pack2(x0[0], x0[1]), a1 = E::pack2(x0[2], x0[3]);
+      const uint32_t b0 = E::pack2(x1[0], x1[1]), b1 = E::pack2(x1[2], x1[3]);
+      const uint32_t s0 = odd ? a0 : b0, s1 = odd ? a1 : b1;
+      const uint32_t r0 = __shfl_xor(s0, 16), r1 = __shfl_xor(s1, 16);
+      const u32x4_t w = odd ? u32x4_t{r0, r1, b0, b1} : u32x4_t{a0, a1, r0, r1};
+      const int col = odd ? 16 * (2 * m + 1) + 4 * (g - 1) : 16 * (2 * m) + 4 * g;
+      // (pairs: every key is real, and every store must issue: the next step's wait counts them)
+      if (PAIR || key < kv1) *(u32x4_t*)(base + key * ss + col) = w;
+    };
 #pragma unroll
     for (int kg = 0; kg < KG; ++kg) {
       const int key = kw0 + 16 * kg + li;
-      if (key < kv1) {
 #pragma unroll
-        for (int dt = 0; dt < T::DT; ++dt) {
-          const f32x4_t x = dka[kg][dt] * p.scale;
-          const f32x4_t y = dva[kg][dt];
-          *(u32x2_t*)(dkp + key * ss + 16 * dt + 4 * g) = u32x2_t{E::pack2(x[0], x[1]), E::pack2(x[2], x[3])};
-          *(u32x2_t*)(dvp + key * ss + 16 * dt + 4 * g) = u32x2_t{E::pack2(y[0], y[1]), E::pack2(y[2], y[3])};
-        }
+      for (int m = 0; m < T::DT / 2; ++m) {
+        put(dkp, key, dka[kg][2 * m] * p.scale, dka[kg][2 * m + 1] * p.scale, m);
+        put(dvp, key, dva[kg][2 * m], dva[kg][2 * m + 1], m);
       }
     }
   };
@@ -838,6 +876,7 @@ __global__ __launch_bounds__(NW * 64, MINB) void fa_bwd_dkdv(BwdParams p) {
     step(j + 1, qs1, os1, rv1, qs0, os0, rv0, more, switch_c);
     j += 2;
     store_dkdv();
+    stores_in_flight = true;  // (cleared by the light tile's first step)
     k_wg = kt_b * BK;
     kw0 = k_wg + wave * KW;
     rbase = -k_wg;  // row 0's position minus the light tile's first key (no offset)
