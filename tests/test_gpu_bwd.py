@@ -96,8 +96,10 @@ def test_large_logits():
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.2, 0.5])
-def test_scale_values(scale):
-    full_compare(1, 2, 190, 64, "bf16", "BHSD", True, scale, 13, "bwd scale %g" % scale)
+@pytest.mark.parametrize("N", [190, 512])
+def test_scale_values(scale, N):
+    # N = 512: the paired backward kernels, on O and lse from the ping-pong forward
+    full_compare(1, 2, N, 64, "bf16", "BHSD", True, scale, 13 + N, "bwd scale %g N=%d" % (scale, N))
 
 
 def test_single_key_rows():

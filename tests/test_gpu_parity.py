@@ -213,9 +213,13 @@ def test_fp32_large_logits_within_dot_product_bound():
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.09, 0.7])
-def test_scale_values(scale):
+@pytest.mark.parametrize("N,D", [(300, 64), (512, 128), (1024, 64)])
+def test_scale_values(scale, N, D):
+    # a negative scale flips Q's sign bits: N = 300 runs the lockstep kernel, N = 512 and 1024 the ping-pong
+    # kernel (causal pairs, non-causal units), which flips each unit's Q right before its first product
     for causal in (False, True):
-        full_compare(1, 2, 300, 64, "bf16", "BSND", causal, scale, 51, "scale=%g causal=%d" % (scale, causal))
+        full_compare(1, 2, N, D, "bf16", "BSND", causal, scale, 51 + N,
+                     "scale=%g N=%d D=%d causal=%d" % (scale, N, D, causal))
 
 
 # ---- bit-exact properties of the kernel ----------------------------------------------------------------
