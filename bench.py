@@ -101,6 +101,13 @@ def fwd_kernel_label(nq, nk, q_offset, window, chunks, causal=True, dtype="bf16"
         return "fa_fwd_16<%d,bf16,non-causal> (one 128-query tile per workgroup, 4 waves)" % d
     if window >= 0:
         return "fa_fwd_16<%d,bf16,causal,window> (4 waves)" % d
+    if chunks > 1:
+        parts = chunk_launches(nq, nk, q_offset, chunks)
+        if all(p is not None for p in parts):
+            return ("per key chunk: fa_fwd_16pp<%d,bf16,causal> (ping-pong pairs) on the chunk's square rows + "
+                    "fa_fwd_16pp<%d,bf16,non-causal> on the rows after it + fa_fwd_16<%d,bf16,causal> (O = 0, "
+                    "lse = -inf) on the rows before it" % (d, d, d))
+        return "fa_fwd_16<%d,bf16,causal> (one 128-query tile per workgroup, 4 waves) per key chunk" % d
     if chunks == 1 and q_offset == 0 and nq == nk and (nq + 63) // 64 % 2 == 0:
         if (nq + 255) // 256 % 2 == 0:
             if nq % 256 == 0:
@@ -109,6 +116,21 @@ def fwd_kernel_label(nq, nk, q_offset, window, chunks, causal=True, dtype="bf16"
         if (nq + 127) // 128 % 2 == 0:
             return "fa_fwd_16<%d,bf16,causal> (paired 128-query tiles, 4 waves)" % d
     return "fa_fwd_16<%d,bf16,causal> (one 128-query tile per workgroup, 4 waves)" % d
+
+
+def chunk_launches(nq, nk, q_offset, chunks):
+    """Per key chunk of a causal call: the kernel launches the library's rule gives when it splits the chunk
+    into row ranges (rows before the chunk's first key, its square, the rows after it), or None when the
+    chunk runs as one fa_fwd_16 launch: the chunk length a multiple of 512, its first key at a query row
+    (q_offset <= kv_start) and the rows after the square a multiple of 256."""
+    out = []
+    for c in range(chunks):
+        a, b = nk * c // chunks, nk * (c + 1) // chunks
+        i0, kv_len = a - q_offset, b - a
+        rest = nq - i0 - kv_len
+        ok = i0 >= 0 and kv_len > 0 and kv_len % 512 == 0 and rest >= 0 and rest % 256 == 0
+        out.append((i0 > 0) + 1 + (rest > 0) if ok else None)
+    return out
 
 
 def log(msg):
@@ -364,7 +386,10 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel": fwd_kernel_label(Nq, Nk, q_offset, window, chunks, w.causal, dtype, D),
-                "mean_launch_ms": round(mean_attn_ms / chunks, 5), "launches_per_step": chunks,
+                "mean_launch_ms": round(mean_attn_ms / chunks, 5),
+                "launches_per_step": (sum(n or 1 for n in chunk_launches(Nq, Nk, q_offset, chunks))
+                                      if chunks > 1 and w.causal and window < 0 else chunks),
+                "calls_per_step": chunks,
                 "kernel_sha": kernel_sha()}
     extra = {}
     if chunks > 1:

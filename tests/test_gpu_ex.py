@@ -67,6 +67,60 @@ def test_split_kv_chunks_and_merge(dtype, causal, layout):
     _check_ex(om, lm, o_ref, l_ref, dtype, "merged %d chunks %s %s c=%d" % (len(cuts) - 1, dtype, layout, causal))
 
 
+# Key chunks that the library splits into row ranges (rows before the chunk's first key: no key; the
+# square of the chunk: a whole causal problem; later rows: every key of the chunk): the chunk length a
+# multiple of 512 and the rows after the square a multiple of 256.  N = 2048 in chunks of 512 is the
+# 4-chunk split of a 4096-token sequence at half size; the others start the square at an odd row, leave
+# no rows after it, or none before it.
+@pytest.mark.parametrize("case", [
+    dict(nq=2048, nk=2048, q_offset=0, chunks=((0, 512), (512, 512), (1024, 512), (1536, 512)), D=128,
+         dtype="bf16", layout="BHSD", scale=0.09),
+    dict(nq=2048, nk=2048, q_offset=0, chunks=((0, 1024), (1024, 1024)), D=64, dtype="fp16", layout="BSND",
+         scale=0.125),
+    dict(nq=1068, nk=1068, q_offset=0, chunks=((300, 512),), D=128, dtype="bf16", layout="BSND", scale=-0.09),
+    dict(nq=1024, nk=2048, q_offset=512, chunks=((1024, 512),), D=64, dtype="bf16", layout="BHSD", scale=0.125),
+    dict(nq=768, nk=512, q_offset=0, chunks=((0, 512),), D=128, dtype="fp16", layout="BHSD", scale=0.09),
+])
+def test_chunk_split_row_ranges(case):
+    c = case
+    B, H, D, dtype, layout = 1, 2, c["D"], c["dtype"], c["layout"]
+    q, k, v = _make_qk(B, H, c["nq"], c["nk"], D, layout, dtype, seed=700 + c["nq"])
+    qd, kd, vd = (to_dev(x, dtype) for x in (q, k, v))
+    o_parts, l_parts = [], []
+    for kv_start, kv_len in c["chunks"]:
+        kw = dict(q_offset=c["q_offset"], kv_start=kv_start, kv_len=kv_len)
+        what = "split chunk %s nq=%d D=%d %s %s" % (kw, c["nq"], D, dtype, layout)
+        _say(what)
+        o, l = fa.attention_ex(qd, kd, vd, layout=layout, causal=True, scale=c["scale"], **kw)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.attention_ex(q, k, v, dtype=dtype, layout=layout, causal=True, scale=c["scale"],
+                                           nthreads=NTHREADS, **kw)
+        _check_ex(o, l, o_ref, l_ref, dtype, what)
+        # each row range holds what one kernel computes for it alone: the square as a whole causal problem
+        # on the chunk's keys, the later rows as a non-causal problem on them
+        i0 = kv_start - c["q_offset"]
+        rows = (lambda t, a, b: t[:, :, a:b]) if layout == "BHSD" else (lambda t, a, b: t[:, a:b])
+        kc, vc = rows(kd, kv_start, kv_start + kv_len).contiguous(), rows(vd, kv_start, kv_start + kv_len).contiguous()
+        o_sq, l_sq = fa.attention(rows(qd, i0, i0 + kv_len).contiguous(), kc, vc, layout=layout, causal=True,
+                                  scale=c["scale"])
+        torch.cuda.synchronize()
+        assert torch.equal(rows(o, i0, i0 + kv_len), o_sq) and torch.equal(l[:, :, i0:i0 + kv_len], l_sq), what
+        if i0 + kv_len < c["nq"]:
+            o_r, l_r = fa.attention_ex(rows(qd, i0 + kv_len, c["nq"]).contiguous(), kc, vc, layout=layout,
+                                       causal=False, scale=c["scale"])
+            torch.cuda.synchronize()
+            assert torch.equal(rows(o, i0 + kv_len, c["nq"]), o_r), what
+            assert torch.equal(l[:, :, i0 + kv_len:], l_r), what
+        o_parts.append(o)
+        l_parts.append(l)
+    if len(c["chunks"]) > 1:
+        om, lm = fa.merge(torch.stack(o_parts), torch.stack(l_parts), layout=layout)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.attention_ex(q, k, v, dtype=dtype, layout=layout, causal=True, scale=c["scale"],
+                                           q_offset=c["q_offset"], nthreads=NTHREADS)
+        _check_ex(om, lm, o_ref, l_ref, dtype, "merged split nq=%d %s %s" % (c["nq"], dtype, layout))
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
 @pytest.mark.parametrize("nq,nk", [(1, 4097), (100, 1000), (130, 130), (7, 300)])
 def test_bottom_right_causal(dtype, nq, nk):

@@ -74,14 +74,21 @@ __device__ __forceinline__ float quad_max(float x) {
 // test can hold them against the closed form of the visibility rule.  Record of block x (kTileRecInts ints):
 // [0] b*H + h (the head slot), [1] queries per unit, [2] keys per tile, [3] queries per wave, [4] first query
 // of the first unit, [5] tiles it streams, [6] first query of a pair's light unit or -1, [7] its tiles,
-// [8 + w] tiles wave w computes on (both units), [16] waves, [17] 0 for fa_fwd_16, 1 for fa_fwd_16pp.
+// [8 + w] tiles wave w computes on (both units), [16] waves, [17] 0 for fa_fwd_16, 1 for fa_fwd_16pp,
+// [18] the row after the record's last real row (a unit's rows end there).
 __device__ int* g_tile_rec = nullptr;
 __device__ long long g_tile_rec_cap = 0;
 #endif
 [[maybe_unused]] constexpr int kTileRecInts = 24;
-__device__ __forceinline__ void record_tiles_at(int slot, int kernel, int bh, int bm, int bn, int qw, int nw, int qa,
-                                                int na, int qb, int nb, int wave, int lane, int n_act) {
+// (slots count from the launch's rec_base, rows from its q_row0: a call split into launches over row ranges
+// records like one launch over all rows)
+__device__ __forceinline__ void record_tiles_at(const Params& p, int slot, int kernel, int bh, int bm, int bn, int qw,
+                                                int nw, int qa, int na, int qb, int nb, int wave, int lane, int n_act,
+                                                int row_end) {
 #ifdef FA_TILE_COUNT
+  slot += p.rec_base;
+  qa += p.q_row0;
+  if (qb >= 0) qb += p.q_row0;
   int* rec = g_tile_rec;
   if (lane == 0 && rec != nullptr && (long long)slot < g_tile_rec_cap) {
     int* r = rec + (size_t)slot * kTileRecInts;
@@ -96,17 +103,18 @@ __device__ __forceinline__ void record_tiles_at(int slot, int kernel, int bh, in
       r[7] = nb;
       r[16] = nw;
       r[17] = kernel;
+      r[18] = p.q_row0 + row_end;
     }
     r[8 + wave] = n_act;
   }
 #else
-  (void)kernel, (void)bh, (void)bm, (void)bn, (void)qw, (void)nw, (void)qa, (void)na, (void)qb, (void)nb, (void)wave,
-      (void)lane, (void)n_act;
+  (void)p, (void)slot, (void)kernel, (void)bh, (void)bm, (void)bn, (void)qw, (void)nw, (void)qa, (void)na, (void)qb,
+      (void)nb, (void)wave, (void)lane, (void)n_act, (void)row_end;
 #endif
 }
-__device__ __forceinline__ void record_tiles(int kernel, int bh, int bm, int bn, int qw, int nw, int qa, int na, int qb,
-                                             int nb, int wave, int lane, int n_act) {
-  record_tiles_at(blockIdx.x, kernel, bh, bm, bn, qw, nw, qa, na, qb, nb, wave, lane, n_act);
+__device__ __forceinline__ void record_tiles(const Params& p, int kernel, int bh, int bm, int bn, int qw, int nw, int qa,
+                                             int na, int qb, int nb, int wave, int lane, int n_act, int row_end) {
+  record_tiles_at(p, blockIdx.x, kernel, bh, bm, bn, qw, nw, qa, na, qb, nb, wave, lane, n_act, row_end);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -160,9 +168,9 @@ __device__ __forceinline__ SeqGeom seq_geometry(const Params& p, int b, int h, i
     sg.Nkv = p.Nkv;
     sg.delta = p.delta;
     sg.window = p.window;
-    sg.q_base = b * p.stride_b_q + h * p.stride_h_q;
+    sg.q_base = b * p.stride_b_q + h * p.stride_h_q + (int64_t)p.q_row0 * p.stride_s;
     sg.kv_base = b * p.stride_b_k + h * p.stride_h_k + p.kv_start * p.stride_s;
-    sg.lse_base = (int64_t)bh * p.Nq;
+    sg.lse_base = (int64_t)bh * p.lse_rows + p.q_row0;
   }
   return sg;
 }
@@ -223,7 +231,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void fa_fwd_16(Params p) {
   const int q_wg_a = q_wg;
   int n_act = 0;  // tiles this wave computes on (recorded by the test-only build)
   if (n_kt == 0) {  // no query of this workgroup sees any key of the chunk: O = 0, lse = -inf
-    record_tiles(0, bh, T::BM, T::BN, T::QW, T::NW, q_wg, 0, -1, 0, wave, lane, 0);
+    record_tiles(p, 0, bh, T::BM, T::BN, T::QW, T::NW, q_wg, 0, -1, 0, wave, lane, 0, p.Nq);
     uint16_t* og = (uint16_t*)p.o + sg.q_base;
 #pragma unroll
     for (int qg = 0; qg < T::QG; ++qg) {
@@ -555,7 +563,8 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void fa_fwd_16(Params p) {
     }
   }
   finish();
-  record_tiles(0, bh, T::BM, T::BN, T::QW, T::NW, q_wg_a, n_kt_a, PAIR ? qt_b * T::BM : -1, n_kt_b, wave, lane, n_act);
+  record_tiles(p, 0, bh, T::BM, T::BN, T::QW, T::NW, q_wg_a, n_kt_a, PAIR ? qt_b * T::BM : -1, n_kt_b, wave, lane,
+               n_act, p.Nq);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -577,7 +586,7 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void fa_fwd_16(Params p) {
 // consumed by the next matrix phase).  A whole causal problem runs as pairs: a workgroup takes the heavy
 // query tile n-1-r and then the light tile r of one head over one continuous K/V stream, so every
 // workgroup computes n+1 tiles of 256 rows by 256 keys.
-template <int D, bool IS_BF16, bool CAUSAL, bool PAIR>
+template <int D, bool IS_BF16, bool CAUSAL, bool PAIR, bool CHUNK = false>
 __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
   typedef Tile16<D, 8> T;
   typedef Elem<IS_BF16> E;
@@ -603,22 +612,57 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
   // - 1 down to c n_pairs; pair r is query tile n_full - 1 - r, then tile r).  The launcher pairs only whole
   // causal problems of an even number of full 256-row tiles and splits the pairs evenly.  Descending, the
   // only unit of four tiles (tile 0) ends its chain.
-  int bh, qt, c_grp = 0, n_pairs = 1;
-  const int n_full = p.Nq / T::BM;
-  if constexpr (PAIR) {
+  // CHUNK (with PAIR): a key chunk split into row ranges (rows counted from q_row0).  Blocks [0, P8) run the
+  // pairs of its square (rows 0 .. Nkv - 1, keys 0 .. Nkv - 1); blocks [P8, P8 + R8) run the rows
+  // Nkv .. Nq - 1, which see every key, in chains of n_chain units of 256 rows (the pair code's masks leave
+  // them alone: their rows lie past every key); the remaining blocks, the shortest, write O = 0 and
+  // lse = -inf for the rows -n_empty .. -1, which see none, into the launch's tail.  P8 and R8 are the
+  // block counts padded to multiples of 8, so each range starts on the first XCD.
+  int bh, qt, c_grp = 0, n_pairs = 1, n_chain = 1;
+  bool pair_wg = PAIR, zero_wg = false;
+  const int n_full = (CHUNK ? p.Nkv : p.Nq) / T::BM;
+  if constexpr (CHUNK) {
+    const int heads = p.B * p.H;
+    const int P8 = (p.n_units + 7) & ~7, R = p.n_rect / p.n_chain * heads, R8 = (R + 7) & ~7;
+    int bid = blockIdx.x;
+    if (bid < P8) {
+      if (bid >= p.n_units) return;
+      unit_of(bid, p.n_units, p.n_qtiles, false, bh, c_grp);
+      n_pairs = (n_full / 2) / p.n_qtiles;
+      qt = n_full - (c_grp + 1) * n_pairs;
+    } else if (bid < P8 + R8) {
+      bid -= P8;
+      if (bid >= R) return;
+      unit_of(bid, R, R / heads, false, bh, c_grp);
+      n_chain = p.n_chain;
+      qt = n_full + c_grp * n_chain;
+      pair_wg = false;
+    } else {
+      bid -= P8 + R8;
+      const int Z = (p.n_empty + T::BM - 1) / T::BM * heads;
+      if (bid >= Z) return;
+      unit_of(bid, Z, Z / heads, false, bh, qt);
+      zero_wg = true;
+    }
+  } else if constexpr (PAIR) {
     unit_of(blockIdx.x, p.n_units, p.n_qtiles, false, bh, c_grp);
     n_pairs = (n_full / 2) / p.n_qtiles;
     qt = n_full - (c_grp + 1) * n_pairs;
   } else {
     unit_of(blockIdx.x, p.n_units, p.n_qtiles, CAUSAL, bh, qt);
   }
-  // unit u of the chain: its query tile and its tile count (keys 0 .. the last key of its last row)
+  // unit u of the chain: its query tile and its tile count (keys 0 .. the last key of its last row; a chunk's
+  // rows after the square: consecutive tiles, every key)
   auto qt_of = [&](int u) __attribute__((always_inline)) {
+    if (CHUNK && !pair_wg) return qt + u;
     const int r = (c_grp + 1) * n_pairs - 1 - (u >> 1);
     return (u & 1) ? r : n_full - 1 - r;
   };
   auto q0_of_unit = [&](int u) __attribute__((always_inline)) { return qt_of(u) * T::BM + wave * T::QW; };
-  auto nt_of_unit = [&](int u) __attribute__((always_inline)) { return (qt_of(u) + 1) * (T::BM / T::BN); };
+  auto nt_of_unit = [&](int u) __attribute__((always_inline)) {
+    return (CHUNK && !pair_wg) ? p.Nkv / T::BN : (qt_of(u) + 1) * (T::BM / T::BN);
+  };
+  const int n_chain_units = pair_wg ? 2 * n_pairs : n_chain;  // units this block runs
   const int b = bh / p.H, h = bh - (bh / p.H) * p.H;
   const SeqGeom sg = seq_geometry<CAUSAL, false>(p, b, h, bh);
   const int Nq = sg.Nq, Nkv = sg.Nkv;
@@ -629,6 +673,16 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
   const uint8_t* __restrict__ kg_ptr = (const uint8_t*)p.k + 2 * sg.kv_base;
   const uint8_t* __restrict__ vg_ptr = (const uint8_t*)p.v + 2 * sg.kv_base;
   uint16_t* og_ptr = (uint16_t*)p.o + sg.q_base;
+
+  if (CHUNK && zero_wg) {  // rows -n_empty + 256 qt .. (at most) -1: no visible key
+    const int r0 = -p.n_empty + qt * T::BM, r1 = min(r0 + T::BM, 0);
+    constexpr int CPR = D / 8;  // 16-byte pieces per row
+    for (int i = threadIdx.x; i < (r1 - r0) * CPR; i += 64 * T::NW)
+      *(u32x4_t*)(og_ptr + (int64_t)(r0 + i / CPR) * p.stride_s + 8 * (i % CPR)) = u32x4_t{0u, 0u, 0u, 0u};
+    for (int i = threadIdx.x; i < r1 - r0; i += 64 * T::NW) p.lse[sg.lse_base + r0 + i] = kNegInf;
+    record_tiles(p, 1, bh, T::BM, T::BN, T::QW, T::NW, r0, 0, -1, 0, wave, lane, 0, r1);
+    return;
+  }
 
   // tiles of 64 keys from key 0 up to the last key visible to the unit's last query
   const int q_wg = qt * T::BM;
@@ -1011,8 +1065,8 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
   // first matrix phase ends the previous unit, whose output is then stored, and its first vector phase
   // sets the reference maximum (a loop per unit nested in a loop over units spilled registers).
   int u = 0, nt = PAIR ? nt_of_unit(0) : n_kt_a, q0 = q0a;
-  bool more = PAIR && 2 * n_pairs > 1;
-  int q0_next = PAIR && more ? q0_of_unit(1) : q0;
+  bool more = PAIR && n_chain_units > 1;
+  int q0_next = more ? q0_of_unit(1) : q0;
   // the first group: its first matrix phase has no P.V
   mphase(0, st0, later_c, false, nt, more, q0_next, true);
   vphase(0, st0, first_c, false, q0);
@@ -1035,7 +1089,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
       ++u;
       nt = nt_of_unit(u);
       q0 = q0_next;
-      more = u + 1 < 2 * n_pairs;
+      more = u + 1 < n_chain_units;
       q0_next = more ? q0_of_unit(u + 1) : q0;
       jl = 0;
       unit_start = true;
@@ -1070,14 +1124,18 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the refetches past the end land before the LDS is released
   finish(q0_last);
   // every wave computes on every tile of the stream
-  if constexpr (PAIR) {
+  if (CHUNK && !pair_wg) {  // one record per unit of the chain, in slots past the grid's
+    for (int i = 0; i < n_chain; ++i)
+      record_tiles_at(p, gridDim.x + (blockIdx.x * n_chain + i), 1, bh, T::BM, T::BN, T::QW, T::NW,
+                      qt_of(i) * T::BM, n_kt_a, -1, 0, wave, lane, n_kt_a, p.Nq);
+  } else if (pair_wg) {
     for (int i = 0; i < n_pairs; ++i) {
       const int na = nt_of_unit(2 * i), nb = nt_of_unit(2 * i + 1);
-      record_tiles_at(blockIdx.x * n_pairs + i, 1, bh, T::BM, T::BN, T::QW, T::NW, qt_of(2 * i) * T::BM, na,
-                      qt_of(2 * i + 1) * T::BM, nb, wave, lane, na + nb);
+      record_tiles_at(p, blockIdx.x * n_pairs + i, 1, bh, T::BM, T::BN, T::QW, T::NW, qt_of(2 * i) * T::BM, na,
+                      qt_of(2 * i + 1) * T::BM, nb, wave, lane, na + nb, p.Nq);
     }
   } else {
-    record_tiles(1, bh, T::BM, T::BN, T::QW, T::NW, q_wg, n_kt_a, -1, 0, wave, lane, n_kt_a);
+    record_tiles(p, 1, bh, T::BM, T::BN, T::QW, T::NW, q_wg, n_kt_a, -1, 0, wave, lane, n_kt_a, p.Nq);
   }
 }
 
@@ -1291,12 +1349,49 @@ static hipError_t launch32(Params p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// A causal call whose key chunk starts at query row i0 = -delta >= 0 (the chunk's first key sits at that
+// row's position) splits into three row ranges: rows 0 .. i0 - 1 see none of its keys, rows i0 .. i0 + Nkv - 1
+// see it as a whole causal problem (row i0 + r sees keys 0 .. r), and every later row sees all of it.  One
+// launch of the ping-pong kernel covers all three (CHUNK): the square's heavy/light pairs first, then the
+// later rows as units of 256 rows, then blocks that write O = 0 and lse = -inf for the first rows.  Needs
+// Nkv a multiple of 512 (pairs of 256-row tiles) and the rows after the square a multiple of 256.  (Three
+// launches, one per range, measured no faster than fa_fwd_16 over the whole chunk: each paid its own
+// ramp and tail, and a square of two pairs per head fills the GPU only twice over.)
+#ifndef FA_CHUNK_CHAIN
+#define FA_CHUNK_CHAIN 2
+#endif
+constexpr int kChunkChain = FA_CHUNK_CHAIN;
+
+template <int D, bool IS_BF16>
+static hipError_t launch16_chunk_split(Params p, int i0, hipStream_t stream) {
+  typedef Tile16<D, 8> T;
+  const int heads = p.B * p.H;
+  const int rest = p.Nq - i0 - p.Nkv;
+  p.q_row0 += i0;  // rows from the square's first row on
+  p.Nq = p.Nkv + rest;
+  p.delta = 0;
+  p.n_qtiles = p.Nkv / (2 * T::BM);  // pairs per head (one pair per block)
+  p.n_units = p.n_qtiles * heads;
+  p.n_rect = rest / T::BM;
+  p.n_empty = i0;
+  // the rows after the square run in chains of up to kChunkChain units per block (the chain streams its
+  // units' tiles back to back, as a pair does, so a block's start-up and drain are paid once per chain)
+  p.n_chain = kChunkChain;
+  while (p.n_chain > 1 && p.n_rect % p.n_chain != 0) p.n_chain /= 2;
+  const int nz = (i0 + T::BM - 1) / T::BM;
+  const int grid = ((p.n_units + 7) & ~7) + ((p.n_rect / p.n_chain * heads + 7) & ~7) + ((nz * heads + 7) & ~7);
+  hipLaunchKernelGGL((fa_fwd_16pp<D, IS_BF16, true, true, true>), dim3(grid), dim3(512), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int D, bool IS_BF16>
 static hipError_t launch16_d(const Params& p, bool causal, hipStream_t stream) {
   // The ping-pong kernel runs non-causal calls whose query and key counts are multiples of 256 (its tiles
   // go in groups of four 64-key tiles, and every wave of a 256-query workgroup then has rows) and whole
-  // causal problems of an even number of 256-query tiles, as heavy and light pairs.  Windows, offsets and
-  // key chunks keep fa_fwd_16 (there the ping-pong kernel measured slower: many of their tiles are masked).
+  // causal problems of an even number of 256-query tiles, as heavy and light pairs, and the square and the
+  // rows after it of a key chunk that splits into row ranges (launch16_chunk_split).  Windows, other
+  // offsets and chunks keep fa_fwd_16 (with the mask on both edges of a window, or a chunk's diagonal cut
+  // through 256-row units, the ping-pong kernel measured slower: many of their tiles are masked).
 #ifndef FA_NO_PINGPONG
   constexpr bool kPingPong = true;
 #else
@@ -1319,6 +1414,11 @@ static hipError_t launch16_d(const Params& p, bool causal, hipStream_t stream) {
   if (kPingPong && pairs(Tile16<D, 8>::BM) && p.Nq % 256 == 0) return launch16pp<D, IS_BF16, true, true>(p, stream);
   if (pairs(Tile16<D, 8>::BM)) return launch16<D, IS_BF16, true, false, false, true, 8>(p, stream);
   if (pairs(Tile16<D, 4>::BM)) return launch16<D, IS_BF16, true, false, false, true, 4>(p, stream);
+  // a key chunk (or keys starting at a later query's position) that splits into the three row ranges
+  if (kPingPong && p.delta <= 0 && p.Nkv > 0 && p.Nkv % 512 == 0) {
+    const int64_t rest = (int64_t)p.Nq + p.delta - p.Nkv;
+    if (rest >= 0 && rest % 256 == 0) return launch16_chunk_split<D, IS_BF16>(p, (int)-p.delta, stream);
+  }
   return launch16<D, IS_BF16, true, false>(p, stream);
 }
 
@@ -1329,7 +1429,9 @@ static hipError_t launch32_d(const Params& p, bool causal, hipStream_t stream) {
 }
 
 // A window is only used with causal attention (the entry point rejects it otherwise).
-hipError_t launch(const Params& p, int dtype, int d, bool causal, hipStream_t stream) {
+hipError_t launch(const Params& p_in, int dtype, int d, bool causal, hipStream_t stream) {
+  Params p = p_in;
+  if (p.lse_rows == 0) p.lse_rows = p.Nq;
   if (dtype == kDtypeBf16) return d == 128 ? launch16_d<128, true>(p, causal, stream) : launch16_d<64, true>(p, causal, stream);
   if (dtype == kDtypeFp16) return d == 128 ? launch16_d<128, false>(p, causal, stream) : launch16_d<64, false>(p, causal, stream);
   return d == 128 ? launch32_d<128>(p, causal, stream) : launch32_d<64>(p, causal, stream);

@@ -41,6 +41,16 @@ struct Params {
   const int* cu_q;
   const int* cu_k;
   int64_t total_q, total_k;
+  // Set by the launcher when it splits a call into launches over row ranges (0 from the entry points):
+  // this launch computes rows q_row0 .. q_row0 + Nq - 1 of each head, whose lse rows hold lse_rows
+  // entries (0: Nq); rec_base is its first tile-record slot (test builds).
+  int q_row0;
+  int64_t lse_rows;
+  int rec_base;
+  // A key chunk split into row ranges in one launch of the ping-pong kernel: rows 0 .. Nkv - 1 (from
+  // q_row0) are its square, the n_rect * 256 rows after it see every key (run in chains of n_chain units
+  // per block), and the n_empty rows before q_row0 see none.
+  int n_rect, n_empty, n_chain;
 };
 
 // Enqueue the attention kernel for (dtype, d, causal, window >= 0) on `stream`.
