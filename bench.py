@@ -91,7 +91,8 @@ def fwd_kernel_label(nq, nk, q_offset, window, chunks, causal=True, dtype="bf16"
     """Which forward kernel a call runs, by the library's own rule: fp32 runs fa_fwd_32; a 16-bit non-causal call
     whose query and key counts are multiples of 256 runs the ping-pong kernel; a whole causal problem pairs
     256-query tiles (8 waves) when ceil(N/256) and ceil(N/64) are even, on the ping-pong kernel when N is also
-    a multiple of 256, else 128-query tiles (4 waves) when ceil(N/128) and ceil(N/64) are even; every other
+    a multiple of 256, else 128-query tiles (4 waves) when ceil(N/128) and ceil(N/64) are even; a key chunk
+    that starts at a query row runs on the ping-pong kernel split into row ranges (chunk_splits); every other
     call runs one 128-query tile per workgroup."""
     if dtype == "fp32":
         return "fa_fwd_32<%d,%s>" % (d, "causal" if causal else "non-causal")
@@ -102,11 +103,10 @@ def fwd_kernel_label(nq, nk, q_offset, window, chunks, causal=True, dtype="bf16"
     if window >= 0:
         return "fa_fwd_16<%d,bf16,causal,window> (4 waves)" % d
     if chunks > 1:
-        parts = chunk_launches(nq, nk, q_offset, chunks)
-        if all(p is not None for p in parts):
-            return ("per key chunk: fa_fwd_16pp<%d,bf16,causal> (ping-pong pairs) on the chunk's square rows + "
-                    "fa_fwd_16pp<%d,bf16,non-causal> on the rows after it + fa_fwd_16<%d,bf16,causal> (O = 0, "
-                    "lse = -inf) on the rows before it" % (d, d, d))
+        if all(chunk_splits(nq, nk, q_offset, chunks)):
+            return ("fa_fwd_16pp<%d,bf16,causal,pair,chunk> per key chunk (ping-pong, 8 waves: the chunk's square "
+                    "as heavy/light pairs, the rows after it in chains of full units, O = 0 for the rows before it)"
+                    % d)
         return "fa_fwd_16<%d,bf16,causal> (one 128-query tile per workgroup, 4 waves) per key chunk" % d
     if chunks == 1 and q_offset == 0 and nq == nk and (nq + 63) // 64 % 2 == 0:
         if (nq + 255) // 256 % 2 == 0:
@@ -118,18 +118,17 @@ def fwd_kernel_label(nq, nk, q_offset, window, chunks, causal=True, dtype="bf16"
     return "fa_fwd_16<%d,bf16,causal> (one 128-query tile per workgroup, 4 waves)" % d
 
 
-def chunk_launches(nq, nk, q_offset, chunks):
-    """Per key chunk of a causal call: the kernel launches the library's rule gives when it splits the chunk
-    into row ranges (rows before the chunk's first key, its square, the rows after it), or None when the
-    chunk runs as one fa_fwd_16 launch: the chunk length a multiple of 512, its first key at a query row
-    (q_offset <= kv_start) and the rows after the square a multiple of 256."""
+def chunk_splits(nq, nk, q_offset, chunks):
+    """Per key chunk of a causal call: whether the library's rule runs it on the ping-pong kernel split into
+    row ranges (rows before the chunk's first key, its square, the rows after it) rather than on fa_fwd_16:
+    the chunk length a multiple of 512, its first key at a query row (q_offset <= kv_start) and the rows
+    after the square a multiple of 256.  Either way a chunk is one launch."""
     out = []
     for c in range(chunks):
         a, b = nk * c // chunks, nk * (c + 1) // chunks
         i0, kv_len = a - q_offset, b - a
         rest = nq - i0 - kv_len
-        ok = i0 >= 0 and kv_len > 0 and kv_len % 512 == 0 and rest >= 0 and rest % 256 == 0
-        out.append((i0 > 0) + 1 + (rest > 0) if ok else None)
+        out.append(i0 >= 0 and kv_len > 0 and kv_len % 512 == 0 and rest >= 0 and rest % 256 == 0)
     return out
 
 
@@ -387,9 +386,7 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel": fwd_kernel_label(Nq, Nk, q_offset, window, chunks, w.causal, dtype, D),
                 "mean_launch_ms": round(mean_attn_ms / chunks, 5),
-                "launches_per_step": (sum(n or 1 for n in chunk_launches(Nq, Nk, q_offset, chunks))
-                                      if chunks > 1 and w.causal and window < 0 else chunks),
-                "calls_per_step": chunks,
+                "launches_per_step": chunks,
                 "kernel_sha": kernel_sha()}
     extra = {}
     if chunks > 1:
