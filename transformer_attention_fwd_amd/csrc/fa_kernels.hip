@@ -592,15 +592,21 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
   typedef Elem<IS_BF16> E;
   typedef typename E::vec8 vec8;
   // four stages for K and four for V, eight LDS objects (a stage fixed at compile time lets the compiler
-  // see that reads of one stage do not wait for the DMA filling another)
-  __shared__ __attribute__((aligned(1024))) uint8_t ks0[T::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t ks1[T::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t ks2[T::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t ks3[T::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs0[T::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs1[T::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs2[T::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t vs3[T::TILE_BYTES];
+  // see that reads of one stage do not wait for the DMA filling another).  The compiler lays a kernel's
+  // LDS objects out in name order: the V stages (lds_a*) take the low 64 KiB and the K stages (lds_b*) the
+  // 64 KiB above.  A DS instruction's immediate offset has 16 bits, so the transposing V reads (two per
+  // fragment, 8 base registers) address every stage with an immediate, and the K reads (one per fragment,
+  // 4 base registers) do the same from bases that already hold the 64 KiB (kb below); with the V stages
+  // above 64 KiB every V read had cost a VALU add, 32 per wave and tile.
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_a_v0[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_a_v1[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_a_v2[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_a_v3[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_b_k0[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_b_k1[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_b_k2[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_b_k3[T::TILE_BYTES];
+  constexpr int K_HIGH = 4 * T::TILE_BYTES >= 65536 ? 65536 : 0;  // what kb holds of the K stages' address
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -717,17 +723,17 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
   const int load_step = (T::NW * 64 / T::CHUNKS) * row_bytes;
   auto kstage = [&](auto st) __attribute__((always_inline)) -> uint8_t* {
     constexpr int s = decltype(st)::value % 4;
-    if constexpr (s == 0) return ks0;
-    else if constexpr (s == 1) return ks1;
-    else if constexpr (s == 2) return ks2;
-    else return ks3;
+    if constexpr (s == 0) return lds_b_k0;
+    else if constexpr (s == 1) return lds_b_k1;
+    else if constexpr (s == 2) return lds_b_k2;
+    else return lds_b_k3;
   };
   auto vstage = [&](auto st) __attribute__((always_inline)) -> uint8_t* {
     constexpr int s = decltype(st)::value % 4;
-    if constexpr (s == 0) return vs0;
-    else if constexpr (s == 1) return vs1;
-    else if constexpr (s == 2) return vs2;
-    else return vs3;
+    if constexpr (s == 0) return lds_a_v0;
+    else if constexpr (s == 1) return lds_a_v1;
+    else if constexpr (s == 2) return lds_a_v2;
+    else return lds_a_v3;
   };
   auto issue_tile = [&](int key, uint8_t* kdst, uint8_t* vdst) __attribute__((always_inline)) {
     const int soff = key * row_bytes;
@@ -789,7 +795,10 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
 
   int kb[T::DC], vb[T::DT];
 #pragma unroll
-  for (int c = 0; c < T::DC; ++c) kb[c] = li * T::ROW_BYTES + (((4 * c + g) ^ T::swz_k(li)) << 4);
+  for (int c = 0; c < T::DC; ++c) {
+    kb[c] = K_HIGH + li * T::ROW_BYTES + (((4 * c + g) ^ T::swz_k(li)) << 4);
+    asm volatile("" : "+v"(kb[c]));  // kept whole: the stage address minus K_HIGH becomes the immediate
+  }
 #pragma unroll
   for (int dt = 0; dt < T::DT; ++dt) {
     const int vrow = 4 * g + (li >> 2);
@@ -848,7 +857,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
   };
   // K fragment g = c * KT + kt of a tile (row reads), in the order the S^T products use them
   auto k_frag = [&](const uint8_t* ks, int g) __attribute__((always_inline)) {
-    return *(const vec8*)(ks + kb[g / T::KT] + 16 * (g % T::KT) * T::ROW_BYTES);
+    return *(const vec8*)(ks + (kb[g / T::KT] - K_HIGH) + 16 * (g % T::KT) * T::ROW_BYTES);
   };
   auto pv_mfma = [&](int f, const vec8& vf) __attribute__((always_inline)) {
     const int kc = f / T::DT, dt = f % T::DT;
@@ -1048,8 +1057,8 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
 
   // Q before the first tiles: the wait for tile 0 covers it and leaves tile 1 in flight
   load_q(q0a, std::false_type());
-  issue_tile(0, ks0, vs0);
-  issue_tile(T::BN, ks1, vs1);
+  issue_tile(0, lds_b_k0, lds_a_v0);
+  issue_tile(T::BN, lds_b_k1, lds_a_v1);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(TILE_LOADS));
   lds_barrier();
 
