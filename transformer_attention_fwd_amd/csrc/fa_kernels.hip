@@ -997,7 +997,8 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
         float pv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qg][kt][r], cexp, neg_m));
-        acc += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+        const float t4 = (pv[0] + pv[1]) + (pv[2] + pv[3]);
+        acc = kt == 0 ? t4 : acc + t4;  // (0 + x is not folded: it would turn -0 into +0)
         const int kc = kt >> 1, half = kt & 1;
         pf[qg][kc][2 * half + 0] = E::pack2(pv[0], pv[1]);
         pf[qg][kc][2 * half + 1] = E::pack2(pv[2], pv[3]);
