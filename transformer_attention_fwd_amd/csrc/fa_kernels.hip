@@ -581,9 +581,9 @@ __global__ __launch_bounds__(64 * NWV, 8 / NWV) void fa_fwd_16(Params p) {
 // interval the two may drift (the formula page, section "ops-transformer 中的实现", has the matrix and
 // vector units of the Ascend core work side by side; here the two waves of a SIMD take those roles in
 // turn).  The matrix wave runs at the higher issue priority.  K/V tiles stream through a 4-stage LDS
-// ring: tile j+2 is issued at the start of M(j), once every wave has passed the barrier after its last
-// use of tile j-2; the extra stage lets a vector phase end with its V reads still in flight (they are
-// consumed by the next matrix phase).  A whole causal problem runs as pairs: a workgroup takes the heavy
+// ring: tile j+2 is issued early in M(j) (behind its first two products), once every wave has passed the
+// barrier after its last use of tile j-2; the extra stage lets a vector phase end with its V reads still in
+// flight (they are consumed by the next matrix phase).  A whole causal problem runs as pairs: a workgroup takes the heavy
 // query tile n-1-r and then the light tile r of one head over one continuous K/V stream, so every
 // workgroup computes n+1 tiles of 256 rows by 256 keys.
 template <int D, bool IS_BF16, bool CAUSAL, bool PAIR, bool CHUNK = false>
@@ -888,8 +888,9 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Every wave issues tile j+2's DMA at the start of its matrix phase M(j) (past the stream's end it
-  // fetches the last tile again into the free stage) and, right before its barrier (after V(j) for waves
+  // Every wave issues tile j+2's DMA in its matrix phase M(j), behind the phase's first two products (past
+  // the stream's end it fetches the last tile again into the free stage; issued first, the DMA held up the
+  // first products: C3 +1.5 %, C5 +1.8 % from the move) and, right before its barrier (after V(j) for waves
   // 0-3, after M(j) for waves 4-7), waits until its share of tile j+1 has landed: at most tile j+2's loads
   // (and the Q loads issued after them) stay in flight, a constant count.  Stage safety: tile j+2 refills
   // the stage of tile j-2, whose last readers (waves 4-7's M(j-1), which drains its LDS reads) finish
@@ -912,13 +913,21 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
                     bool stores = false) __attribute__((always_inline)) {
     constexpr int S = decltype(st)::value;
     constexpr bool PV = decltype(pv_c)::value;
-    issue_next(jl, st, nt, more);
     __builtin_amdgcn_s_setprio(1);
     const uint8_t* ks = kstage(st);
     vec8 ka[H], kc2[H];
     if constexpr (PV) {
       vec8 v2[H];
-      pv_first(vstage(std::integral_constant<int, S + 3>()), v2);
+      // (pv_first with the DMA issued behind the first two products)
+#pragma unroll
+      for (int f = 0; f < H; ++f) {
+        pv_mfma(f, vfr[f]);
+        v2[f] = v_frag(vstage(std::integral_constant<int, S + 3>()), H + f);
+        if (f == 0) u_mfma(0);
+        if (f == 1) issue_next(jl, st, nt, more);
+        if (f == H / 2 && T::KC > 1) u_mfma(1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int f = 0; f < H; ++f) {
         pv_mfma(H + f, v2[f]);
@@ -926,6 +935,7 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
+      issue_next(jl, st, nt, more);
 #pragma unroll
       for (int f = 0; f < H; ++f) ka[f] = k_frag(ks, f);
       __builtin_amdgcn_sched_barrier(0);
