@@ -592,7 +592,8 @@ __global__ __launch_bounds__(512, 1) void fa_fwd_16pp(Params p) {
   typedef Elem<IS_BF16> E;
   typedef typename E::vec8 vec8;
   // four stages for K and four for V, eight LDS objects (a stage fixed at compile time lets the compiler
-  // see that reads of one stage do not wait for the DMA filling another).  The compiler lays a kernel's
+  // see that reads of one stage do not wait for the DMA filling another; as fields of one struct, which
+  // would fix their order, they made it wait for every DMA in flight).  The compiler lays a kernel's
   // LDS objects out in name order: the V stages (lds_a*) take the low 64 KiB and the K stages (lds_b*) the
   // 64 KiB above.  A DS instruction's immediate offset has 16 bits, so the transposing V reads (two per
   // fragment, 8 base registers) address every stage with an immediate, and the K reads (one per fragment,
